@@ -1,0 +1,8 @@
+"""CPU float64 oracle for exact attention (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s ``cpu_baseline``
+leg may import this package. The product (the HIP library and its Python
+binding) never does.
+"""
+from .attention import (attention, attention_head, decode, merge, online_softmax_rows,  # noqa: F401
+                        part_state)
