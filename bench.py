@@ -1,0 +1,172 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One step is one pass of the whole path over resident synthetic inputs:
+  * prefill: fa_fwd on causal self-attention, B=1, H=32, L=16384, d=128, bf16
+    (the pages' 16,384-token example), counted as 4*B*H*L*L*d/2 FLOP;
+  * decode:  fa_decode (split-K + combine) on B=64 requests, 32 query / 8 KV heads,
+    d=128, bf16 cache with per-request context lengths uniform in [8192, 32768],
+    counted as the K and V bytes of every request's context.
+The headline ``value`` is the prefill TFLOP/s; decode KV GB/s is reported beside it.
+Kernel durations come from HIP events on the stream the kernels run on (torch's
+current stream), over exactly K timed steps after W warm-up steps.
+
+``cpu_baseline`` times the CPU fp64 oracle (as it is, untuned) on a bounded sample of
+the same prefill workload: consecutive blocks of query rows of one head, until about
+ten seconds of CPU work, reported in the same unit (algorithmic TFLOP/s of the rows
+it finished).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "bf16 attn-fwd TFLOP/s & % MFMA peak at L=16k d=128; decode KV-read GB/s"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
+PREFILL = "causal_prefill_B1_H32_L16384_d128"
+DECODE = "decode_B64_H32_Hkv8_ctx32768_d128"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def cpu_baseline(w, x, seconds):
+    """Time the fp64 oracle on consecutive 256-row blocks of head (0, 0), newest rows first."""
+    import numpy as np
+
+    import fa_inputs
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    q = fa_inputs.as_oracle_f64(x["q"][0, 0])
+    k = fa_inputs.as_oracle_f64(x["k"][0, 0])
+    v = fa_inputs.as_oracle_f64(x["v"][0, 0])
+    L, d = q.shape
+    block = 256
+    flops = 0.0
+    rows_done = 0
+    t0 = time.perf_counter()
+    hi = L
+    while hi > 0 and time.perf_counter() - t0 < seconds:
+        rows = np.arange(max(0, hi - block), hi)
+        oracle.attention_head(q, k, v, scale=w.scale, causal=True, rows=rows)
+        flops += 4.0 * d * float((rows + 1).sum())  # visible (query, key) pairs of these rows
+        rows_done += len(rows)
+        hi -= block
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{rows_done} query rows (the last ones) of head 0 of {w.name}, fp64, {dt:.1f} s",
+            "seconds": round(dt, 2)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; run with --gpus 1"}))
+        sys.exit(2)
+    import torch
+
+    import exact_attention_111_amd as fa
+    import fa_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wp = fa_inputs.WORKLOADS[PREFILL]
+    wd = fa_inputs.WORKLOADS[DECODE]
+    xp = fa_inputs.workload_inputs(wp, device=dev)
+    xd = fa_inputs.workload_inputs(wd, device=dev)
+    o_p = torch.empty_like(xp["q"])
+    lse_p = torch.empty((wp.B, wp.H, wp.L), dtype=torch.float32, device=dev)
+    o_d = torch.empty_like(xd["q"])
+    lse_d = torch.empty((wd.B, wd.H), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(16, fa.decode_workspace_bytes(wd.B, wd.H, wd.L, wd.d)), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        fa.fwd(xp["q"], xp["k"], xp["v"], causal=True, scale=wp.scale, out=o_p, lse=lse_p)
+        if ev is not None:
+            ev[1].record()
+        fa.decode(xd["q"], xd["k_cache"], xd["v_cache"], xd["ctx_lens"], scale=wd.scale, workspace=ws, out=o_d,
+                  lse=lse_d)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in events]
+    dec_ms = [e[1].elapsed_time(e[2]) for e in events]
+    fwd_avg = sum(fwd_ms) / len(fwd_ms)
+    dec_avg = sum(dec_ms) / len(dec_ms)
+
+    flop = 4.0 * wp.B * wp.H * wp.L * wp.L * wp.d / 2.0
+    tflops = flop / (fwd_avg * 1e-3) / 1e12
+    ctx = xd["ctx_lens_cpu"].to(torch.int64)
+    kv_bytes = float(2 * wd.Hkv * wd.d * 2 * int(ctx.sum()))
+    gbps = kv_bytes / (dec_avg * 1e-3) / 1e9
+
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{PREFILL} + {DECODE}", "prefill": {"B": wp.B, "H": wp.H, "L": wp.L, "d": wp.d,
+                                                                   "causal": True, "seed": wp.seed},
+                   "decode": {"B": wd.B, "H": wd.H, "Hkv": wd.Hkv, "Lmax": wd.L, "d": wd.d,
+                              "ctx_range": list(wd.len_range), "seed": wd.seed,
+                              "ctx_sum": int(ctx.sum())}},
+        "prefill": {"ms": round(fwd_avg, 4), "ms_min": round(min(fwd_ms), 4), "tflops": round(tflops, 2),
+                    "pct_mfma_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2), "flop_per_launch": flop},
+        "decode": {"value": round(gbps, 1), "unit": "GB/s", "ms": round(dec_avg, 4), "ms_min": round(min(dec_ms), 4),
+                   "pct_hbm_peak": round(100 * gbps / PEAK_HBM_GBPS, 2), "kv_bytes_per_launch": kv_bytes},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "fwd_kernel<128, bf16, bf16>"},
+        "roofline_decode": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                            "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None,
+                            "kernels": "decode_split_kernel<128> + decode_combine_kernel<128>"},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wp, xp, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,9 @@
+"""exact_attention_111_amd — exact scaled-dot-product attention for AMD MI355X (gfx950).
+
+FlashAttention-style prefill (``fwd``) and split-K decode (``decode``) run in
+hand-written HIP kernels behind the C ABI of ``libfa.so`` (``include/fa.h``); this
+package only marshals arguments to it.
+"""
+from .binding import FaError, decode, decode_workspace_bytes, fwd, lib, status_string  # noqa: F401
+
+__all__ = ["fwd", "decode", "decode_workspace_bytes", "FaError", "lib", "status_string"]

@@ -1,0 +1,136 @@
+"""ctypes binding of libfa (the C ABI declared in include/fa.h).
+
+Argument marshalling only: every step of the attention computation runs in the HIP
+kernels behind the C ABI. PyTorch supplies device memory and the current stream.
+There is no fallback: if libfa.so is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
+SYMBOLS = ("fa_fwd", "fa_fwd_f32", "fa_decode", "fa_decode_workspace_bytes", "fa_status_string")
+
+
+class FaError(RuntimeError):
+    """A non-OK status returned by libfa."""
+
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libfa.so (loaded once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"libfa.so not found at {_LIB_PATH}; build it with "
+                          "`python -m exact_attention_111_amd.build` (needs hipcc)")
+    L = ctypes.CDLL(_LIB_PATH)
+    vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    fwd_args = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp, vp]
+    L.fa_fwd.argtypes = fwd_args
+    L.fa_fwd.restype = i32
+    L.fa_fwd_f32.argtypes = fwd_args
+    L.fa_fwd_f32.restype = i32
+    L.fa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    L.fa_decode_workspace_bytes.restype = ctypes.c_size_t
+    L.fa_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, vp, vp, ctypes.c_size_t, vp]
+    L.fa_decode.restype = i32
+    L.fa_status_string.argtypes = [i32]
+    L.fa_status_string.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().fa_status_string(status).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(status: int, what: str):
+    if status != FA_OK:
+        raise FaError(status, what)
+
+
+def fwd(q, k, v, *, causal: bool = False, scale: float | None = None, seqlens=None, out=None, lse=None):
+    """Attention forward through ``fa_fwd`` (bf16) or ``fa_fwd_f32`` (fp32 I/O).
+
+    q: [B, H, Lq, d]; k, v: [B, Hkv, Lk, d], contiguous, on one GPU, all bf16 or all
+    fp32. seqlens: optional int32 [B] on the same device (requires Lq == Lk).
+    Returns (o [B, H, Lq, d] in the input dtype, lse [B, H, Lq] fp32).
+    """
+    B, H, Lq, d = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device)
+    for t in (q, k, v, out, lse):
+        if not t.is_contiguous():
+            raise ValueError("libfa needs contiguous tensors")
+    if not (q.dtype == k.dtype == v.dtype == out.dtype) or q.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("q, k, v, out must all be bfloat16 or all float32")
+    if seqlens is not None and seqlens.dtype != torch.int32:
+        raise ValueError("seqlens must be int32")
+    fn = lib().fa_fwd if q.dtype == torch.bfloat16 else lib().fa_fwd_f32
+    st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Hkv, Lq, Lk, d, float(scale), int(bool(causal)),
+            _ptr(seqlens), _stream(q.device))
+    _check(st, "fa_fwd" if q.dtype == torch.bfloat16 else "fa_fwd_f32")
+    return out, lse
+
+
+def decode_workspace_bytes(B: int, H: int, Lmax: int, d: int) -> int:
+    return int(lib().fa_decode_workspace_bytes(B, H, Lmax, d))
+
+
+def decode(q, k_cache, v_cache, ctx_lens, *, scale: float | None = None, workspace=None, out=None, lse=None):
+    """Single-token decode through ``fa_decode``.
+
+    q: [B, H, d] bf16; k_cache, v_cache: [B, Hkv, Lmax, d] bf16; ctx_lens: int32 [B].
+    ``workspace``: optional uint8 device tensor of at least ``decode_workspace_bytes``.
+    Returns (o [B, H, d] bf16, lse [B, H] fp32).
+    """
+    B, H, d = q.shape
+    Hkv, Lmax = k_cache.shape[1], k_cache.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    need = decode_workspace_bytes(B, H, Lmax, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    for t in (q, k_cache, v_cache, out, lse, ctx_lens, workspace):
+        if not t.is_contiguous():
+            raise ValueError("libfa needs contiguous tensors")
+    if not (q.dtype == k_cache.dtype == v_cache.dtype == out.dtype == torch.bfloat16):
+        raise ValueError("decode needs bfloat16 q, caches and out")
+    if ctx_lens.dtype != torch.int32:
+        raise ValueError("ctx_lens must be int32")
+    st = lib().fa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), B, H, Hkv, Lmax, d,
+                         float(scale), _ptr(ctx_lens), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                         _stream(q.device))
+    _check(st, "fa_decode")
+    return out, lse

@@ -1,0 +1,88 @@
+"""Build libfa.so (the HIP kernels and the C ABI) in-tree for gfx950.
+
+    python -m exact_attention_111_amd.build [--asm DIR]
+
+Every source is compiled by hipcc for gfx950 only, with the packed-fp32 VALU forms
+disabled (the compiler would otherwise pair independent fp32 operations itself).
+``--asm DIR`` additionally writes the gfx950 assembly of each source to DIR.
+"""
+from __future__ import annotations
+
+import argparse
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libfa.so")
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_decode.hip"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found: libfa needs the ROCm HIP compiler")
+
+
+def common_flags():
+    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-I", INCLUDE, "-I", CSRC]
+
+
+def build(verbose: bool = False, asm_dir: str | None = None) -> str:
+    """Compile every source and link libfa.so next to this file; returns its path."""
+    cc = hipcc()
+    with tempfile.TemporaryDirectory(prefix="fa_build_") as tmp:
+        objs = []
+        procs = []
+        for src in SOURCES:
+            obj = os.path.join(tmp, src + ".o")
+            cmd = [cc, *common_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+            procs.append((src, cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
+            objs.append(obj)
+        failed = False
+        for src, cmd, p in procs:
+            out, _ = p.communicate()
+            out = "\n".join(ln for ln in out.splitlines() if "packed-fp32-ops" not in ln)
+            if p.returncode != 0:
+                failed = True
+                sys.stderr.write(f"[fa build] {src} failed:\n{' '.join(cmd)}\n{out}\n")
+            elif verbose and out.strip():
+                sys.stderr.write(f"[fa build] {src}:\n{out}\n")
+        if failed:
+            raise RuntimeError("libfa build failed")
+        tmp_lib = LIB + ".tmp"
+        link = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib]
+        r = subprocess.run(link, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"libfa link failed:\n{' '.join(link)}\n{r.stdout}")
+        os.replace(tmp_lib, LIB)
+    if asm_dir:
+        os.makedirs(asm_dir, exist_ok=True)
+        for src in SOURCES:
+            if not src.endswith(".hip"):
+                continue
+            out = os.path.join(asm_dir, src.replace(".hip", ".s"))
+            cmd = [cc, *common_flags(), "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", out]
+            subprocess.run(cmd, check=True, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    return LIB
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--asm", default=None, help="also write gfx950 assembly of the kernels to this directory")
+    ap.add_argument("-v", "--verbose", action="store_true")
+    args = ap.parse_args()
+    print(build(verbose=args.verbose, asm_dir=args.asm))
+
+
+if __name__ == "__main__":
+    main()

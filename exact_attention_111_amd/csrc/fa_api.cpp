@@ -1,0 +1,110 @@
+// fa_api.cpp — the extern "C" boundary of libfa: argument validation and dispatch.
+//
+// Every check here runs on the host before anything is enqueued, so a call that fails
+// validation writes nothing and touches no device state. Unsupported but well-formed
+// requests (a head dimension other than 64 or 128) return FA_ERR_UNSUPPORTED rather than
+// taking a slower path: an attention call that silently falls back is the failure mode
+// "2.1 FlashAttention-2 的核心思想" §2.1.7 and §2.1.11 warn about.
+#include "fa.h"
+
+#include <math.h>
+
+#include "fa_launch.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// A tensor pointer must be non-null and 16-byte aligned unless the tensor is empty.
+bool tensor_ok(const void* p, long long numel) {
+  if (numel == 0) return true;
+  return p != nullptr && aligned16(p);
+}
+
+bool supported_d(int d) { return d == 64 || d == 128; }
+
+fa_status validate_fwd(const void* q, const void* k, const void* v, const void* o, const void* lse, int B, int H,
+                       int Hkv, int Lq, int Lk, int d, float scale, int causal, const int32_t* seqlens) {
+  if (B < 0 || H < 0 || Hkv < 1 || Lq < 0 || Lk < 0 || d < 1) return FA_ERR_INVALID;
+  if (H % Hkv != 0) return FA_ERR_INVALID;
+  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_INVALID;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID;
+  if (seqlens != nullptr && (Lq != Lk || (reinterpret_cast<uintptr_t>(seqlens) & 3u) != 0)) return FA_ERR_INVALID;
+  const long long nq = (long long)B * H * Lq * d;
+  const long long nkv = (long long)B * Hkv * Lk * d;
+  if (!tensor_ok(q, nq) || !tensor_ok(o, nq) || !tensor_ok(k, nkv) || !tensor_ok(v, nkv)) return FA_ERR_INVALID;
+  if (!tensor_ok(lse, (long long)B * H * Lq)) return FA_ERR_INVALID;
+  if (!supported_d(d)) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+fa_status validate_decode(const void* q, const void* kc, const void* vc, const void* o, const void* lse, int B, int H,
+                          int Hkv, int Lmax, int d, float scale, const int32_t* ctx, const void* ws, size_t ws_bytes) {
+  if (B < 0 || H < 0 || Hkv < 1 || Lmax < 0 || d < 1) return FA_ERR_INVALID;
+  if (H % Hkv != 0) return FA_ERR_INVALID;
+  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_INVALID;
+  const long long nq = (long long)B * H * d;
+  const long long nkv = (long long)B * Hkv * Lmax * d;
+  if (!tensor_ok(q, nq) || !tensor_ok(o, nq) || !tensor_ok(kc, nkv) || !tensor_ok(vc, nkv)) return FA_ERR_INVALID;
+  if (!tensor_ok(lse, (long long)B * H)) return FA_ERR_INVALID;
+  if (B > 0 && (ctx == nullptr || (reinterpret_cast<uintptr_t>(ctx) & 3u) != 0)) return FA_ERR_INVALID;
+  if (!supported_d(d)) return FA_ERR_UNSUPPORTED;
+  const size_t need = fa_decode_workspace_bytes(B, H, Lmax, d);
+  if (need > 0 && (ws == nullptr || !aligned16(ws) || ws_bytes < need)) return FA_ERR_INVALID;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int Lq,
+                 int Lk, int d, float scale, int causal, const int32_t* seqlens, void* stream) {
+  const fa_status s = validate_fwd(q, k, v, o, lse, B, H, Hkv, Lq, Lk, d, scale, causal, seqlens);
+  if (s != FA_OK) return s;
+  if (B == 0 || H == 0 || Lq == 0) return FA_OK;
+  fa::FwdParams p{q, k, v, o, lse, B, H, Hkv, Lq, Lk, d, scale, causal, seqlens};
+  return fa::launch_fwd_bf16(p, static_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int Hkv,
+                     int Lq, int Lk, int d, float scale, int causal, const int32_t* seqlens, void* stream) {
+  const fa_status s = validate_fwd(q, k, v, o, lse, B, H, Hkv, Lq, Lk, d, scale, causal, seqlens);
+  if (s != FA_OK) return s;
+  if (B == 0 || H == 0 || Lq == 0) return FA_OK;
+  fa::FwdParams p{q, k, v, o, lse, B, H, Hkv, Lq, Lk, d, scale, causal, seqlens};
+  return fa::launch_fwd_f32(p, static_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_decode_workspace_bytes(int B, int H, int Lmax, int d) {
+  if (B < 0 || H < 0 || Lmax < 0 || d < 1) return 0;
+  const size_t nc = (size_t)fa::decode_num_chunks(Lmax);
+  // Partial outputs [B, H, nc, d] then (max, sum) pairs [B, H, nc, 2], both fp32.
+  return (size_t)B * H * nc * ((size_t)d + 2) * sizeof(float);
+}
+
+fa_status fa_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse, int B, int H,
+                    int Hkv, int Lmax, int d, float scale, const int32_t* ctx_lens, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  const fa_status s = validate_decode(q, k_cache, v_cache, o, lse, B, H, Hkv, Lmax, d, scale, ctx_lens, workspace,
+                                      workspace_bytes);
+  if (s != FA_OK) return s;
+  if (B == 0 || H == 0) return FA_OK;
+  const size_t nc = (size_t)fa::decode_num_chunks(Lmax);
+  float* ws_o = static_cast<float*>(workspace);
+  float* ws_ml = ws_o + (size_t)B * H * nc * d;
+  fa::DecodeParams p{q, k_cache, v_cache, o, lse, B, H, Hkv, Lmax, d, scale, ctx_lens, ws_o, ws_ml};
+  return fa::launch_decode(p, static_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+const char* fa_status_string(fa_status s) {
+  switch (s) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_INVALID: return "FA_ERR_INVALID";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
+    case FA_ERR_HIP: return "FA_ERR_HIP";
+  }
+  return "FA_ERR_UNKNOWN";
+}
+
+}  // extern "C"

@@ -1,0 +1,277 @@
+// fa_decode.hip — single-token decode over a long KV cache for gfx950 (MI355X).
+//
+// Decode has one query row per head and a long history of keys ("FlashAttention 与长上下文：
+// 先分清三张账", section "Prefill 和 decode 是两类问题"): every step reads the whole KV cache
+// once, so the kernel is bound by HBM bandwidth, not by the matrix cores. The keys of a
+// request are cut into fixed-size chunks; one workgroup produces the online-softmax state
+// (m, l, o) of one chunk for the query heads that share a KV head, and a second kernel
+// merges the chunk states of each (request, head) with the merge rule of
+// "2.1 FlashAttention-2 的核心思想" §2.1.3 (rescale each state by exp(m_c - max m)).
+//
+// gfx950 mapping of the split kernel (one wave64 per workgroup):
+//   * Every K and V byte of the chunk is loaded once, 16 bytes per lane per instruction,
+//     and reused by up to 4 query heads of the GQA group (more heads are split over grid
+//     slots of 4).
+//   * Scores use v_mfma_f32_16x16x32_bf16 with K as the B operand straight from the
+//     loaded registers (16 keys as columns) and the 4 query heads replicated 4 times over
+//     the 16 A rows, so each lane ends up holding all 4 heads' scores of one key.
+//   * Probabilities are passed through 512 bytes of LDS to the lanes holding the
+//     matching V rows, and P V is accumulated in fp32 on the VALU (8 dims x 4 heads per
+//     lane), so P is not rounded before the product.
+//   * The chunk's K/V for the next 32 keys are loaded before the current 32 are used.
+#include "fa_device.h"
+#include "fa_launch.h"
+
+namespace fa {
+namespace {
+
+constexpr int kHeadsPerPass = 4;
+constexpr int kKeysPerStep = 32;
+
+struct DecArgs {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  __bf16* o;
+  float* lse;
+  int B, H, Hkv, Lmax;
+  int group;   // H / Hkv
+  int nsg;     // head slots of 4 per KV head
+  int nchunk;  // chunks per request at capacity
+  float scale_log2;
+  const int32_t* ctx;
+  float* ws_o;
+  float* ws_ml;
+};
+
+template <int D>
+__global__ __launch_bounds__(64) void decode_split_kernel(const DecArgs a) {
+  constexpr int NCH = D / 8;            // 16-byte chunks per row
+  constexpr int VKPL = 64 / NCH;        // keys per V load instruction
+  constexpr int VLOADS = kKeysPerStep / VKPL;
+  constexpr int QS = D / 32;            // 16x16x32 k-steps over d
+  __shared__ __attribute__((aligned(16))) float pl[kKeysPerStep][kHeadsPerPass];
+
+  const int lane = threadIdx.x;
+  const int chunk = blockIdx.y;
+  const int x = blockIdx.x;  // (b, kvh, head slot group)
+  const int sg = x % a.nsg;
+  const int bk = x / a.nsg;
+  const int b = bk / a.Hkv;
+  const int kvh = bk - b * a.Hkv;
+
+  const int n = min(max(a.ctx[b], 0), a.Lmax);
+  const int c0 = chunk * kDecodeChunk;
+  if (c0 >= n) return;  // chunk past this request's context: nothing to write
+  const int c1 = min(n, c0 + kDecodeChunk);
+  const int h0 = kvh * a.group + sg * kHeadsPerPass;
+  const int nh = min(kHeadsPerPass, a.group - sg * kHeadsPerPass);
+
+  const size_t kv_off = (size_t)(b * a.Hkv + kvh) * a.Lmax * D;
+  const __bf16* __restrict__ kp = a.k + kv_off;
+  const __bf16* __restrict__ vp = a.v + kv_off;
+
+  // A operand: row r = lane % 16 is head slot r % 4; element t of k-step s is d = 32 s + 8 (lane / 16) + t.
+  const int slot_a = (lane & 15) & 3;
+  bf16x8 qa[QS];
+#pragma unroll
+  for (int s = 0; s < QS; ++s) {
+    u32x4 u = {0u, 0u, 0u, 0u};
+    if (slot_a < nh) u = *reinterpret_cast<const u32x4*>(a.q + (size_t)(b * a.H + h0 + slot_a) * D + 32 * s + 8 * (lane >> 4));
+    qa[s] = as_bf16x8(u);
+  }
+
+  // K as the B operand: column = key k0 + 16 blk + lane % 16, same d mapping as the A operand.
+  // V rows for the VALU product: load i covers key k0 + i * VKPL + lane / NCH, dims 8 * (lane % NCH) .. +8.
+  const int vkey = lane / NCH;
+  const int vch = lane - vkey * NCH;
+  u32x4 kr[2][QS], vr[VLOADS];
+  auto load_step = [&](int k0) {
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      const int key = k0 + 16 * blk + (lane & 15);
+#pragma unroll
+      for (int s = 0; s < QS; ++s) {
+        u32x4 u = {0u, 0u, 0u, 0u};
+        if (key < c1) u = *reinterpret_cast<const u32x4*>(kp + (size_t)key * D + 32 * s + 8 * (lane >> 4));
+        kr[blk][s] = u;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < VLOADS; ++i) {
+      const int key = k0 + i * VKPL + vkey;
+      u32x4 u = {0u, 0u, 0u, 0u};
+      if (key < c1) u = *reinterpret_cast<const u32x4*>(vp + (size_t)key * D + 8 * vch);
+      vr[i] = u;
+    }
+  };
+
+  float m[kHeadsPerPass], lp[kHeadsPerPass], o[kHeadsPerPass][8];
+#pragma unroll
+  for (int i = 0; i < kHeadsPerPass; ++i) {
+    m[i] = kNegInf;
+    lp[i] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[i][e] = 0.f;
+  }
+
+  load_step(c0);
+  for (int k0 = c0; k0 < c1; k0 += kKeysPerStep) {
+    // Scores for 32 keys: accumulator element i is head slot i, key k0 + 16 blk + lane % 16.
+    f32x4 sc[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      sc[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < QS; ++s) sc[blk] = mfma_16x16x32(qa[s], as_bf16x8(kr[blk][s]), sc[blk]);
+    }
+    u32x4 vcur[VLOADS];
+#pragma unroll
+    for (int i = 0; i < VLOADS; ++i) vcur[i] = vr[i];
+    if (k0 + kKeysPerStep < c1) load_step(k0 + kKeysPerStep);  // prefetch the next 32 keys
+
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+      if (k0 + 16 * blk + (lane & 15) >= c1) sc[blk] = f32x4{kNegInf, kNegInf, kNegInf, kNegInf};
+
+    float p[2][kHeadsPerPass];
+#pragma unroll
+    for (int i = 0; i < kHeadsPerPass; ++i) {
+      float mx = fmaxf(sc[0][i], sc[1][i]);
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+      const float m_new = fmaxf(m[i], mx * a.scale_log2);  // finite: every step has a visible key
+      const float alpha = exp2_hw(m[i] - m_new);
+      p[0][i] = exp2_hw(fmaf(sc[0][i], a.scale_log2, -m_new));
+      p[1][i] = exp2_hw(fmaf(sc[1][i], a.scale_log2, -m_new));
+      lp[i] = lp[i] * alpha + p[0][i] + p[1][i];
+      m[i] = m_new;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[i][e] *= alpha;
+    }
+
+    __syncthreads();  // the previous step's reads of pl are complete
+    if (lane < 16) {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+        *reinterpret_cast<f32x4*>(&pl[16 * blk + lane][0]) = f32x4{p[blk][0], p[blk][1], p[blk][2], p[blk][3]};
+    }
+    __syncthreads();
+
+#pragma unroll
+    for (int i = 0; i < VLOADS; ++i) {
+      const f32x4 pp = *reinterpret_cast<const f32x4*>(&pl[i * VKPL + vkey][0]);
+      float vf[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        vf[2 * j] = bf16_bits_lo(vcur[i][j]);
+        vf[2 * j + 1] = bf16_bits_hi(vcur[i][j]);
+      }
+#pragma unroll
+      for (int hs = 0; hs < kHeadsPerPass; ++hs)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[hs][e] = fmaf(pp[hs], vf[e], o[hs][e]);
+    }
+  }
+
+  // Reduce the partial sums: o over the lanes holding the same dims, l over the 16 key lanes.
+#pragma unroll
+  for (int hs = 0; hs < kHeadsPerPass; ++hs) {
+#pragma unroll
+    for (int off = NCH; off < 64; off <<= 1)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[hs][e] += __shfl_xor(o[hs][e], off);
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) lp[hs] += __shfl_xor(lp[hs], off);
+  }
+  if (lane < NCH) {
+#pragma unroll
+    for (int hs = 0; hs < kHeadsPerPass; ++hs) {
+      if (hs < nh) {
+        float* dst = a.ws_o + ((size_t)(b * a.H + h0 + hs) * a.nchunk + chunk) * D + 8 * lane;
+        *reinterpret_cast<f32x4*>(dst) = f32x4{o[hs][0], o[hs][1], o[hs][2], o[hs][3]};
+        *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[hs][4], o[hs][5], o[hs][6], o[hs][7]};
+        if (lane == 0) {
+          float* ml = a.ws_ml + ((size_t)(b * a.H + h0 + hs) * a.nchunk + chunk) * 2;
+          ml[0] = m[hs];
+          ml[1] = lp[hs];
+        }
+      }
+    }
+  }
+}
+
+// Merge the chunk states of one (request, head): M = max m_c, L = sum 2^(m_c - M) l_c,
+// O = sum 2^(m_c - M) o_c / L, LSE = ln(2) (M + log2 L). One wave per (request, head).
+template <int D>
+__global__ __launch_bounds__(64) void decode_combine_kernel(const DecArgs a) {
+  constexpr int PER = D / 64;  // dims per lane
+  const int lane = threadIdx.x;
+  const int bh = blockIdx.x;
+  const int b = bh / a.H;
+  const int n = min(max(a.ctx[b], 0), a.Lmax);
+  const int nc = (n + kDecodeChunk - 1) / kDecodeChunk;
+  const float* ml = a.ws_ml + (size_t)bh * a.nchunk * 2;
+  const float* wo = a.ws_o + (size_t)bh * a.nchunk * D;
+
+  float M = kNegInf;
+  for (int c = lane; c < nc; c += 64) M = fmaxf(M, ml[2 * c]);
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
+
+  float L = 0.f, acc[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+  for (int c = 0; c < nc; ++c) {
+    const float wgt = exp2_hw(ml[2 * c] - M);
+    L += wgt * ml[2 * c + 1];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[e] = fmaf(wgt, wo[(size_t)c * D + PER * lane + e], acc[e]);
+  }
+  const bool ok = nc > 0 && L > 0.f;
+  const float inv = ok ? 1.f / L : 0.f;
+  __bf16* op = a.o + (size_t)bh * D + PER * lane;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) op[e] = (__bf16)(ok ? acc[e] * inv : 0.f);
+  if (lane == 0) a.lse[bh] = ok ? (M + __log2f(L)) * kLn2 : kNegInf;
+}
+
+template <int D>
+hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
+  DecArgs a;
+  a.q = static_cast<const __bf16*>(p.q);
+  a.k = static_cast<const __bf16*>(p.k);
+  a.v = static_cast<const __bf16*>(p.v);
+  a.o = static_cast<__bf16*>(p.o);
+  a.lse = p.lse;
+  a.B = p.B; a.H = p.H; a.Hkv = p.Hkv; a.Lmax = p.Lmax;
+  a.group = p.H / p.Hkv;
+  a.nsg = (a.group + kHeadsPerPass - 1) / kHeadsPerPass;
+  a.nchunk = decode_num_chunks(p.Lmax);
+  a.scale_log2 = p.scale * kLog2e;
+  a.ctx = p.ctx_lens;
+  a.ws_o = p.ws_o;
+  a.ws_ml = p.ws_ml;
+  void* args[] = {&a};
+  hipError_t e = hipSuccess;
+  if (a.nchunk > 0) {
+    const long long nx = (long long)p.B * p.Hkv * a.nsg;
+    if (nx > 0x7fffffffLL || a.nchunk > 65535) return hipErrorInvalidConfiguration;
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&decode_split_kernel<D>), dim3((unsigned)nx, a.nchunk),
+                        dim3(64), args, 0, stream);
+    if (e != hipSuccess) return e;
+  }
+  const long long nbh = (long long)p.B * p.H;
+  if (nbh > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  return hipLaunchKernel(reinterpret_cast<const void*>(&decode_combine_kernel<D>), dim3((unsigned)nbh), dim3(64),
+                         args, 0, stream);
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
+  if (p.d == 64) return launch_d<64>(p, stream);
+  return launch_d<128>(p, stream);
+}
+
+}  // namespace fa

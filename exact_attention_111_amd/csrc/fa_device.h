@@ -1,0 +1,69 @@
+// fa_device.h — vector types and small device helpers shared by the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+// 2^x on the hardware transcendental unit (v_exp_f32); 2^-inf = 0.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
+__device__ __forceinline__ u32x4 as_u32x4(bf16x8 v) { return __builtin_bit_cast(u32x4, v); }
+
+// Eight consecutive input elements as bf16 bits. bf16 input is copied; fp32 input is
+// rounded to bf16 with round-to-nearest-even (v_cvt_pk_bf16_f32).
+template <typename T> struct Load8;
+template <> struct Load8<__bf16> {
+  static __device__ __forceinline__ u32x4 load(const __bf16* p) { return *reinterpret_cast<const u32x4*>(p); }
+};
+template <> struct Load8<float> {
+  static __device__ __forceinline__ u32x4 load(const float* p) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+    bf16x8 r;
+    r[0] = (__bf16)a[0]; r[1] = (__bf16)a[1]; r[2] = (__bf16)a[2]; r[3] = (__bf16)a[3];
+    r[4] = (__bf16)b[0]; r[5] = (__bf16)b[1]; r[6] = (__bf16)b[2]; r[7] = (__bf16)b[3];
+    return as_u32x4(r);
+  }
+};
+
+// Four consecutive output elements from fp32 values (bf16 outputs round to nearest even).
+template <typename T> struct Store4;
+template <> struct Store4<__bf16> {
+  static __device__ __forceinline__ void store(__bf16* p, float a, float b, float c, float d) {
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    bf16x4 r;
+    r[0] = (__bf16)a; r[1] = (__bf16)b; r[2] = (__bf16)c; r[3] = (__bf16)d;
+    *reinterpret_cast<u32x2*>(p) = __builtin_bit_cast(u32x2, r);
+  }
+};
+template <> struct Store4<float> {
+  static __device__ __forceinline__ void store(float* p, float a, float b, float c, float d) {
+    f32x4 r = {a, b, c, d};
+    *reinterpret_cast<f32x4*>(p) = r;
+  }
+};
+
+__device__ __forceinline__ float bf16_bits_lo(uint32_t u) { return __builtin_bit_cast(float, u << 16); }
+__device__ __forceinline__ float bf16_bits_hi(uint32_t u) { return __builtin_bit_cast(float, u & 0xffff0000u); }
+
+}  // namespace fa

@@ -1,0 +1,42 @@
+// fa_launch.h — host-side launch entry points of the kernels (internal to libfa).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa {
+
+// Prefill forward. Arguments are already validated; sizes are non-zero.
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, H, Hkv, Lq, Lk, d;
+  float scale;
+  int causal;
+  const int32_t* seqlens;
+};
+hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream);
+hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
+
+// Decode: split kernel over key chunks, then the combine kernel.
+constexpr int kDecodeChunk = 512;  // keys per split partial
+struct DecodeParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, H, Hkv, Lmax, d;
+  float scale;
+  const int32_t* ctx_lens;
+  float* ws_o;   // [B, H, nchunk, d]
+  float* ws_ml;  // [B, H, nchunk, 2]
+};
+inline int decode_num_chunks(int Lmax) { return (Lmax + kDecodeChunk - 1) / kDecodeChunk; }
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,113 @@
+/*
+ * fa.h — C ABI of libfa: exact scaled-dot-product attention on AMD MI355X (gfx950).
+ *
+ * What every entry point computes. For one (batch b, query head h):
+ *
+ *     O = softmax((Q K^T + M) * scale) V,   LSE_i = ln sum_j exp(((Q K^T + M) * scale)_ij)
+ *
+ * following "FlashAttention 与长上下文：先分清三张账" (charles2530.github.io),
+ * section "标准 attention 的问题不只在 FLOPs" (the equation for O, with M a causal or
+ * padding mask), and the same page's section "FlashAttention 的关键是 online softmax"
+ * (running max / sum / unnormalised output per query row, O = o / l at the end, and
+ * the small per-row statistics kept for a backward pass, emitted here as LSE).
+ * The tensors use the [batch, heads, n, d] layout of "2.1 FlashAttention-2 的核心思想"
+ * (aiknowledge.cn) §2.1.1. M takes only the values 0 and -inf:
+ *   - causal: key j is visible to query i iff j <= i + (Lk - Lq) (queries are the
+ *     newest positions; with Lq == Lk this is the usual lower triangle);
+ *   - padding: with per-sequence lengths n_b, keys j >= n_b are hidden and query
+ *     rows i >= n_b are padding, for which O = 0 and LSE = -inf are written.
+ * A query row that sees no key gets O = 0 and LSE = -inf (never NaN).
+ * Query head h reads KV head h / (H / Hkv) (grouped-query attention; contiguous groups).
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers to tensors are DEVICE pointers (HIP device memory) owned by the caller;
+ *     the library never allocates, frees or synchronises on a call.
+ *   - Tensors are dense, row-major, with d innermost; every tensor pointer must be
+ *     16-byte aligned.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and the
+ *     call returns at once. Errors in arguments are detected on the host before
+ *     anything is enqueued, so a failing call writes nothing. Faults during execution
+ *     surface at the caller's next synchronisation.
+ *   - Device-resident lengths (seqlens, ctx_lens) cannot be checked without a
+ *     synchronisation; the kernels clamp each to [0, capacity].
+ *   - Head dimensions 64 and 128 are supported; any other d returns
+ *     FA_ERR_UNSUPPORTED (never a slower fallback path).
+ *   - Calls are reentrant; the library has no global mutable state.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_status {
+  FA_OK = 0,
+  FA_ERR_INVALID = 1,     /* a null/misaligned pointer, a negative size, H % Hkv != 0, ... */
+  FA_ERR_UNSUPPORTED = 2, /* valid request this library does not implement (e.g. d = 96) */
+  FA_ERR_HIP = 3          /* the HIP runtime refused the launch */
+} fa_status;
+
+/*
+ * fa_fwd — prefill / self-attention forward, bf16 in, bf16 out, fp32 accumulation.
+ *
+ *   q   : bf16 [B, H,   Lq, d]     k, v : bf16 [B, Hkv, Lk, d]
+ *   o   : bf16 [B, H,   Lq, d]     lse  : fp32 [B, H, Lq] (natural log)
+ *   scale  : multiplies Q K^T (usually 1/sqrt(d)); must be finite and > 0.
+ *   causal : 0 or 1 (bottom-right aligned, see above).
+ *   seqlens: NULL, or device int32 [B] of per-sequence valid lengths; allowed only
+ *            when Lq == Lk (one length covers both query rows and keys).
+ *   B, H, Lq == 0 is a valid empty call (nothing is enqueued). Lk == 0 writes O = 0 and
+ *   LSE = -inf. Requirements: B, H, Hkv, Lq, Lk >= 0, Hkv >= 1, H % Hkv == 0.
+ * The score and probability matrices are never written to memory; the call needs no
+ * workspace.
+ */
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int Hkv, int Lq, int Lk, int d, float scale, int causal,
+                 const int32_t* seqlens, void* stream);
+
+/*
+ * fa_fwd_f32 — the same contract with fp32 q, k, v and fp32 o. The kernel rounds
+ * q, k, v to bf16 (round-to-nearest-even) as it loads them and multiplies them on the
+ * bf16 matrix cores with fp32 accumulation; O and LSE are produced in fp32.
+ */
+fa_status fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                     int B, int H, int Hkv, int Lq, int Lk, int d, float scale, int causal,
+                     const int32_t* seqlens, void* stream);
+
+/*
+ * fa_decode_workspace_bytes — bytes of device workspace fa_decode needs for a cache of
+ * capacity Lmax (the split partials: one (max, sum, d-vector) per query head and key
+ * chunk). Returns 0 for invalid sizes.
+ */
+size_t fa_decode_workspace_bytes(int B, int H, int Lmax, int d);
+
+/*
+ * fa_decode — one new query token per request against a long KV cache (Lq = 1).
+ *
+ *   q        : bf16 [B, H, d]             k_cache, v_cache : bf16 [B, Hkv, Lmax, d]
+ *   o        : bf16 [B, H, d]             lse              : fp32 [B, H]
+ *   ctx_lens : device int32 [B]; request b attends to cache positions 0 .. ctx_lens[b]-1
+ *              (all of them: the new token is the newest position).
+ *   workspace: device memory of at least fa_decode_workspace_bytes(B, H, Lmax, d) bytes,
+ *              16-byte aligned, owned by the caller; its contents are scratch.
+ * The keys are split into fixed-size chunks; one kernel computes each chunk's partial
+ * (max, sum, unnormalised output) and a second merges the partials of a row with the
+ * two-state merge rule of "2.1 FlashAttention-2 的核心思想" §2.1.3 into O and LSE.
+ * Requirements: B, H >= 0 (0 = empty call), Hkv >= 1, H % Hkv == 0, Lmax >= 0.
+ */
+fa_status fa_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                    int B, int H, int Hkv, int Lmax, int d, float scale, const int32_t* ctx_lens,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* fa_status_string — a static, human-readable name for a status code. */
+const char* fa_status_string(fa_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

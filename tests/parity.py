@@ -1,0 +1,57 @@
+"""Comparison of HIP-path outputs with the fp64 oracle, at the stated tolerance.
+
+Tolerance: O within max-abs 1e-2 and mean-abs 1e-3, LSE within 1e-3 abs, with the
+oracle fed the bf16-rounded inputs. For a bf16 output the rounding of the output
+itself is not counted as error: an element passes when it is within 1e-2 of the exact
+value plus half a bf16 ulp of that value (|O| >= 4 alone has a half ulp of 0.0156), and
+the mean is taken against the oracle rounded to bf16. fp32 outputs are compared with
+the exact value directly. Rows the oracle marks empty (LSE = -inf) must be exactly
+O = 0 and LSE = -inf.
+"""
+import numpy as np
+import torch
+
+O_MAX = 1e-2
+O_MEAN = 1e-3
+LSE_MAX = 1e-3
+
+
+def half_ulp_bf16(x: np.ndarray) -> np.ndarray:
+    """Half the bf16 spacing at |x| (8 significand bits): 2^(e - 9) for |x| in [2^(e-1), 2^e)."""
+    _, e = np.frexp(np.abs(x))
+    return np.where(x == 0, 0.0, np.ldexp(1.0, e - 9))
+
+
+def compare(o_gpu, lse_gpu, O_ref, LSE_ref, *, bf16_out: bool, what: str = ""):
+    """Assert parity; returns a dict of error statistics. Arrays are broadcast-compatible."""
+    o = o_gpu.detach().float().cpu().numpy().astype(np.float64) if torch.is_tensor(o_gpu) else np.asarray(o_gpu)
+    lse = lse_gpu.detach().float().cpu().numpy().astype(np.float64) if torch.is_tensor(lse_gpu) else np.asarray(lse_gpu)
+    O_ref = np.asarray(O_ref, dtype=np.float64)
+    LSE_ref = np.asarray(LSE_ref, dtype=np.float64)
+    assert o.shape == O_ref.shape, (what, o.shape, O_ref.shape)
+    assert lse.shape == LSE_ref.shape, (what, lse.shape, LSE_ref.shape)
+    assert not np.isnan(o).any(), f"{what}: NaN in O"
+    empty = ~np.isfinite(LSE_ref)  # rows that see no key
+    assert np.array_equal(np.isneginf(lse), empty), f"{what}: LSE = -inf rows differ"
+    empty_o = np.broadcast_to(empty[..., None], O_ref.shape)
+    assert np.all(o[empty_o] == 0.0), f"{what}: empty rows must have O = 0"
+    full_o = ~empty_o
+    stats = {"rows": int((~empty).sum())}
+    if not full_o.any():
+        return stats
+    err = np.abs(o - O_ref)[full_o]
+    if bf16_out:
+        excess = (np.abs(o - O_ref) - half_ulp_bf16(O_ref))[full_o]
+        ref_r = torch.from_numpy(np.ascontiguousarray(O_ref)).to(torch.bfloat16).double().numpy()
+        mean = float(np.abs(o - ref_r)[full_o].mean())
+        worst = float(excess.max())
+        assert worst <= O_MAX, f"{what}: O error beyond output rounding {worst:.3g} > {O_MAX}"
+    else:
+        mean = float(err.mean())
+        worst = float(err.max())
+        assert worst <= O_MAX, f"{what}: O max-abs error {worst:.3g} > {O_MAX}"
+    assert mean <= O_MEAN, f"{what}: O mean-abs error {mean:.3g} > {O_MEAN}"
+    lerr = float(np.abs(lse[~empty] - LSE_ref[~empty]).max())
+    assert lerr <= LSE_MAX, f"{what}: LSE error {lerr:.3g} > {LSE_MAX}"
+    stats.update(o_max=worst, o_mean=mean, lse_max=lerr, o_raw_max=float(err.max()))
+    return stats

@@ -1,0 +1,106 @@
+"""The C ABI without a GPU: libfa.so loads, exports every function include/fa.h declares,
+and rejects malformed calls on the host before anything is enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+fa = pytest.importorskip("exact_attention_111_amd")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = fa.lib()
+    names = _declared_functions()
+    assert set(names) == {"fa_fwd", "fa_fwd_f32", "fa_decode", "fa_decode_workspace_bytes", "fa_status_string"}
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    assert fa.status_string(0) == "FA_OK"
+    assert fa.status_string(1) == "FA_ERR_INVALID"
+    assert fa.status_string(2) == "FA_ERR_UNSUPPORTED"
+    assert fa.status_string(3) == "FA_ERR_HIP"
+
+
+# Fake, never-dereferenced device addresses: validation only looks at their values.
+A = 0x10000
+A2 = 0x20000
+MIS = 0x10008  # 8-byte aligned only
+
+
+def _fwd(q=A, k=A, v=A, o=A2, lse=A2, B=1, H=2, Hkv=1, Lq=4, Lk=4, d=64, scale=0.125, causal=0, seqlens=None,
+         fn="fa_fwd"):
+    L = fa.lib()
+    return getattr(L, fn)(q, k, v, o, lse, B, H, Hkv, Lq, Lk, d, scale, causal, seqlens, None)
+
+
+@pytest.mark.parametrize("fn", ["fa_fwd", "fa_fwd_f32"])
+def test_fwd_validation(fn):
+    INV, UNS = fa.binding.FA_ERR_INVALID, fa.binding.FA_ERR_UNSUPPORTED
+    assert _fwd(q=None, fn=fn) == INV
+    assert _fwd(o=None, fn=fn) == INV
+    assert _fwd(lse=None, fn=fn) == INV
+    assert _fwd(k=MIS, fn=fn) == INV
+    assert _fwd(B=-1, fn=fn) == INV
+    assert _fwd(Hkv=0, fn=fn) == INV
+    assert _fwd(H=3, Hkv=2, fn=fn) == INV
+    assert _fwd(scale=0.0, fn=fn) == INV
+    assert _fwd(scale=float("nan"), fn=fn) == INV
+    assert _fwd(scale=float("inf"), fn=fn) == INV
+    assert _fwd(causal=2, fn=fn) == INV
+    assert _fwd(Lq=4, Lk=5, seqlens=A, fn=fn) == INV  # lengths need Lq == Lk
+    assert _fwd(d=96, fn=fn) == UNS
+    assert _fwd(d=256, fn=fn) == UNS
+    assert _fwd(d=0, fn=fn) == INV
+    # Empty calls are valid and enqueue nothing (so they are safe without a GPU).
+    assert _fwd(B=0, fn=fn) == 0
+    assert _fwd(H=0, fn=fn) == 0
+    assert _fwd(Lq=0, Lk=0, fn=fn) == 0
+    assert _fwd(q=None, o=None, lse=None, B=0, fn=fn) == 0
+
+
+def test_decode_workspace_bytes():
+    L = fa.lib()
+    assert L.fa_decode_workspace_bytes(64, 32, 32768, 128) == 64 * 32 * (32768 // 512) * 130 * 4
+    assert L.fa_decode_workspace_bytes(2, 4, 513, 64) == 2 * 4 * 2 * 66 * 4
+    assert L.fa_decode_workspace_bytes(2, 4, 0, 64) == 0
+    assert L.fa_decode_workspace_bytes(-1, 4, 10, 64) == 0
+
+
+def test_decode_validation():
+    L = fa.lib()
+    INV, UNS = fa.binding.FA_ERR_INVALID, fa.binding.FA_ERR_UNSUPPORTED
+    need = L.fa_decode_workspace_bytes(2, 4, 100, 64)
+
+    def call(q=A, k=A, v=A, o=A2, lse=A2, B=2, H=4, Hkv=2, Lmax=100, d=64, scale=0.125, ctx=A, ws=A2, wsb=need):
+        return L.fa_decode(q, k, v, o, lse, B, H, Hkv, Lmax, d, scale, ctx, ws, wsb, None)
+
+    assert call(q=None) == INV
+    assert call(ctx=None) == INV
+    assert call(ws=None) == INV
+    assert call(wsb=need - 1) == INV
+    assert call(ws=MIS) == INV
+    assert call(H=4, Hkv=3) == INV
+    assert call(scale=-1.0) == INV
+    assert call(d=80) == UNS
+    assert call(B=0) == 0
+    assert call(H=0, q=None, o=None, lse=None) == 0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    from exact_attention_111_amd import binding
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setattr(binding, "_LIB_PATH", str(tmp_path / "missing" / "libfa.so"))
+    with pytest.raises(ImportError):
+        binding.lib()
