@@ -43,11 +43,14 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
+                    help="time one part alone (for profiling); prints a short JSON line instead of the bench line")
     return ap.parse_args()
 
 
 def cpu_baseline(w, x, seconds):
-    """Time the fp64 oracle on consecutive 256-row blocks of head (0, 0), newest rows first."""
+    """Time the fp64 oracle on 256-row blocks of query rows, newest rows first, head after
+    head, until about `seconds` of CPU work; report algorithmic TFLOP/s of those rows."""
     import numpy as np
 
     import fa_inputs
@@ -57,25 +60,67 @@ def cpu_baseline(w, x, seconds):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
-    q = fa_inputs.as_oracle_f64(x["q"][0, 0])
-    k = fa_inputs.as_oracle_f64(x["k"][0, 0])
-    v = fa_inputs.as_oracle_f64(x["v"][0, 0])
-    L, d = q.shape
     block = 256
     flops = 0.0
     rows_done = 0
+    heads_touched = 0
     t0 = time.perf_counter()
-    hi = L
-    while hi > 0 and time.perf_counter() - t0 < seconds:
-        rows = np.arange(max(0, hi - block), hi)
-        oracle.attention_head(q, k, v, scale=w.scale, causal=True, rows=rows)
-        flops += 4.0 * d * float((rows + 1).sum())  # visible (query, key) pairs of these rows
-        rows_done += len(rows)
-        hi -= block
+    for h in range(w.H):
+        if time.perf_counter() - t0 >= seconds:
+            break
+        q = fa_inputs.as_oracle_f64(x["q"][0, h])
+        k = fa_inputs.as_oracle_f64(x["k"][0, h * w.Hkv // w.H])
+        v = fa_inputs.as_oracle_f64(x["v"][0, h * w.Hkv // w.H])
+        heads_touched += 1
+        L, d = q.shape
+        hi = L
+        while hi > 0 and time.perf_counter() - t0 < seconds:
+            rows = np.arange(max(0, hi - block), hi)
+            oracle.attention_head(q, k, v, scale=w.scale, causal=True, rows=rows)
+            flops += 4.0 * d * float((rows + 1).sum())  # visible (query, key) pairs of these rows
+            rows_done += len(rows)
+            hi -= block
     dt = time.perf_counter() - t0
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{rows_done} query rows (the last ones) of head 0 of {w.name}, fp64, {dt:.1f} s",
+            "sample": f"{rows_done} query rows over {heads_touched} head(s) of {w.name} (newest rows first), "
+                      f"fp64, {dt:.1f} s",
             "seconds": round(dt, 2)}
+
+
+def run_only(part, steps, warmup):
+    """Time one part alone (for profiling): prefill, decode, or a plain 1 GiB device copy."""
+    import torch
+
+    import exact_attention_111_amd as fa
+    import fa_inputs
+    dev = torch.device("cuda:0")
+    if part == "prefill":
+        w = fa_inputs.WORKLOADS[PREFILL]
+        x = fa_inputs.workload_inputs(w, device=dev)
+        o = torch.empty_like(x["q"])
+        lse = torch.empty((w.B, w.H, w.L), dtype=torch.float32, device=dev)
+        fn = lambda: fa.fwd(x["q"], x["k"], x["v"], causal=True, scale=w.scale, out=o, lse=lse)  # noqa: E731
+    elif part == "decode":
+        w = fa_inputs.WORKLOADS[DECODE]
+        x = fa_inputs.workload_inputs(w, device=dev)
+        o = torch.empty_like(x["q"])
+        lse = torch.empty((w.B, w.H), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(16, fa.decode_workspace_bytes(w.B, w.H, w.L, w.d)), dtype=torch.uint8, device=dev)
+        fn = lambda: fa.decode(x["q"], x["k_cache"], x["v_cache"], x["ctx_lens"], scale=w.scale,  # noqa: E731
+                               workspace=ws, out=o, lse=lse)
+    else:  # a plain copy of 1 GiB: reads 1 GiB and writes 1 GiB per launch
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        fn = lambda: dst.copy_(src)  # noqa: E731
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        a.record(); fn(); b.record()
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in ev]
+    print(json.dumps({"only": part, "steps": steps, "ms_avg": sum(ms) / len(ms), "ms_min": min(ms)}), flush=True)
 
 
 def main():
@@ -83,6 +128,9 @@ def main():
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; run with --gpus 1"}))
         sys.exit(2)
+    if args.only:
+        run_only(args.only, args.steps, args.warmup)
+        return
     import torch
 
     import exact_attention_111_amd as fa
