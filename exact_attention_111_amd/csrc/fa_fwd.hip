@@ -8,33 +8,40 @@
 // o are multiplied by exp(m_old - m_new). At the end O = o / l and the row's log-sum-exp
 // is written. Score and probability tiles never leave the compute unit.
 //
-// gfx950 mapping (one workgroup = 8 wave64s = one 256-row query tile of one head, so two
-// waves share each SIMD and one wave's softmax overlaps the other's matrix products):
-//   * Each wave owns 32 query rows, held in VGPRs as the B operand of
-//     v_mfma_f32_32x32x16_bf16 for the whole kernel.
+// gfx950 mapping. One workgroup = 8 wave64s = one 256-row query tile of one head; wave w
+// owns 32 query rows and runs on SIMD w % 4, so waves w and w + 4 share a SIMD.
+//   * The two wave groups (waves 0-3 and 4-7) run one phase apart ("ping-pong"): in every
+//     phase one group issues matrix products — P V of tile j-1, then S of tile j — while
+//     the other group runs the softmax of its latest S tile on the VALU; a workgroup
+//     barrier separates phases, and the roles swap each phase. The softmax, which costs
+//     about as much issue time as the products at d = 128 (one exp per score element runs
+//     at a quarter of the FMA rate), is thus hidden behind the other wave's MFMAs. The
+//     wave in its product phase raises its issue priority.
+//   * Q rows stay in VGPRs as the B operand of v_mfma_f32_32x32x16_bf16.
 //   * K/V tiles of 64 keys go HBM -> LDS with 16-byte direct-to-LDS loads
-//     (global_load_lds_dwordx4; no VGPR staging, no VALU work), double buffered so the
-//     next tile streams in while the current one is used; one barrier per tile.
-//     Both tiles stay row major; 16-byte chunks are XOR-swizzled per row so that the
-//     operand reads below spread over the LDS banks.
-//   * S^T = K Q^T (keys down, queries across): in the 32x32 accumulator layout a lane
-//     holds one query column, so a row's max, sum and rescale factor live in that lane
-//     (plus lane ^ 32, one exchange per tile for the max).
-//   * O^T = V^T P^T with P taken straight from the accumulators (converted to bf16) and
-//     V^T operands read from the row-major V tile with ds_read_b64_tr_b16, whose 16-lane
-//     transpose turns 4 rows x 4 dims into the 4-keys-per-lane operand layout. The
+//     (global_load_lds_dwordx4; no VGPR staging, no VALU work). K runs one tile ahead of V;
+//     both are double buffered and loads have two phases to land.
+//   * S^T = K Q^T (keys down, queries across): in the 32x32 accumulator layout a lane holds
+//     one query column, so a row's max, sum and rescale factor live in that lane (plus
+//     lane ^ 32, one exchange per tile for the max).
+//   * O^T = V^T P^T with P taken straight from the accumulators (converted to bf16) and the
+//     V^T operand read from the row-major V tile with ds_read_b64_tr_b16 (its 16-lane
+//     transpose turns 4 rows x 4 dims into the 4-keys-per-lane operand layout). The
 //     contraction index of that product is ordered to match the accumulator layout.
-//   * exp is 2^x on v_exp_f32 with scale*log2(e) folded into one FMA.
-//   * A row's reference maximum is raised only when a tile's maximum exceeds it by more
-//     than 2^8 (then o and l are rescaled); otherwise the tile's probabilities are taken
-//     against the old reference and can be up to 256. The result o / l does not depend on
-//     the reference, so this only skips rescaling work.
+//   * LDS rows are XOR-swizzled in 16-byte chunks so that both operand reads are free of
+//     bank conflicts on gfx950's LDS (128-bit reads are served 16 lanes at a time); every
+//     operand address is computed once per lane and reused with immediate offsets.
+//   * exp is 2^x on v_exp_f32 with scale*log2(e) folded into one FMA. A row's reference
+//     maximum is raised only when a tile's maximum exceeds it by more than 2^8 (then o and
+//     l are rescaled); o / l does not depend on the reference, so this only skips work.
 //   * Causal and padding masks are applied element-wise only on tiles that straddle the
 //     diagonal or the sequence end; a wave skips tiles none of its rows can see, and key
 //     tiles past the query tile's last visible key are never loaded.
 //   * Workgroups are renumbered so that the ones dispatched to the same XCD (dispatch is
 //     round-robin over the 8 XCDs) work on the same head at the same time and share its
 //     K/V through that XCD's L2; within a head the heaviest (latest) query tiles go first.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -77,25 +84,30 @@ struct FwdArgs {
   const int32_t* seqlens;
 };
 
-// Byte offset of 16-byte chunk `c` of tile row `r`; K and V use different XOR swizzles.
-//   K: chunk ^ (r & 7): the 8 lanes of a 128-bit read (8 consecutive rows, same chunk)
-//      hit 8 different bank groups.
-//   V: chunk ^ 2 (r & 3): a 16-lane transposed read touches 4 consecutive rows x one
-//      32-byte chunk pair; the swizzle keeps the pair together and moves it per row.
+// XOR applied to the 16-byte chunk index of tile row r.
+//   K (read by 16 lanes = 16 consecutive rows, same logical chunk): every row of a 16-row
+//   group must land on a different 16-byte bank slot of the 256-byte bank window.
+//   V (read transposed: a 16-lane group touches 4 consecutive rows x one 32-byte chunk pair,
+//   two groups per access): the 8 (row, pair) slots of an access must differ.
 template <int D>
-__device__ __forceinline__ int k_off(int r, int c) { return r * (D * 2) + ((c ^ (r & 7)) << 4); }
+__device__ __forceinline__ int k_xor(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
 template <int D>
-__device__ __forceinline__ int v_off(int r, int c) { return r * (D * 2) + ((c ^ ((r & 3) << 1)) << 4); }
+__device__ __forceinline__ int v_xor(int r) {
+  const int j = r & 3;
+  return D == 128 ? 2 * (j ^ ((j & 1) << 2)) : ((j & 2) << 1);
+}
 
 template <int D, typename IT, typename OT>
 __global__ __launch_bounds__(512) void fwd_kernel(const FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   using C = FwdCfg<D>;
-  __shared__ __attribute__((aligned(1024))) char smem[2][2][C::TILE_BYTES];  // [buffer][K, V]
+  // [K slot 0 | K slot 1 | V slot 0 | V slot 1 | V slot 2]
+  __shared__ __attribute__((aligned(1024))) char smem[5 * C::TILE_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, provably uniform
+  const int grp = w >> 2;                                  // ping-pong group
   const int col = lane & 31;   // this lane's query row within the wave
   const int half = lane >> 5;  // which 8-element half of a 16-wide k-step
 
@@ -144,6 +156,21 @@ __global__ __launch_bounds__(512) void fwd_kernel(const FwdArgs a) {
     qf[ks] = as_bf16x8(u);
   }
 
+  // Operand addresses, computed once. K: lane reads row kb*32 + col, logical chunk
+  // 2*ks + half. V (transposed read): lane (g, sl) = (lane / 16, lane % 16) reads row
+  // 16*ks + 8*rr + 4*(g/2) + sl/4, dims 32*nb + 16*(g%2) + 4*(sl%4) .. +3.
+  int kaddr[C::QKS];
+#pragma unroll
+  for (int ks = 0; ks < C::QKS; ++ks) kaddr[ks] = col * C::ROWB + (((2 * ks + half) ^ k_xor<D>(col)) << 4);
+  const int g = lane >> 4, sl = lane & 15;
+  const int vrow = 4 * (g >> 1) + (sl >> 2);
+  int vaddr[C::NB];
+#pragma unroll
+  for (int nb = 0; nb < C::NB; ++nb) {
+    const int dim = 32 * nb + 16 * (g & 1) + 4 * (sl & 3);
+    vaddr[nb] = vrow * C::ROWB + (((dim >> 3) ^ v_xor<D>(vrow)) << 4) + ((dim & 4) << 1);
+  }
+
   f32x16 oacc[C::NB];
 #pragma unroll
   for (int nb = 0; nb < C::NB; ++nb)
@@ -151,11 +178,22 @@ __global__ __launch_bounds__(512) void fwd_kernel(const FwdArgs a) {
     for (int r = 0; r < 16; ++r) oacc[nb][r] = 0.f;
   float m = kNegInf;  // reference max (scaled, base 2) of this lane's row
   float l = 0.f;      // this lane's part of the running sum (the other part is in lane ^ 32)
+  f32x16 s[2];        // S^T of the latest tile, two 32-key halves
+  bf16x8 pb[4];       // P^T of the latest tile as PV operands
+  float alpha = 1.f;  // rescale of o decided by the softmax phase, applied by the next product phase
+  bool rescale = false;
 
-  // Stage key tile t into buffer `buf`. Keys past kv_end read row kv_end - 1 instead (always
-  // a visible, finite row); the mask gives them probability 0.
-  auto stage = [&](int t, int buf) {
+  // LDS: K tiles double buffered (K tile t in slot t % 2), V tiles triple buffered (slot
+  // t % 3), so that V tile t is resident one phase before the product phase that reads it.
+  auto k_slot = [&](int t) { return (t & 1) * C::TILE_BYTES; };
+  auto v_slot = [&](int t) { return (2 + t % 3) * C::TILE_BYTES; };
+
+  // Stage K tile t (which = 0) or V tile t (which = 1). Keys past kv_end read row
+  // kv_end - 1 instead (a visible, finite row); the mask gives them p = 0.
+  auto stage = [&](int t, int which) {
     const int k0 = t * C::BN;
+    char* dst = smem + (which ? v_slot(t) : k_slot(t));
+    const IT* src = which ? vp : kp;
     if constexpr (sizeof(IT) == 2) {
 #pragma unroll
       for (int i = 0; i < C::SEGS_PER_WAVE; ++i) {
@@ -164,10 +202,8 @@ __global__ __launch_bounds__(512) void fwd_kernel(const FwdArgs a) {
         const int r = byte / C::ROWB;
         const int cp = (byte - r * C::ROWB) >> 4;  // physical chunk this lane fills
         const int key = min(k0 + r, kv_end - 1);
-        const IT* ksrc = kp + (size_t)key * D + ((cp ^ (r & 7)) << 3);
-        const IT* vsrc = vp + (size_t)key * D + ((cp ^ ((r & 3) << 1)) << 3);
-        __builtin_amdgcn_global_load_lds(ksrc, (lds_void*)(&smem[buf][0][seg * 1024]), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vsrc, (lds_void*)(&smem[buf][1][seg * 1024]), 16, 0, 0);
+        const int cl = cp ^ (which ? v_xor<D>(r) : k_xor<D>(r));
+        __builtin_amdgcn_global_load_lds(src + (size_t)key * D + (cl << 3), (lds_void*)(dst + seg * 1024), 16, 0, 0);
       }
     } else {
       // fp32 input: load, round to bf16 (RNE) in registers, store into the same layout.
@@ -178,126 +214,177 @@ __global__ __launch_bounds__(512) void fwd_kernel(const FwdArgs a) {
         const int r = idx / CH;
         const int c = idx - r * CH;
         const int key = min(k0 + r, kv_end - 1);
-        *reinterpret_cast<u32x4*>(&smem[buf][0][k_off<D>(r, c)]) = Load8<IT>::load(kp + (size_t)key * D + 8 * c);
-        *reinterpret_cast<u32x4*>(&smem[buf][1][v_off<D>(r, c)]) = Load8<IT>::load(vp + (size_t)key * D + 8 * c);
+        const int cp = c ^ (which ? v_xor<D>(r) : k_xor<D>(r));
+        *reinterpret_cast<u32x4*>(dst + r * C::ROWB + (cp << 4)) = Load8<IT>::load(src + (size_t)key * D + 8 * c);
       }
     }
   };
 
-  if (ntk > 0) {
-    stage(0, 0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  }
-  for (int t = 0; t < ntk; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntk) stage(t + 1, buf ^ 1);  // streams in while this tile is used
+  // Does this wave see any key of tile t?
+  auto active = [&](int t) { return (qw0 < n_q) && !(a.causal && t * C::BN > qw0 + 31 + delta); };
 
-    const int k0 = t * C::BN;
-    const bool active = (qw0 < n_q) && !(a.causal && k0 > qw0 + 31 + delta);
-    if (active) {
-      const char* Kt = smem[buf][0];
-      const char* Vt = smem[buf][1];
-      const bool need_mask = (k0 + C::BN > n_kv) || (a.causal && k0 + C::BN - 1 > qw0 + delta);
+  // Operand reads. PV product i (k-step i / NB, block i % NB) of a tile whose V sits in
+  // slot `vs`: two transposed 64-bit reads. S product i of a tile whose K sits in slot
+  // `ksl`: one 128-bit read of half i / QKS, k-step i % QKS.
+  auto read_v = [&](int vs, int i) {
+    const int ks = i / C::NB, nb = i % C::NB;
+    const s16x4 p0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)(smem + vaddr[nb] + vs + (16 * ks) * C::ROWB));
+    const s16x4 p1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)(smem + vaddr[nb] + vs + (16 * ks + 8) * C::ROWB));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(p0, p1, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  auto read_k = [&](int ksl, int i) {
+    return *reinterpret_cast<const bf16x8*>(smem + kaddr[i % C::QKS] + ksl + (i / C::QKS) * 32 * C::ROWB);
+  };
 
-      // S^T = K Q^T for the two 32-key halves of the tile. All 2*QKS operand reads are
-      // issued before the first product so LDS latency is paid once per tile.
-      bf16x8 kf[2][C::QKS];
+  // Product phase for tile j: one chain of MFMAs, O^T += V^T P^T of tile j - 1 (NPV
+  // products) followed by S^T = K Q^T of tile j (NSP products), with every operand read
+  // PF products ahead and the first PF V operands already read at the end of the
+  // previous softmax phase (vpre). Scheduling groups pin the interleaving. The chain always
+  // runs whole: where tile j - 1 gives this wave nothing (j = 0, or no visible key) P is
+  // zero and V is a resident tile of finite values, so the products add exact zeros; where
+  // tile j does not exist or is invisible, S is computed and never read.
+  constexpr int PF = 4;
+  constexpr int NPV = 4 * C::NB;   // 16 at d = 128
+  constexpr int NSP = 2 * C::QKS;  // 16 at d = 128
+  constexpr int N = NPV + NSP;
+  bf16x8 vpre[PF];
+  auto product_phase = [&](int j) {
+    // Keep the per-lane operand bases opaque to loop-invariant code motion: otherwise every
+    // (base + immediate offset) pair is hoisted out of the phase loop into its own VGPR.
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int ks = 0; ks < C::QKS; ++ks) asm volatile("" : "+v"(kaddr[ks]));
 #pragma unroll
-        for (int ks = 0; ks < C::QKS; ++ks)
-          kf[kb][ks] = *reinterpret_cast<const bf16x8*>(Kt + k_off<D>(kb * 32 + col, 2 * ks + half));
-      __builtin_amdgcn_sched_barrier(0);
-      f32x16 s[2];
+    for (int nb = 0; nb < C::NB; ++nb) asm volatile("" : "+v"(vaddr[nb]));
+    __builtin_amdgcn_s_setprio(1);
+    if (rescale) {  // wave-uniform; rare once a row's maximum has settled
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+        for (int r = 0; r < 16; ++r) oacc[nb][r] *= alpha;
+      rescale = false;
+    }
+    const int vs = v_slot(max(j - 1, 0));
+    const int ksl = k_slot(j);
+    bf16x8 buf[PF];
 #pragma unroll
-        for (int ks = 0; ks < C::QKS; ++ks) s[kb] = mfma_32x32x16(kf[kb][ks], qf[ks], s[kb]);
-      }
-      // Accumulator element r of half kb is key k0 + 32*kb + 8*(r/4) + 4*half + r%4, query my_q.
-      if (need_mask) {
+    for (int f = 0; f < PF; ++f) buf[f] = vpre[f];
+    const f32x16 zero = {};
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
-            const bool vis = key < n_kv && (!a.causal || key <= my_q + delta);
-            if (!vis) s[kb][r] = kNegInf;
-          }
-      }
-
-      // Online softmax with a lazily raised reference max (base 2, scaled).
-      float mx = kNegInf;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
-      const bool raise = mx > m + kLazyRescale;  // also true for the first visible tile
-      if (__builtin_amdgcn_ballot_w64(raise)) {
-        const float m_new = raise ? mx : m;
-        const float alpha = raise ? exp2_hw(m - m_new) : 1.f;
-        l *= alpha;
-#pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[nb][r] *= alpha;
-        m = m_new;
-      }
-      const float neg_m = (m == kNegInf) ? 0.f : -m;  // a row that has seen nothing keeps p = 0
-
-      bf16x8 pb[4];
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float p = exp2_hw(fmaf(s[kb][8 * hh + e], a.scale_log2, neg_m));
-            rs += p;
-            pb[2 * kb + hh][e] = (__bf16)p;
-          }
-      l += rs;
-
-      // O^T += V^T P^T. k-step ks uses accumulator registers 8*(ks%2) .. +7 of half ks/2,
-      // i.e. keys 16*ks + 8*(e/4) + 4*half + e%4 for element e. The transposed read gives
-      // lane (16 g + j) the 4 keys 16*ks + 8*rr + 4*(g/2) + u at dim 32*nb + 16*(g%2) + j
-      // when its source lanes s = 0..15 point at row 16*ks + 8*rr + 4*(g/2) + s/4,
-      // dims 32*nb + 16*(g%2) + 4*(s%4) .. +3.
-      const int g = lane >> 4, sl = lane & 15;
-      auto read_v = [&](int ks, int nb) {
-        s16x4 part[2];
-#pragma unroll
-        for (int rr = 0; rr < 2; ++rr) {
-          const int row = 16 * ks + 8 * rr + 4 * (g >> 1) + (sl >> 2);
-          const int dim = 32 * nb + 16 * (g & 1) + 4 * (sl & 3);
-          const int off = v_off<D>(row, dim >> 3) + ((dim & 4) << 1);
-          part[rr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(Vt + off));
-        }
-        const s16x4 p0 = part[0], p1 = part[1];
-        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(p0, p1, 0, 1, 2, 3, 4, 5, 6, 7));
-      };
-      // Operands of k-step ks + 1 are read while k-step ks multiplies.
-      bf16x8 vf[2][C::NB];
-#pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb) vf[0][nb] = read_v(0, nb);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        if (ks + 1 < 4) {
-#pragma unroll
-          for (int nb = 0; nb < C::NB; ++nb) vf[(ks + 1) & 1][nb] = read_v(ks + 1, nb);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb) oacc[nb] = mfma_32x32x16(vf[ks & 1][nb], pb[ks], oacc[nb]);
+    for (int i = 0; i < N; ++i) {
+      const bf16x8 x = buf[i % PF];
+      const int nx = i + PF;
+      if (nx < N) buf[i % PF] = nx < NPV ? read_v(vs, nx) : read_k(ksl, nx - NPV);
+      if (i < NPV) {
+        oacc[i % C::NB] = mfma_32x32x16(x, pb[i / C::NB], oacc[i % C::NB]);
+      } else {
+        const int ii = i - NPV, kb = ii / C::QKS, ks = ii % C::QKS;
+        s[kb] = mfma_32x32x16(x, qf[ks], ks == 0 ? zero : s[kb]);
       }
     }
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of the next tile have landed
-    __syncthreads();                // ... everyone's have, and nobody reads `buf` any more
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int nx = i + PF;
+      if (nx < NPV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);       // two transposed reads
+      else if (nx < N) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one 128-bit read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // one MFMA
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  // Softmax phase for tile j: mask, online max / rescale, P = 2^(S*c - m), row sums.
+  auto softmax_phase = [&](int j) {
+    if (!(j >= 0 && j < ntk && active(j))) {  // nothing visible: the next PV chain adds zeros
+#pragma unroll
+      for (int q = 0; q < 4; ++q) pb[q] = bf16x8{};
+      return;
+    }
+    const int k0 = j * C::BN;
+    const bool need_mask = (k0 + C::BN > n_kv) || (a.causal && k0 + C::BN - 1 > qw0 + delta);
+    // Accumulator element r of half kb is key k0 + 4*half + (32*kb + 8*(r/4) + r%4), query
+    // my_q; it is visible when that constant offset is below both per-lane limits.
+    if (need_mask) {
+      const int base = k0 + 4 * half;
+      const int lim = min(n_kv - base, a.causal ? my_q + delta + 1 - base : n_kv - base);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (32 * kb + 8 * (r >> 2) + (r & 3) >= lim) s[kb][r] = kNegInf;
+    }
+    // Row max and row sum are taken as four independent partial chains (short dependency
+    // chains; the order of a max does not matter, the sum's grouping is fixed here).
+    float mp[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mp[r & 3] = fmaxf(mp[r & 3], s[kb][r]);
+    float mx = fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
+    {  // lanes l and l ^ 32 hold the same row: exchange halves with v_permlane32_swap
+      const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, mx), __builtin_bit_cast(unsigned, mx),
+                                                       false, false);
+      mx = fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1])) * a.scale_log2;
+    }
+    const bool raise = mx > m + kLazyRescale;  // also true for the first visible tile
+    if (__builtin_amdgcn_ballot_w64(raise)) {
+      const float m_new = raise ? mx : m;
+      alpha = raise ? exp2_hw(m - m_new) : 1.f;
+      l *= alpha;
+      m = m_new;
+      rescale = true;
+    }
+    const float neg_m = (m == kNegInf) ? 0.f : -m;  // a row that has seen nothing keeps p = 0
+    float rs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p = exp2_hw(fmaf(s[kb][8 * hh + e], a.scale_log2, neg_m));
+          rs[e & 3] += p;
+          pb[2 * kb + hh][e] = (__bf16)p;
+        }
+    l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+  };
+
+  // First V operands of the PV chain of tile i (read at the end of its softmax phase).
+  auto pre_read_v = [&](int i) {
+#pragma unroll
+    for (int f = 0; f < PF; ++f) vpre[f] = read_v(v_slot(i), f);
+  };
+
+  if (ntk > 0) {
+    stage(0, 0);
+    stage(0, 1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) pb[q] = bf16x8{};
+    pre_read_v(0);
+    // Global phases are separated by workgroup barriers. Every wave runs the same body per
+    // tile i: its product phase, a barrier, its softmax phase, a barrier. Group 1 starts one
+    // phase late (a leading barrier) and so runs each softmax beside group 0's next product
+    // phase. K and V tile i + 1 are loaded in global phase 2i (group 0: before product i;
+    // group 1: before softmax i - 1) and every wave waits for its own loads at the end of
+    // phase 2i + 1, before the barrier that opens phase 2i + 2.
+    if (grp == 1) {
+      if (1 < ntk) { stage(1, 0); stage(1, 1); }
+      lds_barrier();
+    }
+    for (int i = 0; i <= ntk; ++i) {
+      if (grp == 0 && i + 1 < ntk) { stage(i + 1, 0); stage(i + 1, 1); }
+      product_phase(i);
+      if (grp == 1) __builtin_amdgcn_s_waitcnt(0);
+      lds_barrier();
+      if (grp == 1 && i + 2 < ntk) { stage(i + 2, 0); stage(i + 2, 1); }
+      softmax_phase(i);
+      if (i < ntk) pre_read_v(i);
+      if (grp == 0) __builtin_amdgcn_s_waitcnt(0);
+      if (grp == 0 || i < ntk) lds_barrier();
+    }
   }
 
   // Epilogue: O = o / l and LSE = ln(2) * (m + log2 l); padding rows and rows that saw
