@@ -34,6 +34,33 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4): lane i
+// lands at lds_byte_addr + 16 * i. Issued as inline assembly so that the compiler does not
+// track it: otherwise it cannot tell which LDS bytes are being written and stalls every
+// later LDS read until the load completes. Callers must therefore wait for completion
+// themselves (s_waitcnt vmcnt(0)) before the barrier that publishes the data. M0 carries
+// the LDS base; nothing else in these kernels uses M0.
+__device__ __forceinline__ void lds_dma16(const void* gptr, unsigned lds_byte_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds_byte_addr))
+               : "memory");
+}
+
+// Wait until at most N vector-memory loads of this wave are outstanding (they complete in
+// issue order). Encoding (gfx9 family): vmcnt in bits [3:0] and [15:14]; expcnt [6:4] and
+// lgkmcnt [11:8] left at their maxima, i.e. not waited for.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Byte address of a pointer into LDS.
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
 __device__ __forceinline__ u32x4 as_u32x4(bf16x8 v) { return __builtin_bit_cast(u32x4, v); }
 

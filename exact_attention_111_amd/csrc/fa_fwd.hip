@@ -8,22 +8,25 @@
 // o are multiplied by exp(m_old - m_new). At the end O = o / l and the row's log-sum-exp
 // is written. Score and probability tiles never leave the compute unit.
 //
-// gfx950 mapping. One workgroup = 8 wave64s = one 256-row query tile of one head; wave w
-// owns 32 query rows and runs on SIMD w % 4, so waves w and w + 4 share a SIMD.
-//   * The two wave groups (waves 0-3 and 4-7) run one phase apart ("ping-pong"): in every
-//     phase one group issues matrix products — P V of tile j-1, then S of tile j — while
-//     the other group runs the softmax of its latest S tile on the VALU; a workgroup
-//     barrier separates phases, and the roles swap each phase. The softmax, which costs
-//     about as much issue time as the products at d = 128 (one exp per score element runs
-//     at a quarter of the FMA rate), is thus hidden behind the other wave's MFMAs. The
-//     wave in its product phase raises its issue priority.
-//   * Q rows stay in VGPRs as the B operand of v_mfma_f32_32x32x16_bf16.
-//   * K/V tiles of 64 keys go HBM -> LDS with 16-byte direct-to-LDS loads
-//     (global_load_lds_dwordx4; no VGPR staging, no VALU work). K runs one tile ahead of V;
-//     both are double buffered and loads have two phases to land.
+// gfx950 mapping. One workgroup = one 256-row query tile of one head. At d = 128 it is 8
+// wave64s of 32 query rows (two waves per SIMD, so a wave fits in 256 VGPRs); at d = 64 it
+// is 4 wave64s of 64 rows (two 32-row blocks each, one wave per SIMD).
+//   * Software pipeline inside each wave, one workgroup barrier per 64-key tile. The body
+//     for tile j has two regions, each a single straight run of code that the scheduler
+//     interleaves: (X) the MFMAs of S for tile j + 1 beside the exp / row-sum / bf16
+//     conversion of tile j, then (Y) the MFMAs of P V for tile j beside the mask / row-max /
+//     scale-and-shift of tile j + 1. The matrix cores run while the same wave issues its
+//     softmax arithmetic, so the softmax costs issue slots, not a serial phase.
+//   * Q rows stay in registers as the B operand of v_mfma_f32_32x32x16_bf16; every K or V
+//     operand read from LDS feeds both 32-row blocks (two MFMAs), halving LDS reads per MFMA
+//     compared with 32 rows per wave.
+//   * K/V tiles go HBM -> LDS with 16-byte direct-to-LDS loads (global_load_lds_dwordx4; no
+//     VGPR staging, no VALU work), double buffered, K one tile ahead of V. They are issued
+//     so that the compiler does not see them (it would otherwise make every LDS read wait
+//     for them); each wave waits for its own loads before the barrier that closes a tile.
 //   * S^T = K Q^T (keys down, queries across): in the 32x32 accumulator layout a lane holds
 //     one query column, so a row's max, sum and rescale factor live in that lane (plus
-//     lane ^ 32, one exchange per tile for the max).
+//     lane ^ 32, exchanged with v_permlane32_swap).
 //   * O^T = V^T P^T with P taken straight from the accumulators (converted to bf16) and the
 //     V^T operand read from the row-major V tile with ds_read_b64_tr_b16 (its 16-lane
 //     transpose turns 4 rows x 4 dims into the 4-keys-per-lane operand layout). The
@@ -35,8 +38,9 @@
 //     maximum is raised only when a tile's maximum exceeds it by more than 2^8 (then o and
 //     l are rescaled); o / l does not depend on the reference, so this only skips work.
 //   * Causal and padding masks are applied element-wise only on tiles that straddle the
-//     diagonal or the sequence end; a wave skips tiles none of its rows can see, and key
-//     tiles past the query tile's last visible key are never loaded.
+//     diagonal or the sequence end, and key tiles past the query tile's last visible key are
+//     never loaded. Tiles a wave cannot see at all are still multiplied (with P = 0): the
+//     pipeline stays branch-free at the price of a few MFMAs near the diagonal.
 //   * Workgroups are renumbered so that the ones dispatched to the same XCD (dispatch is
 //     round-robin over the 8 XCDs) work on the same head at the same time and share its
 //     K/V through that XCD's L2; within a head the heaviest (latest) query tiles go first.
@@ -54,9 +58,14 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 template <int D>
 struct FwdCfg {
-  static constexpr int BM = 256;                  // query rows per workgroup
+  // d = 128: 32 rows per wave (a wave fits in 256 VGPRs) and 8 waves, two per SIMD.
+  // d = 64: 64 rows per wave and 4 waves, one per SIMD. Either way a workgroup covers 256
+  // query rows, which sets how often each K/V tile is streamed from L2 into LDS.
+  static constexpr int QB = D == 128 ? 1 : 2;     // 32-row query blocks per wave
+  static constexpr int NW = D == 128 ? 8 : 4;     // waves per workgroup
+  static constexpr int BM = 32 * QB * NW;         // query rows per workgroup (256)
+  static constexpr int WAVES_PER_SIMD = NW / 4;
   static constexpr int BN = 64;                   // keys per tile
-  static constexpr int NW = 8;                    // waves
   static constexpr int NT = NW * 64;              // threads
   static constexpr int ROWB = D * 2;              // bytes per K/V row
   static constexpr int TILE_BYTES = BN * ROWB;    // one K (or V) tile
@@ -64,10 +73,13 @@ struct FwdCfg {
   static constexpr int SEGS_PER_WAVE = SEGS / NW;
   static constexpr int QKS = D / 16;              // 32x32x16 k-steps over d
   static constexpr int NB = D / 32;               // 32-row blocks of O^T
+  static constexpr int NKF = 2 * QKS;             // K operands per tile (2 key halves x QKS)
+  static constexpr int NVF = 4 * NB;              // V operands per tile (4 k-steps x NB)
   static_assert(SEGS % NW == 0, "tile must split evenly over the waves");
 };
 
 constexpr float kLazyRescale = 8.0f;  // log2 of the largest probability allowed before rescaling
+constexpr int kPF = 4;                // operand reads issued this many operands ahead
 
 struct FwdArgs {
   const void* q;
@@ -98,17 +110,18 @@ __device__ __forceinline__ int v_xor(int r) {
 }
 
 template <int D, typename IT, typename OT>
-__global__ __launch_bounds__(512) void fwd_kernel(const FwdArgs a) {
+__global__ __launch_bounds__(FwdCfg<D>::NT)
+__attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_PER_SIMD))) void fwd_kernel(const FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   using C = FwdCfg<D>;
-  // [K slot 0 | K slot 1 | V slot 0 | V slot 1 | V slot 2]
-  __shared__ __attribute__((aligned(1024))) char smem[5 * C::TILE_BYTES];
+  constexpr int QB = C::QB;
+  // [K slots 0-2 | V slots 0-2]
+  __shared__ __attribute__((aligned(1024))) char smem[6 * C::TILE_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, provably uniform
-  const int grp = w >> 2;                                  // ping-pong group
-  const int col = lane & 31;   // this lane's query row within the wave
+  const int col = lane & 31;   // this lane's query row within a 32-row block
   const int half = lane >> 5;  // which 8-element half of a 16-wide k-step
 
   // XCD-aware renumbering: hardware id i runs on XCD i % 8; give each XCD a contiguous
@@ -131,8 +144,10 @@ __global__ __launch_bounds__(512) void fwd_kernel(const FwdArgs a) {
   }
   const int delta = a.Lk - a.Lq;  // bottom-right causal alignment
   const int q0 = qt * C::BM;
-  const int qw0 = q0 + 32 * w;
-  const int my_q = qw0 + col;
+  const int qw0 = q0 + 32 * QB * w;  // first query row of this wave
+  int my_q[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) my_q[qb] = qw0 + 32 * qb + col;
 
   // Keys this query tile can see: [0, kv_end).
   int kv_end = 0;
@@ -148,13 +163,15 @@ __global__ __launch_bounds__(512) void fwd_kernel(const FwdArgs a) {
   const IT* __restrict__ vp = static_cast<const IT*>(a.v) + (size_t)(b * a.Hkv + kvh) * a.Lk * D;
 
   // Q rows of this lane as MFMA B operands: element t of k-step ks is d = 16*ks + 8*half + t.
-  bf16x8 qf[C::QKS];
+  bf16x8 qf[QB][C::QKS];
 #pragma unroll
-  for (int ks = 0; ks < C::QKS; ++ks) {
-    u32x4 u = {0u, 0u, 0u, 0u};
-    if (my_q < n_q && ntk > 0) u = Load8<IT>::load(qp + (size_t)my_q * D + 16 * ks + 8 * half);
-    qf[ks] = as_bf16x8(u);
-  }
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int ks = 0; ks < C::QKS; ++ks) {
+      u32x4 u = {0u, 0u, 0u, 0u};
+      if (my_q[qb] < n_q && ntk > 0) u = Load8<IT>::load(qp + (size_t)my_q[qb] * D + 16 * ks + 8 * half);
+      qf[qb][ks] = as_bf16x8(u);
+    }
 
   // Operand addresses, computed once. K: lane reads row kb*32 + col, logical chunk
   // 2*ks + half. V (transposed read): lane (g, sl) = (lane / 16, lane % 16) reads row
@@ -171,22 +188,27 @@ __global__ __launch_bounds__(512) void fwd_kernel(const FwdArgs a) {
     vaddr[nb] = vrow * C::ROWB + (((dim >> 3) ^ v_xor<D>(vrow)) << 4) + ((dim & 4) << 1);
   }
 
-  f32x16 oacc[C::NB];
+  f32x16 oacc[QB][C::NB];
 #pragma unroll
-  for (int nb = 0; nb < C::NB; ++nb)
+  for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[nb][r] = 0.f;
-  float m = kNegInf;  // reference max (scaled, base 2) of this lane's row
-  float l = 0.f;      // this lane's part of the running sum (the other part is in lane ^ 32)
-  f32x16 s[2];        // S^T of the latest tile, two 32-key halves
-  bf16x8 pb[4];       // P^T of the latest tile as PV operands
-  float alpha = 1.f;  // rescale of o decided by the softmax phase, applied by the next product phase
-  bool rescale = false;
+    for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[qb][nb][r] = 0.f;
+  float m[QB], l[QB], alpha[QB];  // reference max (scaled, base 2), this lane's part of the sum
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m[qb] = kNegInf;
+    l[qb] = 0.f;
+    alpha[qb] = 1.f;
+  }
+  bool rescale = false;  // o must be multiplied by alpha before the next P V
+  f32x16 sa[QB][2], sb[QB][2];  // S^T (then scaled, shifted scores) of two consecutive tiles
+  bf16x8 pb[QB][4];              // P^T of the tile whose P V runs next
 
-  // LDS: K tiles double buffered (K tile t in slot t % 2), V tiles triple buffered (slot
-  // t % 3), so that V tile t is resident one phase before the product phase that reads it.
-  auto k_slot = [&](int t) { return (t & 1) * C::TILE_BYTES; };
-  auto v_slot = [&](int t) { return (2 + t % 3) * C::TILE_BYTES; };
+  // K and V tile t live in slot t % 3, so loads can run two tiles ahead of their use.
+  auto k_slot = [&](int t) { return (t % 3) * C::TILE_BYTES; };
+  auto v_slot = [&](int t) { return (3 + t % 3) * C::TILE_BYTES; };
 
   // Stage K tile t (which = 0) or V tile t (which = 1). Keys past kv_end read row
   // kv_end - 1 instead (a visible, finite row); the mask gives them p = 0.
@@ -203,7 +225,7 @@ __global__ __launch_bounds__(512) void fwd_kernel(const FwdArgs a) {
         const int cp = (byte - r * C::ROWB) >> 4;  // physical chunk this lane fills
         const int key = min(k0 + r, kv_end - 1);
         const int cl = cp ^ (which ? v_xor<D>(r) : k_xor<D>(r));
-        __builtin_amdgcn_global_load_lds(src + (size_t)key * D + (cl << 3), (lds_void*)(dst + seg * 1024), 16, 0, 0);
+        lds_dma16(src + (size_t)key * D + (cl << 3), lds_addr(dst + seg * 1024));
       }
     } else {
       // fp32 input: load, round to bf16 (RNE) in registers, store into the same layout.
@@ -220,192 +242,234 @@ __global__ __launch_bounds__(512) void fwd_kernel(const FwdArgs a) {
     }
   };
 
-  // Does this wave see any key of tile t?
-  auto active = [&](int t) { return (qw0 < n_q) && !(a.causal && t * C::BN > qw0 + 31 + delta); };
-
-  // Operand reads. PV product i (k-step i / NB, block i % NB) of a tile whose V sits in
-  // slot `vs`: two transposed 64-bit reads. S product i of a tile whose K sits in slot
-  // `ksl`: one 128-bit read of half i / QKS, k-step i % QKS.
-  auto read_v = [&](int vs, int i) {
-    const int ks = i / C::NB, nb = i % C::NB;
-    const s16x4 p0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_s16x4*)(smem + vaddr[nb] + vs + (16 * ks) * C::ROWB));
-    const s16x4 p1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_s16x4*)(smem + vaddr[nb] + vs + (16 * ks + 8) * C::ROWB));
+  // Operand reads: K operand f = (half kb = f / QKS, k-step f % QKS) of the tile in K slot
+  // `ksl`; V operand f = (k-step f / NB, block f % NB) of the tile in V slot `vs` (two
+  // transposed 64-bit reads).
+  auto read_k = [&](int ksl, int f) {
+    return *reinterpret_cast<const bf16x8*>(smem + kaddr[f % C::QKS] + ksl + (f / C::QKS) * 32 * C::ROWB);
+  };
+  auto read_v = [&](int vs, int f) {
+    const int ks = f / C::NB, nb = f % C::NB;
+    const s16x4 p0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(smem + vaddr[nb] + vs + (16 * ks) * C::ROWB));
+    const s16x4 p1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(smem + vaddr[nb] + vs + (16 * ks + 8) * C::ROWB));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(p0, p1, 0, 1, 2, 3, 4, 5, 6, 7));
   };
-  auto read_k = [&](int ksl, int i) {
-    return *reinterpret_cast<const bf16x8*>(smem + kaddr[i % C::QKS] + ksl + (i / C::QKS) * 32 * C::ROWB);
-  };
 
-  // Product phase for tile j: one chain of MFMAs, O^T += V^T P^T of tile j - 1 (NPV
-  // products) followed by S^T = K Q^T of tile j (NSP products), with every operand read
-  // PF products ahead and the first PF V operands already read at the end of the
-  // previous softmax phase (vpre). Scheduling groups pin the interleaving. The chain always
-  // runs whole: where tile j - 1 gives this wave nothing (j = 0, or no visible key) P is
-  // zero and V is a resident tile of finite values, so the products add exact zeros; where
-  // tile j does not exist or is invisible, S is computed and never read.
-  constexpr int PF = 4;
-  constexpr int NPV = 4 * C::NB;   // 16 at d = 128
-  constexpr int NSP = 2 * C::QKS;  // 16 at d = 128
-  constexpr int N = NPV + NSP;
-  bf16x8 vpre[PF];
-  auto product_phase = [&](int j) {
-    // Keep the per-lane operand bases opaque to loop-invariant code motion: otherwise every
-    // (base + immediate offset) pair is hoisted out of the phase loop into its own VGPR.
-#pragma unroll
-    for (int ks = 0; ks < C::QKS; ++ks) asm volatile("" : "+v"(kaddr[ks]));
-#pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb) asm volatile("" : "+v"(vaddr[nb]));
-    __builtin_amdgcn_s_setprio(1);
-    if (rescale) {  // wave-uniform; rare once a row's maximum has settled
-#pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[nb][r] *= alpha;
-      rescale = false;
-    }
-    const int vs = v_slot(max(j - 1, 0));
-    const int ksl = k_slot(j);
-    bf16x8 buf[PF];
-#pragma unroll
-    for (int f = 0; f < PF; ++f) buf[f] = vpre[f];
+  // S^T = K Q^T of the tile in K slot `ksl` into `sx`: each K operand feeds both row blocks.
+  auto s_mfmas = [&](int ksl, f32x16 (&sx)[QB][2]) {
     const f32x16 zero = {};
+    bf16x8 buf[kPF];
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const bf16x8 x = buf[i % PF];
-      const int nx = i + PF;
-      if (nx < N) buf[i % PF] = nx < NPV ? read_v(vs, nx) : read_k(ksl, nx - NPV);
-      if (i < NPV) {
-        oacc[i % C::NB] = mfma_32x32x16(x, pb[i / C::NB], oacc[i % C::NB]);
-      } else {
-        const int ii = i - NPV, kb = ii / C::QKS, ks = ii % C::QKS;
-        s[kb] = mfma_32x32x16(x, qf[ks], ks == 0 ? zero : s[kb]);
-      }
-    }
+    for (int f = 0; f < kPF; ++f) buf[f] = read_k(ksl, f);
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const int nx = i + PF;
-      if (nx < NPV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);       // two transposed reads
-      else if (nx < N) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one 128-bit read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // one MFMA
+    for (int f = 0; f < C::NKF; ++f) {
+      const bf16x8 x = buf[f % kPF];
+      if (f + kPF < C::NKF) buf[f % kPF] = read_k(ksl, f + kPF);
+      const int kb = f / C::QKS, ks = f % C::QKS;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) sx[qb][kb] = mfma_32x32x16(x, qf[qb][ks], ks == 0 ? zero : sx[qb][kb]);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_setprio(0);
+  };
+  // O^T += V^T P^T of the tile in V slot `vs`.
+  auto pv_mfmas = [&](int vs) {
+    bf16x8 buf[kPF];
+#pragma unroll
+    for (int f = 0; f < kPF; ++f) buf[f] = read_v(vs, f);
+#pragma unroll
+    for (int f = 0; f < C::NVF; ++f) {
+      const bf16x8 x = buf[f % kPF];
+      if (f + kPF < C::NVF) buf[f % kPF] = read_v(vs, f + kPF);
+      const int ks = f / C::NB, nb = f % C::NB;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) oacc[qb][nb] = mfma_32x32x16(x, pb[qb][ks], oacc[qb][nb]);
+    }
   };
 
-  // Softmax phase for tile j: mask, online max / rescale, P = 2^(S*c - m), row sums.
-  auto softmax_phase = [&](int j) {
-    if (!(j >= 0 && j < ntk && active(j))) {  // nothing visible: the next PV chain adds zeros
+  // Mask of tile t (uniform branch; only boundary tiles). Accumulator element r of half kb
+  // is key k0 + 4*half + (32*kb + 8*(r/4) + r%4) for query my_q[qb].
+  auto mask_tile = [&](int t, f32x16 (&sx)[QB][2]) {
+    const int k0 = t * C::BN;
+    if (!((k0 + C::BN > n_kv) || (a.causal && k0 + C::BN - 1 > qw0 + delta))) return;  // uniform
+    const int base = k0 + 4 * half;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) pb[q] = bf16x8{};
-      return;
-    }
-    const int k0 = j * C::BN;
-    const bool need_mask = (k0 + C::BN > n_kv) || (a.causal && k0 + C::BN - 1 > qw0 + delta);
-    // Accumulator element r of half kb is key k0 + 4*half + (32*kb + 8*(r/4) + r%4), query
-    // my_q; it is visible when that constant offset is below both per-lane limits.
-    if (need_mask) {
-      const int base = k0 + 4 * half;
-      const int lim = min(n_kv - base, a.causal ? my_q + delta + 1 - base : n_kv - base);
+    for (int qb = 0; qb < QB; ++qb) {
+      const int lim = min(n_kv - base, a.causal ? my_q[qb] + delta + 1 - base : n_kv - base);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (32 * kb + 8 * (r >> 2) + (r & 3) >= lim) s[kb][r] = kNegInf;
+          if (32 * kb + 8 * (r >> 2) + (r & 3) >= lim) sx[qb][kb][r] = kNegInf;
     }
-    // Row max and row sum are taken as four independent partial chains (short dependency
-    // chains; the order of a max does not matter, the sum's grouping is fixed here).
-    float mp[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mp[r & 3] = fmaxf(mp[r & 3], s[kb][r]);
-    float mx = fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
-    {  // lanes l and l ^ 32 hold the same row: exchange halves with v_permlane32_swap
-      const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, mx), __builtin_bit_cast(unsigned, mx),
-                                                       false, false);
-      mx = fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1])) * a.scale_log2;
-    }
-    const bool raise = mx > m + kLazyRescale;  // also true for the first visible tile
-    if (__builtin_amdgcn_ballot_w64(raise)) {
-      const float m_new = raise ? mx : m;
-      alpha = raise ? exp2_hw(m - m_new) : 1.f;
-      l *= alpha;
-      m = m_new;
-      rescale = true;
-    }
-    const float neg_m = (m == kNegInf) ? 0.f : -m;  // a row that has seen nothing keeps p = 0
-    float rs[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = exp2_hw(fmaf(s[kb][8 * hh + e], a.scale_log2, neg_m));
-          rs[e & 3] += p;
-          pb[2 * kb + hh][e] = (__bf16)p;
-        }
-    l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
   };
 
-  // First V operands of the PV chain of tile i (read at the end of its softmax phase).
-  auto pre_read_v = [&](int i) {
+  // Softmax, first half (branch-free): row max, lazy reference update, and the shift
+  // t = s * scale*log2(e) - m in place. `valid` = false turns it into a no-op on the state.
+  auto softmax_max = [&](bool valid, f32x16 (&sx)[QB][2]) {
+    bool any_raise = false;
 #pragma unroll
-    for (int f = 0; f < PF; ++f) vpre[f] = read_v(v_slot(i), f);
+    for (int qb = 0; qb < QB; ++qb) {
+      float mp[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mp[r & 3] = fmaxf(mp[r & 3], sx[qb][kb][r]);
+      float mx = fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
+      // lanes l and l ^ 32 hold the same row: exchange halves with v_permlane32_swap
+      const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, mx),
+                                                       __builtin_bit_cast(unsigned, mx), false, false);
+      mx = fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1])) * a.scale_log2;
+      const bool raise = valid && (mx > m[qb] + kLazyRescale);  // also true for the first visible tile
+      const float m_new = raise ? mx : m[qb];
+      const float al = raise ? exp2_hw(m[qb] - m_new) : 1.f;
+      alpha[qb] = rescale ? alpha[qb] * al : al;
+      l[qb] *= al;
+      m[qb] = m_new;
+      any_raise |= raise;
+      const float neg_m = (m_new == kNegInf) ? 0.f : -m_new;  // a row that has seen nothing keeps p = 0
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sx[qb][kb][r] = fmaf(sx[qb][kb][r], a.scale_log2, neg_m);
+    }
+    rescale = rescale || (__builtin_amdgcn_ballot_w64(any_raise) != 0);
+  };
+  // Softmax, second half (branch-free): p = 2^t, row sums, P^T as bf16 operands.
+  // `valid` = false yields P = 0 (a dummy tile adds nothing).
+  auto softmax_exp = [&](bool valid, f32x16 (&sx)[QB][2]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float rs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            float p = exp2_hw(sx[qb][kb][8 * hh + e]);
+            p = valid ? p : 0.f;
+            rs[e & 3] += p;
+            pb[qb][2 * kb + hh][e] = (__bf16)p;
+          }
+      l[qb] += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+    }
+  };
+
+  // Tile j: region X = S of tile j + 1 beside the exp half of tile j's softmax; region Y =
+  // P V of tile j beside the max half of tile j + 1's softmax. Loads of K tile j + 2 and V
+  // tile j + 1 stream in meanwhile.
+  auto body = [&](int j, f32x16 (&cur)[QB][2], f32x16 (&nxt)[QB][2]) {
+    // Keep the per-lane operand bases opaque to loop-invariant code motion: otherwise every
+    // (base + immediate offset) pair is hoisted out of the loop into its own VGPR.
+#pragma unroll
+    for (int ks = 0; ks < C::QKS; ++ks) asm volatile("" : "+v"(kaddr[ks]));
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb) asm volatile("" : "+v"(vaddr[nb]));
+    // Loads two tiles ahead: K tile j + 3 (read by the S products of iteration j + 2) and
+    // V tile j + 2 (read by the P V products of iteration j + 2).
+    const bool ld_k = j + 3 < ntk, ld_v = j + 2 < ntk;
+    if (ld_k) stage(j + 3, 0);
+    if (ld_v) stage(j + 2, 1);
+    if (rescale) {  // wave-uniform; rare once a row's maximum has settled
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[qb][nb][r] *= alpha[qb];
+      rescale = false;
+    }
+    // Region X.
+    __builtin_amdgcn_sched_barrier(0);
+    s_mfmas(k_slot(j + 1), nxt);
+    softmax_exp(j < ntk, cur);
+#pragma unroll
+    for (int f = 0; f < C::NKF; ++f) {
+      if (f + kPF < C::NKF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one 128-bit read
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // softmax VALU
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // Region Y.
+    if (j + 1 < ntk) mask_tile(j + 1, nxt);
+    __builtin_amdgcn_sched_barrier(0);
+    pv_mfmas(v_slot(j));
+    softmax_max(j + 1 < ntk, nxt);
+#pragma unroll
+    for (int f = 0; f < C::NVF; ++f) {
+      if (f + kPF < C::NVF) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two transposed reads
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // softmax VALU
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // Wait for this wave's loads issued one iteration ago (K tile j + 2, V tile j + 1; the
+    // ones just issued may stay in flight), then the barrier makes everyone's visible and
+    // frees the slots read in this iteration.
+    if (ld_k && ld_v) wait_vmcnt<2 * C::SEGS_PER_WAVE>();
+    else if (ld_k || ld_v) wait_vmcnt<C::SEGS_PER_WAVE>();
+    else wait_vmcnt<0>();
+    lds_barrier();
   };
 
   if (ntk > 0) {
+    // Zero the buffers once, so that operand reads of a slot never written (dummy work at
+    // the end of the pipeline) see finite values.
+    for (int i = tid; i < (int)sizeof(smem) / 16; i += C::NT) *reinterpret_cast<u32x4*>(smem + 16 * i) = u32x4{0u, 0u, 0u, 0u};
+    __syncthreads();
     stage(0, 0);
     stage(0, 1);
+    if (1 < ntk) stage(1, 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-#pragma unroll
-    for (int q = 0; q < 4; ++q) pb[q] = bf16x8{};
-    pre_read_v(0);
-    // Global phases are separated by workgroup barriers. Every wave runs the same body per
-    // tile i: its product phase, a barrier, its softmax phase, a barrier. Group 1 starts one
-    // phase late (a leading barrier) and so runs each softmax beside group 0's next product
-    // phase. K and V tile i + 1 are loaded in global phase 2i (group 0: before product i;
-    // group 1: before softmax i - 1) and every wave waits for its own loads at the end of
-    // phase 2i + 1, before the barrier that opens phase 2i + 2.
-    if (grp == 1) {
-      if (1 < ntk) { stage(1, 0); stage(1, 1); }
-      lds_barrier();
-    }
-    for (int i = 0; i <= ntk; ++i) {
-      if (grp == 0 && i + 1 < ntk) { stage(i + 1, 0); stage(i + 1, 1); }
-      product_phase(i);
-      if (grp == 1) __builtin_amdgcn_s_waitcnt(0);
-      lds_barrier();
-      if (grp == 1 && i + 2 < ntk) { stage(i + 2, 0); stage(i + 2, 1); }
-      softmax_phase(i);
-      if (i < ntk) pre_read_v(i);
-      if (grp == 0) __builtin_amdgcn_s_waitcnt(0);
-      if (grp == 0 || i < ntk) lds_barrier();
+    // Tiles the first iteration does not read yet, kept in flight: K tile 2 and V tile 1.
+    if (2 < ntk) stage(2, 0);
+    if (1 < ntk) stage(1, 1);
+    s_mfmas(k_slot(0), sa);
+    mask_tile(0, sa);
+    softmax_max(true, sa);
+    // Bodies run in pairs so that the two S buffers keep fixed registers; an odd tile count
+    // ends with one dummy body whose P is zero.
+    for (int j = 0; j < ntk; j += 2) {
+      body(j, sa, sb);
+      body(j + 1, sb, sa);
     }
   }
 
   // Epilogue: O = o / l and LSE = ln(2) * (m + log2 l); padding rows and rows that saw
   // no key get O = 0 and LSE = -inf.
-  const float lt = l + __shfl_xor(l, 32);
-  const bool row_ok = (my_q < n_q) && (lt > 0.f);
-  const float inv = row_ok ? 1.f / lt : 0.f;
-  if (my_q < a.Lq) {
-    OT* op = static_cast<OT*>(a.o) + ((size_t)(b * a.H + h) * a.Lq + my_q) * D;
+  if (rescale) {
 #pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb)
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d0 = 32 * nb + 8 * j + 4 * half;
-        float x0 = oacc[nb][4 * j + 0] * inv, x1 = oacc[nb][4 * j + 1] * inv;
-        float x2 = oacc[nb][4 * j + 2] * inv, x3 = oacc[nb][4 * j + 3] * inv;
-        if (!row_ok) x0 = x1 = x2 = x3 = 0.f;
-        Store4<OT>::store(op + d0, x0, x1, x2, x3);
-      }
-    if (half == 0)
-      a.lse[(size_t)(b * a.H + h) * a.Lq + my_q] = row_ok ? (m + __log2f(lt)) * kLn2 : kNegInf;
+      for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[qb][nb][r] *= alpha[qb];
+  }
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float lt = l[qb] + __shfl_xor(l[qb], 32);
+    const bool row_ok = (my_q[qb] < n_q) && (lt > 0.f);
+    const float inv = row_ok ? 1.f / lt : 0.f;
+    if (my_q[qb] < a.Lq) {
+      OT* op = static_cast<OT*>(a.o) + ((size_t)(b * a.H + h) * a.Lq + my_q[qb]) * D;
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int d0 = 32 * nb + 8 * jj + 4 * half;
+          float x0 = oacc[qb][nb][4 * jj + 0] * inv, x1 = oacc[qb][nb][4 * jj + 1] * inv;
+          float x2 = oacc[qb][nb][4 * jj + 2] * inv, x3 = oacc[qb][nb][4 * jj + 3] * inv;
+          if (!row_ok) x0 = x1 = x2 = x3 = 0.f;
+          Store4<OT>::store(op + d0, x0, x1, x2, x3);
+        }
+      if (half == 0)
+        a.lse[(size_t)(b * a.H + h) * a.Lq + my_q[qb]] = row_ok ? (m[qb] + __log2f(lt)) * kLn2 : kNegInf;
+    }
   }
 #endif
 }
