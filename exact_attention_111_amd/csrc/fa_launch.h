@@ -23,7 +23,7 @@ hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
 
 // Decode: split kernel over key chunks, then the combine kernel.
-constexpr int kDecodeChunk = 512;  // keys per split partial
+constexpr int kDecodeChunk = 2048;  // keys per split partial
 struct DecodeParams {
   const void* q;
   const void* k;

@@ -80,8 +80,9 @@ fa_status fa_fwd_f32(const float* q, const float* k, const float* v, float* o, f
 
 /*
  * fa_decode_workspace_bytes — bytes of device workspace fa_decode needs for a cache of
- * capacity Lmax (the split partials: one (max, sum, d-vector) per query head and key
- * chunk). Returns 0 for invalid sizes.
+ * capacity Lmax (the split partials: one (max, sum, d-vector) of fp32 per query head and
+ * 2048-key chunk, i.e. B * H * ceil(Lmax / 2048) * (d + 2) * 4 bytes). Returns 0 for
+ * invalid sizes.
  */
 size_t fa_decode_workspace_bytes(int B, int H, int Lmax, int d);
 

@@ -72,8 +72,9 @@ def test_fwd_validation(fn):
 
 def test_decode_workspace_bytes():
     L = fa.lib()
-    assert L.fa_decode_workspace_bytes(64, 32, 32768, 128) == 64 * 32 * (32768 // 512) * 130 * 4
-    assert L.fa_decode_workspace_bytes(2, 4, 513, 64) == 2 * 4 * 2 * 66 * 4
+    assert L.fa_decode_workspace_bytes(64, 32, 32768, 128) == 64 * 32 * (32768 // 2048) * 130 * 4
+    assert L.fa_decode_workspace_bytes(2, 4, 2049, 64) == 2 * 4 * 2 * 66 * 4
+    assert L.fa_decode_workspace_bytes(2, 4, 2048, 64) == 2 * 4 * 1 * 66 * 4
     assert L.fa_decode_workspace_bytes(2, 4, 0, 64) == 0
     assert L.fa_decode_workspace_bytes(-1, 4, 10, 64) == 0
 

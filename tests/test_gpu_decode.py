@@ -51,8 +51,8 @@ def run_decode(B, H, Hkv, Lmax, d, *, seed, ctx=None, len_range=(1, None), heads
 
 @pytest.mark.parametrize("d", [64, 128])
 def test_decode_multi_chunk_ragged(d):
-    # 1500 keys = 2 full 512-key chunks + 476; 1 key; 777 keys; 512 exactly.
-    run_decode(4, 8, 2, 1500, d, seed=100 + d, ctx=[1500, 1, 777, 512])
+    # 4500 keys = 2 full 2048-key chunks + 404; 1 key; one key short of a chunk; a chunk exactly.
+    run_decode(4, 8, 2, 4500, d, seed=100 + d, ctx=[4500, 1, 2047, 2048])
 
 
 @pytest.mark.parametrize("H,Hkv", [(4, 4), (16, 2), (12, 2), (3, 1)])
