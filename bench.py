@@ -20,6 +20,8 @@ it finished).
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import math
 import os
@@ -34,6 +36,9 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
 PREFILL = "causal_prefill_B1_H32_L16384_d128"
 DECODE = "decode_B64_H32_Hkv8_ctx32768_d128"
+# Sources whose compiled kernels a committed counter profile describes.
+KERNEL_SOURCES = {"prefill": ["fa_fwd.hip", "fa_device.h", "fa_launch.h"],
+                  "decode": ["fa_decode.hip", "fa_device.h", "fa_launch.h"]}
 
 
 def parse():
@@ -46,6 +51,34 @@ def parse():
     ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
                     help="time one part alone (for profiling); prints a short JSON line instead of the bench line")
     return ap.parse_args()
+
+
+def source_digest(part):
+    """First 16 hex digits of sha256 over the kernel sources of one part, in order."""
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[part]:
+        with open(os.path.join(ROOT, "exact_attention_111_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record(part):
+    """Calibrated HBM bytes per launch of one part, from the `traffic-record:` line of a
+    rocprofv3 FETCH_SIZE/WRITE_SIZE summary under profiles/. Returned only while the
+    kernel sources are byte-identical to the ones profiled; otherwise (None, reason)."""
+    want = source_digest(part)
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        with open(path, encoding="utf-8") as fh:
+            for line in fh:
+                if not line.startswith("traffic-record:"):
+                    continue
+                rec = json.loads(line.split(":", 1)[1])
+                if rec.get("part") != part:
+                    continue
+                if rec.get("source_sha256_16") != want:
+                    return None, f"{os.path.relpath(path, ROOT)} profiled other sources"
+                return rec, os.path.relpath(path, ROOT)
+    return None, "no counter profile"
 
 
 def cpu_baseline(w, x, seconds):
@@ -181,6 +214,9 @@ def main():
     kv_bytes = float(2 * wd.Hkv * wd.d * 2 * int(ctx.sum()))
     gbps = kv_bytes / (dec_avg * 1e-3) / 1e9
 
+    tr_p, src_p = traffic_record("prefill")
+    tr_d, src_d = traffic_record("decode")
+    alg_p = float(3 * wp.B * wp.H * wp.L * wp.d * 2 + wp.B * wp.H * wp.L * wp.d * 2 + wp.B * wp.H * wp.L * 4)
     line = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -204,10 +240,14 @@ def main():
         "decode": {"value": round(gbps, 1), "unit": "GB/s", "ms": round(dec_avg, 4), "ms_min": round(min(dec_ms), 4),
                    "pct_hbm_peak": round(100 * gbps / PEAK_HBM_GBPS, 2), "kv_bytes_per_launch": kv_bytes},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": tr_p["bytes_per_launch"] if tr_p else None, "traffic_unit": "bytes/launch",
+                     "traffic_algorithmic": alg_p, "traffic_source": src_p,
                      "kernel": "fwd_kernel<128, bf16, bf16>"},
         "roofline_decode": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                            "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None,
+                            "frac": round(gbps / PEAK_HBM_GBPS, 4),
+                            "traffic": tr_d["bytes_per_launch"] if tr_d else None, "traffic_unit": "bytes/launch",
+                            "traffic_algorithmic": kv_bytes, "traffic_source": src_d,
                             "kernels": "decode_split_kernel<128> + decode_combine_kernel<128>"},
         "cpu_baseline": None,
     }
