@@ -47,6 +47,15 @@ __device__ __forceinline__ void lds_dma16(const void* gptr, unsigned lds_byte_ad
                : "memory");
 }
 
+// The same load with a wave-uniform 64-bit base in SGPRs and a per-lane 32-bit byte offset
+// (the global "saddr" form): the address costs no VALU work when the offsets are fixed.
+__device__ __forceinline__ void lds_dma16_s(const void* sbase, unsigned voff, unsigned lds_byte_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_byte_addr))
+               : "memory");
+}
+
 // Wait until at most N vector-memory loads of this wave are outstanding (they complete in
 // issue order). Encoding (gfx9 family): vmcnt in bits [3:0] and [15:14]; expcnt [6:4] and
 // lgkmcnt [11:8] left at their maxima, i.e. not waited for.

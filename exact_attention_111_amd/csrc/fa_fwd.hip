@@ -185,7 +185,19 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
 #pragma unroll
   for (int nb = 0; nb < C::NB; ++nb) {
     const int dim = 32 * nb + 16 * (g & 1) + 4 * (sl & 3);
-    vaddr[nb] = vrow * C::ROWB + (((dim >> 3) ^ v_xor<D>(vrow)) << 4) + ((dim & 4) << 1);
+    vaddr[nb] = 3 * C::TILE_BYTES + vrow * C::ROWB + (((dim >> 3) ^ v_xor<D>(vrow)) << 4) + ((dim & 4) << 1);
+  }
+  // Direct-load source offsets within a tile (bytes from the tile's first row): segment i
+  // of this wave puts 16 bytes at LDS byte seg * 1024 + 16 * lane, holding row r's logical
+  // chunk (physical chunk ^ swizzle).
+  unsigned koff[C::SEGS_PER_WAVE], voff[C::SEGS_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < C::SEGS_PER_WAVE; ++i) {
+    const int byte = (w * C::SEGS_PER_WAVE + i) * 1024 + lane * 16;
+    const int r = byte / C::ROWB;
+    const int cp = (byte - r * C::ROWB) >> 4;
+    koff[i] = r * C::ROWB + ((cp ^ k_xor<D>(r)) << 4);
+    voff[i] = r * C::ROWB + ((cp ^ v_xor<D>(r)) << 4);
   }
 
   f32x16 oacc[QB][C::NB];
@@ -206,26 +218,35 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
   f32x16 sa[QB][2], sb[QB][2];  // S^T (then scaled, shifted scores) of two consecutive tiles
   bf16x8 pb[QB][4];              // P^T of the tile whose P V runs next
 
-  // K and V tile t live in slot t % 3, so loads can run two tiles ahead of their use.
+  // K and V tile t live in slot t % 3 (K slots first, then V slots), so loads can run two
+  // tiles ahead of their use.
   auto k_slot = [&](int t) { return (t % 3) * C::TILE_BYTES; };
   auto v_slot = [&](int t) { return (3 + t % 3) * C::TILE_BYTES; };
 
-  // Stage K tile t (which = 0) or V tile t (which = 1). Keys past kv_end read row
-  // kv_end - 1 instead (a visible, finite row); the mask gives them p = 0.
-  auto stage = [&](int t, int which) {
+  // Stage K tile t (which = 0) or V tile t (which = 1) into the slot at byte `slot` of the
+  // LDS buffer. Keys past kv_end read row kv_end - 1 instead (a visible, finite row); the
+  // mask gives them p = 0.
+  auto stage = [&](int t, int which, int slot) {
     const int k0 = t * C::BN;
-    char* dst = smem + (which ? v_slot(t) : k_slot(t));
+    char* dst = smem + slot;
     const IT* src = which ? vp : kp;
     if constexpr (sizeof(IT) == 2) {
+      if (k0 + C::BN <= kv_end) {  // uniform: a whole tile, fixed per-lane offsets
+        const char* tile = reinterpret_cast<const char*>(src) + (size_t)k0 * C::ROWB;
 #pragma unroll
-      for (int i = 0; i < C::SEGS_PER_WAVE; ++i) {
-        const int seg = w * C::SEGS_PER_WAVE + i;
-        const int byte = seg * 1024 + lane * 16;
-        const int r = byte / C::ROWB;
-        const int cp = (byte - r * C::ROWB) >> 4;  // physical chunk this lane fills
-        const int key = min(k0 + r, kv_end - 1);
-        const int cl = cp ^ (which ? v_xor<D>(r) : k_xor<D>(r));
-        lds_dma16(src + (size_t)key * D + (cl << 3), lds_addr(dst + seg * 1024));
+        for (int i = 0; i < C::SEGS_PER_WAVE; ++i)
+          lds_dma16_s(tile, which ? voff[i] : koff[i], lds_addr(dst + (w * C::SEGS_PER_WAVE + i) * 1024));
+      } else {
+#pragma unroll
+        for (int i = 0; i < C::SEGS_PER_WAVE; ++i) {
+          const int seg = w * C::SEGS_PER_WAVE + i;
+          const int byte = seg * 1024 + lane * 16;
+          const int r = byte / C::ROWB;
+          const int cp = (byte - r * C::ROWB) >> 4;  // physical chunk this lane fills
+          const int key = min(k0 + r, kv_end - 1);
+          const int cl = cp ^ (which ? v_xor<D>(r) : k_xor<D>(r));
+          lds_dma16(src + (size_t)key * D + (cl << 3), lds_addr(dst + seg * 1024));
+        }
       }
     } else {
       // fp32 input: load, round to bf16 (RNE) in registers, store into the same layout.
@@ -242,9 +263,10 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
     }
   };
 
-  // Operand reads: K operand f = (half kb = f / QKS, k-step f % QKS) of the tile in K slot
-  // `ksl`; V operand f = (k-step f / NB, block f % NB) of the tile in V slot `vs` (two
-  // transposed 64-bit reads).
+  // Operand reads: K operand f = (half kb = f / QKS, k-step f % QKS) of the tile at byte
+  // `ksl` of the K slots; V operand f = (k-step f / NB, block f % NB) of the tile at byte
+  // `vs` of the V slots (two transposed 64-bit reads). Slot offsets are compile-time
+  // constants, so they become immediate offsets of the LDS reads.
   auto read_k = [&](int ksl, int f) {
     return *reinterpret_cast<const bf16x8*>(smem + kaddr[f % C::QKS] + ksl + (f / C::QKS) * 32 * C::ROWB);
   };
@@ -334,8 +356,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
     rescale = rescale || (__builtin_amdgcn_ballot_w64(any_raise) != 0);
   };
   // Softmax, second half (branch-free): p = 2^t, row sums, P^T as bf16 operands.
-  // `valid` = false yields P = 0 (a dummy tile adds nothing).
-  auto softmax_exp = [&](bool valid, f32x16 (&sx)[QB][2]) {
+  auto softmax_exp = [&](f32x16 (&sx)[QB][2]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float rs[4] = {0.f, 0.f, 0.f, 0.f};
@@ -345,8 +366,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
         for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            float p = exp2_hw(sx[qb][kb][8 * hh + e]);
-            p = valid ? p : 0.f;
+            const float p = exp2_hw(sx[qb][kb][8 * hh + e]);
             rs[e & 3] += p;
             pb[qb][2 * kb + hh][e] = (__bf16)p;
           }
@@ -356,8 +376,13 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
 
   // Tile j: region X = S of tile j + 1 beside the exp half of tile j's softmax; region Y =
   // P V of tile j beside the max half of tile j + 1's softmax. Loads of K tile j + 2 and V
-  // tile j + 1 stream in meanwhile.
-  auto body = [&](int j, f32x16 (&cur)[QB][2], f32x16 (&nxt)[QB][2]) {
+  // tile j + 1 stream in meanwhile. `uc` is j mod 6 as a compile-time constant (the loop is
+  // unrolled six times, the period of the 3 slots and the 2 score buffers), which makes
+  // every slot offset an immediate.
+  auto body = [&](auto uc, int j, f32x16 (&cur)[QB][2], f32x16 (&nxt)[QB][2]) {
+    constexpr int u = decltype(uc)::value;
+    constexpr int ksl_next = ((u + 1) % 3) * C::TILE_BYTES;  // K slot of tile j + 1
+    constexpr int vsl_cur = (u % 3) * C::TILE_BYTES;         // V slot of tile j
     // Keep the per-lane operand bases opaque to loop-invariant code motion: otherwise every
     // (base + immediate offset) pair is hoisted out of the loop into its own VGPR.
 #pragma unroll
@@ -367,8 +392,8 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
     // Loads two tiles ahead: K tile j + 3 (read by the S products of iteration j + 2) and
     // V tile j + 2 (read by the P V products of iteration j + 2).
     const bool ld_k = j + 3 < ntk, ld_v = j + 2 < ntk;
-    if (ld_k) stage(j + 3, 0);
-    if (ld_v) stage(j + 2, 1);
+    if (ld_k) stage(j + 3, 0, (u % 3) * C::TILE_BYTES);        // slot of tile j + 3
+    if (ld_v) stage(j + 2, 1, (3 + (u + 2) % 3) * C::TILE_BYTES);  // slot of tile j + 2
     if (rescale) {  // wave-uniform; rare once a row's maximum has settled
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
@@ -380,8 +405,8 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
     }
     // Region X.
     __builtin_amdgcn_sched_barrier(0);
-    s_mfmas(k_slot(j + 1), nxt);
-    softmax_exp(j < ntk, cur);
+    s_mfmas(ksl_next, nxt);
+    softmax_exp(cur);
 #pragma unroll
     for (int f = 0; f < C::NKF; ++f) {
       if (f + kPF < C::NKF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one 128-bit read
@@ -391,11 +416,19 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
         __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // softmax VALU
       }
     }
+    // Keep the results here: otherwise they are sunk past the mask branch below, into a
+    // stretch of VALU work with no MFMA beside it.
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      asm volatile("" : "+v"(l[qb]));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(pb[qb][i]));
+    }
     __builtin_amdgcn_sched_barrier(0);
     // Region Y.
     if (j + 1 < ntk) mask_tile(j + 1, nxt);
     __builtin_amdgcn_sched_barrier(0);
-    pv_mfmas(v_slot(j));
+    pv_mfmas(vsl_cur);
     softmax_max(j + 1 < ntk, nxt);
 #pragma unroll
     for (int f = 0; f < C::NVF; ++f) {
@@ -405,6 +438,12 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
         __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // softmax VALU
       }
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      asm volatile("" : "+v"(l[qb]), "+v"(m[qb]), "+v"(alpha[qb]));
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) asm volatile("" : "+v"(nxt[qb][kb]));
     }
     __builtin_amdgcn_sched_barrier(0);
     // Wait for this wave's loads issued one iteration ago (K tile j + 2, V tile j + 1; the
@@ -421,22 +460,32 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
     // the end of the pipeline) see finite values.
     for (int i = tid; i < (int)sizeof(smem) / 16; i += C::NT) *reinterpret_cast<u32x4*>(smem + 16 * i) = u32x4{0u, 0u, 0u, 0u};
     __syncthreads();
-    stage(0, 0);
-    stage(0, 1);
-    if (1 < ntk) stage(1, 0);
+    stage(0, 0, k_slot(0));
+    stage(0, 1, v_slot(0));
+    if (1 < ntk) stage(1, 0, k_slot(1));
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     // Tiles the first iteration does not read yet, kept in flight: K tile 2 and V tile 1.
-    if (2 < ntk) stage(2, 0);
-    if (1 < ntk) stage(1, 1);
-    s_mfmas(k_slot(0), sa);
+    if (2 < ntk) stage(2, 0, k_slot(2));
+    if (1 < ntk) stage(1, 1, v_slot(1));
+    s_mfmas(0, sa);
     mask_tile(0, sa);
     softmax_max(true, sa);
-    // Bodies run in pairs so that the two S buffers keep fixed registers; an odd tile count
-    // ends with one dummy body whose P is zero.
-    for (int j = 0; j < ntk; j += 2) {
-      body(j, sa, sb);
-      body(j + 1, sb, sa);
+    // Six bodies per trip, leaving after the body of the last tile.
+    using std::integral_constant;
+    for (int j = 0;; j += 6) {
+      body(integral_constant<int, 0>{}, j, sa, sb);
+      if (j + 1 >= ntk) break;
+      body(integral_constant<int, 1>{}, j + 1, sb, sa);
+      if (j + 2 >= ntk) break;
+      body(integral_constant<int, 2>{}, j + 2, sa, sb);
+      if (j + 3 >= ntk) break;
+      body(integral_constant<int, 3>{}, j + 3, sb, sa);
+      if (j + 4 >= ntk) break;
+      body(integral_constant<int, 4>{}, j + 4, sa, sb);
+      if (j + 5 >= ntk) break;
+      body(integral_constant<int, 5>{}, j + 5, sb, sa);
+      if (j + 6 >= ntk) break;
     }
   }
 
