@@ -56,6 +56,29 @@ __device__ __forceinline__ void lds_dma16_s(const void* sbase, unsigned voff, un
                : "memory");
 }
 
+// Raw buffer resource (gfx9 format: 48-bit base, stride 0, byte size in num_records, and
+// the format word used for untyped dword loads). Lanes whose byte offset is at or past
+// num_records are out of range: they read no memory.
+__device__ __forceinline__ u32x4 raw_buffer_rsrc(const void* base, unsigned num_bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  u32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((unsigned)p);
+  r[1] = __builtin_amdgcn_readfirstlane((unsigned)(p >> 32)) & 0xffffu;
+  r[2] = __builtin_amdgcn_readfirstlane(num_bytes);
+  r[3] = 0x00020000u;
+  return r;
+}
+
+// 16 bytes per lane from a raw buffer straight into LDS (buffer_load_dwordx4 ... lds): lane
+// i lands at lds_byte_addr + 16 * i, read from byte voff of the buffer. Out-of-range lanes
+// read nothing; their LDS bytes are not relied on. Same completion rule as lds_dma16.
+__device__ __forceinline__ void lds_dma16_buf(u32x4 rsrc, unsigned voff, unsigned lds_byte_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds_byte_addr))
+               : "memory");
+}
+
 // Wait until at most N vector-memory loads of this wave are outstanding (they complete in
 // issue order). Encoding (gfx9 family): vmcnt in bits [3:0] and [15:14]; expcnt [6:4] and
 // lgkmcnt [11:8] left at their maxima, i.e. not waited for.

@@ -80,6 +80,7 @@ struct FwdCfg {
 
 constexpr float kLazyRescale = 8.0f;  // log2 of the largest probability allowed before rescaling
 constexpr int kPF = 4;                // operand reads issued this many operands ahead
+constexpr int kDmaStep = 2;           // step of each region at which its tile loads are issued
 
 struct FwdArgs {
   const void* q;
@@ -224,30 +225,21 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
   auto v_slot = [&](int t) { return (3 + t % 3) * C::TILE_BYTES; };
 
   // Stage K tile t (which = 0) or V tile t (which = 1) into the slot at byte `slot` of the
-  // LDS buffer. Keys past kv_end read row kv_end - 1 instead (a visible, finite row); the
-  // mask gives them p = 0.
+  // LDS buffer. bf16 input: branch-free direct loads through a buffer resource that ends at
+  // key kv_end, so rows past it (and whole tiles past it) read no memory; their LDS rows are
+  // masked (K) or multiplied by p = 0 (V) and only need to be finite, which they are (the
+  // buffers start zeroed and only ever hold input rows). fp32 input: rows past kv_end read
+  // row kv_end - 1 instead.
   auto stage = [&](int t, int which, int slot) {
     const int k0 = t * C::BN;
     char* dst = smem + slot;
     const IT* src = which ? vp : kp;
     if constexpr (sizeof(IT) == 2) {
-      if (k0 + C::BN <= kv_end) {  // uniform: a whole tile, fixed per-lane offsets
-        const char* tile = reinterpret_cast<const char*>(src) + (size_t)k0 * C::ROWB;
+      const u32x4 rsrc = raw_buffer_rsrc(reinterpret_cast<const char*>(src) + (size_t)k0 * C::ROWB,
+                                         (unsigned)max(kv_end - k0, 0) * C::ROWB);
 #pragma unroll
-        for (int i = 0; i < C::SEGS_PER_WAVE; ++i)
-          lds_dma16_s(tile, which ? voff[i] : koff[i], lds_addr(dst + (w * C::SEGS_PER_WAVE + i) * 1024));
-      } else {
-#pragma unroll
-        for (int i = 0; i < C::SEGS_PER_WAVE; ++i) {
-          const int seg = w * C::SEGS_PER_WAVE + i;
-          const int byte = seg * 1024 + lane * 16;
-          const int r = byte / C::ROWB;
-          const int cp = (byte - r * C::ROWB) >> 4;  // physical chunk this lane fills
-          const int key = min(k0 + r, kv_end - 1);
-          const int cl = cp ^ (which ? v_xor<D>(r) : k_xor<D>(r));
-          lds_dma16(src + (size_t)key * D + (cl << 3), lds_addr(dst + seg * 1024));
-        }
-      }
+      for (int i = 0; i < C::SEGS_PER_WAVE; ++i)
+        lds_dma16_buf(rsrc, which ? voff[i] : koff[i], lds_addr(dst + (w * C::SEGS_PER_WAVE + i) * 1024));
     } else {
       // fp32 input: load, round to bf16 (RNE) in registers, store into the same layout.
       constexpr int CH = D / 8;
@@ -292,21 +284,6 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
       for (int qb = 0; qb < QB; ++qb) sx[qb][kb] = mfma_32x32x16(x, qf[qb][ks], ks == 0 ? zero : sx[qb][kb]);
     }
   };
-  // O^T += V^T P^T of the tile in V slot `vs`.
-  auto pv_mfmas = [&](int vs) {
-    bf16x8 buf[kPF];
-#pragma unroll
-    for (int f = 0; f < kPF; ++f) buf[f] = read_v(vs, f);
-#pragma unroll
-    for (int f = 0; f < C::NVF; ++f) {
-      const bf16x8 x = buf[f % kPF];
-      if (f + kPF < C::NVF) buf[f % kPF] = read_v(vs, f + kPF);
-      const int ks = f / C::NB, nb = f % C::NB;
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) oacc[qb][nb] = mfma_32x32x16(x, pb[qb][ks], oacc[qb][nb]);
-    }
-  };
-
   // Mask of tile t (uniform branch; only boundary tiles). Accumulator element r of half kb
   // is key k0 + 4*half + (32*kb + 8*(r/4) + r%4) for query my_q[qb].
   auto mask_tile = [&](int t, f32x16 (&sx)[QB][2]) {
@@ -355,23 +332,126 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
     }
     rescale = rescale || (__builtin_amdgcn_ballot_w64(any_raise) != 0);
   };
-  // Softmax, second half (branch-free): p = 2^t, row sums, P^T as bf16 operands.
-  auto softmax_exp = [&](f32x16 (&sx)[QB][2]) {
+  // The two halves of a body, written out step by step. A region is one step per MFMA
+  // operand: step f takes the operand read kPF steps earlier, issues the read for step
+  // f + kPF, runs its MFMA(s) and a fixed slice of the softmax arithmetic. A scheduling
+  // fence between steps keeps that order; left to itself the scheduler either reads each
+  // operand just before its MFMA (a full LDS round trip per MFMA) or gathers the softmax
+  // work into stretches with no MFMA beside them. `mid` runs at step kDmaStep (tile loads).
+
+  // Region X: S^T of the next tile into `nx`, beside p = 2^t, the row sums and the bf16 P^T
+  // operands of the current tile `cu` (whose scores were shifted in the previous region Y).
+  auto region_x = [&](int ksl, f32x16 (&nx)[QB][2], f32x16 (&cu)[QB][2], auto&& mid) {
+    constexpr int NF = C::NKF;
+    constexpr int EPS = 32 * QB / NF;  // elements of `cu` per step
+    const f32x16 zero = {};
+    float rs[QB][4];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rs[qb][i] = 0.f;
+    bf16x8 buf[kPF];
+#pragma unroll
+    for (int f = 0; f < kPF; ++f) buf[f] = read_k(ksl, f);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      __builtin_amdgcn_sched_barrier(0);
+      const bf16x8 x = buf[f % kPF];
+      if (f + kPF < NF) buf[f % kPF] = read_k(ksl, f + kPF);
+      const int kb = f / C::QKS, ks = f % C::QKS;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) nx[qb][kb] = mfma_32x32x16(x, qf[qb][ks], ks == 0 ? zero : nx[qb][kb]);
+#pragma unroll
+      for (int e = f * EPS; e < (f + 1) * EPS; ++e) {
+        const int qb = e / 32, h = (e % 32) / 16, r = e % 16;
+        const float p = exp2_hw(cu[qb][h][r]);
+        rs[qb][e & 3] += p;
+        pb[qb][2 * h + (r >> 3)][r & 7] = (__bf16)p;
+      }
+      if (f == kDmaStep) mid();
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      float rs[4] = {0.f, 0.f, 0.f, 0.f};
+      l[qb] += (rs[qb][0] + rs[qb][1]) + (rs[qb][2] + rs[qb][3]);
+      asm volatile("" : "+v"(l[qb]));
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float p = exp2_hw(sx[qb][kb][8 * hh + e]);
-            rs[e & 3] += p;
-            pb[qb][2 * kb + hh][e] = (__bf16)p;
-          }
-      l[qb] += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+      for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(pb[qb][i]));
     }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // Region Y: O^T += V^T P^T of the current tile (V tile at byte `vs` of the V slots),
+  // beside the softmax's first half for the next tile `nx`: row maximum over the first half
+  // of the steps, the lazy reference update at the middle step, then t = s * scale*log2(e)
+  // - m in place. `valid` = false leaves the row state untouched.
+  auto region_y = [&](int vs, f32x16 (&nx)[QB][2], bool valid, auto&& mid) {
+    constexpr int NF = C::NVF;
+    constexpr int NM = NF / 2;                       // steps of the row maximum
+    constexpr int EPM = 32 * QB / NM;                // elements per maximum step
+    constexpr int NS = NF - NM - 1;                  // steps of the shift
+    constexpr int EPF = (32 * QB + NS - 1) / NS;     // elements per shift step
+    float mp[QB][4], neg_m[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      neg_m[qb] = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mp[qb][i] = kNegInf;
+    }
+    bf16x8 buf[kPF];
+#pragma unroll
+    for (int f = 0; f < kPF; ++f) buf[f] = read_v(vs, f);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      __builtin_amdgcn_sched_barrier(0);
+      const bf16x8 x = buf[f % kPF];
+      if (f + kPF < NF) buf[f % kPF] = read_v(vs, f + kPF);
+      const int ks = f / C::NB, nb = f % C::NB;
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) oacc[qb][nb] = mfma_32x32x16(x, pb[qb][ks], oacc[qb][nb]);
+      if (f < NM) {
+#pragma unroll
+        for (int e = f * EPM; e < (f + 1) * EPM; ++e) {
+          const int qb = e / 32, h = (e % 32) / 16, r = e % 16;
+          mp[qb][e & 3] = fmaxf(mp[qb][e & 3], nx[qb][h][r]);
+        }
+      } else if (f == NM) {
+        bool any_raise = false;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          float mx = fmaxf(fmaxf(mp[qb][0], mp[qb][1]), fmaxf(mp[qb][2], mp[qb][3]));
+          // lanes l and l ^ 32 hold the same row: exchange halves with v_permlane32_swap
+          const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, mx),
+                                                           __builtin_bit_cast(unsigned, mx), false, false);
+          mx = fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1])) * a.scale_log2;
+          const bool raise = valid && (mx > m[qb] + kLazyRescale);  // also true for the first visible tile
+          const float m_new = raise ? mx : m[qb];
+          const float al = raise ? exp2_hw(m[qb] - m_new) : 1.f;
+          alpha[qb] = rescale ? alpha[qb] * al : al;
+          l[qb] *= al;
+          m[qb] = m_new;
+          any_raise |= raise;
+          neg_m[qb] = (m_new == kNegInf) ? 0.f : -m_new;  // a row that has seen nothing keeps p = 0
+        }
+        rescale = rescale || (__builtin_amdgcn_ballot_w64(any_raise) != 0);
+      } else {
+        const int s0 = (f - NM - 1) * EPF;
+#pragma unroll
+        for (int e = s0; e < s0 + EPF && e < 32 * QB; ++e) {
+          const int qb = e / 32, h = (e % 32) / 16, r = e % 16;
+          nx[qb][h][r] = fmaf(nx[qb][h][r], a.scale_log2, neg_m[qb]);
+        }
+      }
+      if (f == kDmaStep) mid();
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      asm volatile("" : "+v"(l[qb]), "+v"(m[qb]), "+v"(alpha[qb]));
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) asm volatile("" : "+v"(nx[qb][kb]));
+    }
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   // Tile j: region X = S of tile j + 1 beside the exp half of tile j's softmax; region Y =
@@ -390,10 +470,14 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
 #pragma unroll
     for (int nb = 0; nb < C::NB; ++nb) asm volatile("" : "+v"(vaddr[nb]));
     // Loads two tiles ahead: K tile j + 3 (read by the S products of iteration j + 2) and
-    // V tile j + 2 (read by the P V products of iteration j + 2).
-    const bool ld_k = j + 3 < ntk, ld_v = j + 2 < ntk;
-    if (ld_k) stage(j + 3, 0, (u % 3) * C::TILE_BYTES);        // slot of tile j + 3
-    if (ld_v) stage(j + 2, 1, (3 + (u + 2) % 3) * C::TILE_BYTES);  // slot of tile j + 2
+    // V tile j + 2 (read by the P V products of iteration j + 2), issued inside the regions
+    // so that the workgroup's waves do not all queue on the load path at once. bf16 loads
+    // are issued even past the last tile (they read nothing), which keeps the regions free
+    // of branches; fp32 staging keeps its bounds.
+    constexpr bool kAll = sizeof(IT) == 2;
+    const bool ld_k = kAll || j + 3 < ntk, ld_v = kAll || j + 2 < ntk;
+    auto load_k = [&] { if (ld_k) stage(j + 3, 0, (u % 3) * C::TILE_BYTES); };        // slot of tile j + 3
+    auto load_v = [&] { if (ld_v) stage(j + 2, 1, (3 + (u + 2) % 3) * C::TILE_BYTES); };  // slot of tile j + 2
     if (rescale) {  // wave-uniform; rare once a row's maximum has settled
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
@@ -403,49 +487,11 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
           for (int r = 0; r < 16; ++r) oacc[qb][nb][r] *= alpha[qb];
       rescale = false;
     }
-    // Region X.
     __builtin_amdgcn_sched_barrier(0);
-    s_mfmas(ksl_next, nxt);
-    softmax_exp(cur);
-#pragma unroll
-    for (int f = 0; f < C::NKF; ++f) {
-      if (f + kPF < C::NKF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one 128-bit read
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // softmax VALU
-      }
-    }
-    // Keep the results here: otherwise they are sunk past the mask branch below, into a
-    // stretch of VALU work with no MFMA beside it.
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      asm volatile("" : "+v"(l[qb]));
-#pragma unroll
-      for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(pb[qb][i]));
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // Region Y.
+    region_x(ksl_next, nxt, cur, load_k);
     if (j + 1 < ntk) mask_tile(j + 1, nxt);
     __builtin_amdgcn_sched_barrier(0);
-    pv_mfmas(vsl_cur);
-    softmax_max(j + 1 < ntk, nxt);
-#pragma unroll
-    for (int f = 0; f < C::NVF; ++f) {
-      if (f + kPF < C::NVF) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two transposed reads
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // softmax VALU
-      }
-    }
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      asm volatile("" : "+v"(l[qb]), "+v"(m[qb]), "+v"(alpha[qb]));
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) asm volatile("" : "+v"(nxt[qb][kb]));
-    }
-    __builtin_amdgcn_sched_barrier(0);
+    region_y(vsl_cur, nxt, j + 1 < ntk, load_v);
     // Wait for this wave's loads issued one iteration ago (K tile j + 2, V tile j + 1; the
     // ones just issued may stay in flight), then the barrier makes everyone's visible and
     // frees the slots read in this iteration.
@@ -487,6 +533,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
       body(integral_constant<int, 5>{}, j + 5, sb, sa);
       if (j + 6 >= ntk) break;
     }
+    wait_vmcnt<0>();  // loads issued by the last bodies must land before the workgroup ends
   }
 
   // Epilogue: O = o / l and LSE = ln(2) * (m + log2 l); padding rows and rows that saw
