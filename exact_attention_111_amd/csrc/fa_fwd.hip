@@ -339,11 +339,25 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
   // operand just before its MFMA (a full LDS round trip per MFMA) or gathers the softmax
   // work into stretches with no MFMA beside them. `mid` runs at step kDmaStep (tile loads).
 
+  // p = 2^t of element e of tile `cu`, added to the row-sum partials and converted into the
+  // bf16 P^T operands. Accumulator element r of key half h of row block qb is element
+  // 32 qb + 16 h + r; P^T operand 2 h + r / 8 (k-step) holds its elements r % 8.
+  auto exp_elem = [&](f32x16 (&cu)[QB][2], int e, float (&rs)[QB][4]) {
+    const int qb = e / 32, h = (e % 32) / 16, r = e % 16;
+    const float p = exp2_hw(cu[qb][h][r]);
+    rs[qb][e & 3] += p;
+    pb[qb][2 * h + (r >> 3)][r & 7] = (__bf16)p;
+  };
+  // The exp work of a tile is split between the two regions so that both carry about the
+  // same VALU load: region X takes elements [0, kExpX), region Y the last quarter (their
+  // operands belong to the last P V k-step, which region Y reaches only in its second half).
+  constexpr int kElems = 32 * QB;
+  constexpr int kExpX = kElems - kElems / 4;
+
   // Region X: S^T of the next tile into `nx`, beside p = 2^t, the row sums and the bf16 P^T
-  // operands of the current tile `cu` (whose scores were shifted in the previous region Y).
+  // operands of most of the current tile `cu` (whose scores were shifted in region Y).
   auto region_x = [&](int ksl, f32x16 (&nx)[QB][2], f32x16 (&cu)[QB][2], auto&& mid) {
     constexpr int NF = C::NKF;
-    constexpr int EPS = 32 * QB / NF;  // elements of `cu` per step
     const f32x16 zero = {};
     float rs[QB][4];
 #pragma unroll
@@ -362,12 +376,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) nx[qb][kb] = mfma_32x32x16(x, qf[qb][ks], ks == 0 ? zero : nx[qb][kb]);
 #pragma unroll
-      for (int e = f * EPS; e < (f + 1) * EPS; ++e) {
-        const int qb = e / 32, h = (e % 32) / 16, r = e % 16;
-        const float p = exp2_hw(cu[qb][h][r]);
-        rs[qb][e & 3] += p;
-        pb[qb][2 * h + (r >> 3)][r & 7] = (__bf16)p;
-      }
+      for (int e = f * kExpX / NF; e < (f + 1) * kExpX / NF; ++e) exp_elem(cu, e, rs);
       if (f == kDmaStep) mid();
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -381,22 +390,27 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // Region Y: O^T += V^T P^T of the current tile (V tile at byte `vs` of the V slots),
-  // beside the softmax's first half for the next tile `nx`: row maximum over the first half
-  // of the steps, the lazy reference update at the middle step, then t = s * scale*log2(e)
-  // - m in place. `valid` = false leaves the row state untouched.
-  auto region_y = [&](int vs, f32x16 (&nx)[QB][2], bool valid, auto&& mid) {
+  // Region Y: O^T += V^T P^T of the current tile `cu` (V tile at byte `vs` of the V slots),
+  // beside the rest of `cu`'s exp work (first half of the steps) and the softmax's first half
+  // for the next tile `nx`: row maximum over the first half of the steps, the lazy reference
+  // update at the middle step, then t = s * scale*log2(e) - m in place. `valid` = false
+  // leaves the row state untouched.
+  auto region_y = [&](int vs, f32x16 (&nx)[QB][2], f32x16 (&cu)[QB][2], bool valid, auto&& mid) {
     constexpr int NF = C::NVF;
     constexpr int NM = NF / 2;                       // steps of the row maximum
     constexpr int EPM = 32 * QB / NM;                // elements per maximum step
     constexpr int NS = NF - NM - 1;                  // steps of the shift
     constexpr int EPF = (32 * QB + NS - 1) / NS;     // elements per shift step
-    float mp[QB][4], neg_m[QB];
+    constexpr int NE = kElems - kExpX;               // exp elements left over from region X
+    float mp[QB][4], neg_m[QB], rs[QB][4];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       neg_m[qb] = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) mp[qb][i] = kNegInf;
+      for (int i = 0; i < 4; ++i) {
+        mp[qb][i] = kNegInf;
+        rs[qb][i] = 0.f;
+      }
     }
     bf16x8 buf[kPF];
 #pragma unroll
@@ -411,6 +425,8 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
       for (int qb = 0; qb < QB; ++qb) oacc[qb][nb] = mfma_32x32x16(x, pb[qb][ks], oacc[qb][nb]);
       if (f < NM) {
 #pragma unroll
+        for (int e = kExpX + f * NE / NM; e < kExpX + (f + 1) * NE / NM; ++e) exp_elem(cu, e, rs);
+#pragma unroll
         for (int e = f * EPM; e < (f + 1) * EPM; ++e) {
           const int qb = e / 32, h = (e % 32) / 16, r = e % 16;
           mp[qb][e & 3] = fmaxf(mp[qb][e & 3], nx[qb][h][r]);
@@ -419,6 +435,8 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
         bool any_raise = false;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
+          // the current tile's sum joins l before l is rescaled to a new reference
+          l[qb] += (rs[qb][0] + rs[qb][1]) + (rs[qb][2] + rs[qb][3]);
           float mx = fmaxf(fmaxf(mp[qb][0], mp[qb][1]), fmaxf(mp[qb][2], mp[qb][3]));
           // lanes l and l ^ 32 hold the same row: exchange halves with v_permlane32_swap
           const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, mx),
@@ -491,7 +509,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
     region_x(ksl_next, nxt, cur, load_k);
     if (j + 1 < ntk) mask_tile(j + 1, nxt);
     __builtin_amdgcn_sched_barrier(0);
-    region_y(vsl_cur, nxt, j + 1 < ntk, load_v);
+    region_y(vsl_cur, nxt, cur, j + 1 < ntk, load_v);
     // Wait for this wave's loads issued one iteration ago (K tile j + 2, V tile j + 1; the
     // ones just issued may stay in flight), then the barrier makes everyone's visible and
     // frees the slots read in this iteration.
