@@ -48,8 +48,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
-    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
-                    help="time one part alone (for profiling); prints a short JSON line instead of the bench line")
+    ap.add_argument("--only", default=None,
+                    help="time one part alone (for profiling): prefill, decode, copy, or any workload name of "
+                         "fa_inputs.WORKLOADS; prints a short JSON line instead of the bench line")
     return ap.parse_args()
 
 
@@ -121,30 +122,43 @@ def cpu_baseline(w, x, seconds):
 
 
 def run_only(part, steps, warmup):
-    """Time one part alone (for profiling): prefill, decode, or a plain 1 GiB device copy."""
+    """Time one part alone (for profiling): the prefill or decode part of the step, a plain
+    1 GiB device copy, or any named workload. Prints the kernel time and, for workloads,
+    the algorithmic rate (prefill: TFLOP/s over visible pairs as in the metric; decode: K/V
+    GB/s)."""
     import torch
 
     import exact_attention_111_amd as fa
     import fa_inputs
     dev = torch.device("cuda:0")
-    if part == "prefill":
-        w = fa_inputs.WORKLOADS[PREFILL]
-        x = fa_inputs.workload_inputs(w, device=dev)
-        o = torch.empty_like(x["q"])
-        lse = torch.empty((w.B, w.H, w.L), dtype=torch.float32, device=dev)
-        fn = lambda: fa.fwd(x["q"], x["k"], x["v"], causal=True, scale=w.scale, out=o, lse=lse)  # noqa: E731
-    elif part == "decode":
-        w = fa_inputs.WORKLOADS[DECODE]
-        x = fa_inputs.workload_inputs(w, device=dev)
-        o = torch.empty_like(x["q"])
-        lse = torch.empty((w.B, w.H), dtype=torch.float32, device=dev)
-        ws = torch.empty(max(16, fa.decode_workspace_bytes(w.B, w.H, w.L, w.d)), dtype=torch.uint8, device=dev)
-        fn = lambda: fa.decode(x["q"], x["k_cache"], x["v_cache"], x["ctx_lens"], scale=w.scale,  # noqa: E731
-                               workspace=ws, out=o, lse=lse)
-    else:  # a plain copy of 1 GiB: reads 1 GiB and writes 1 GiB per launch
+    name = {"prefill": PREFILL, "decode": DECODE}.get(part, part)
+    rate = None
+    if name == "copy":  # a plain copy of 1 GiB: reads 1 GiB and writes 1 GiB per launch
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         fn = lambda: dst.copy_(src)  # noqa: E731
+    elif name in fa_inputs.WORKLOADS:
+        w = fa_inputs.WORKLOADS[name]
+        x = fa_inputs.workload_inputs(w, device=dev)
+        if w.kind == "decode":
+            o = torch.empty_like(x["q"])
+            lse = torch.empty((w.B, w.H), dtype=torch.float32, device=dev)
+            ws = torch.empty(max(16, fa.decode_workspace_bytes(w.B, w.H, w.L, w.d)), dtype=torch.uint8, device=dev)
+            fn = lambda: fa.decode(x["q"], x["k_cache"], x["v_cache"], x["ctx_lens"], scale=w.scale,  # noqa: E731
+                                   workspace=ws, out=o, lse=lse)
+            work, unit = float(2 * w.Hkv * w.d * 2 * int(x["ctx_lens_cpu"].to(torch.int64).sum())), "GB/s"
+        else:
+            o = torch.empty_like(x["q"])
+            lse = torch.empty((w.B, w.H, w.L), dtype=torch.float32, device=dev)
+            sl = x.get("seqlens")
+            fn = lambda: fa.fwd(x["q"], x["k"], x["v"], causal=w.causal, scale=w.scale, seqlens=sl,  # noqa: E731
+                                out=o, lse=lse)
+            lens = x["seqlens_cpu"].to(torch.float64) if sl is not None else torch.full((w.B,), float(w.L))
+            pairs = float((lens * lens).sum()) * (0.5 if w.causal else 1.0)
+            work, unit = 4.0 * w.H * w.d * pairs, "TFLOP/s"
+        rate = (work, unit)
+    else:
+        raise SystemExit(f"unknown part or workload: {part}")
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -152,8 +166,13 @@ def run_only(part, steps, warmup):
     for a, b in ev:
         a.record(); fn(); b.record()
     torch.cuda.synchronize()
-    ms = [a.elapsed_time(b) for a, b in ev]
-    print(json.dumps({"only": part, "steps": steps, "ms_avg": sum(ms) / len(ms), "ms_min": min(ms)}), flush=True)
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    line = {"only": name, "steps": steps, "ms_avg": sum(ms) / len(ms), "ms_min": ms[0], "ms_median": ms[len(ms) // 2]}
+    if rate is not None:
+        work, unit = rate
+        scale = 1e12 if unit == "TFLOP/s" else 1e9
+        line.update({"value": work / (line["ms_median"] * 1e-3) / scale, "unit": unit})
+    print(json.dumps(line), flush=True)
 
 
 def main():

@@ -125,14 +125,27 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
   const int col = lane & 31;   // this lane's query row within a 32-row block
   const int half = lane >> 5;  // which 8-element half of a 16-wide k-step
 
-  // XCD-aware renumbering: hardware id i runs on XCD i % 8; give each XCD a contiguous
-  // range of logical ids so its CUs work through one head at a time.
+  // XCD-aware renumbering: hardware id i runs on XCD i % 8 as that XCD's slot i / 8.
+  // When the (batch, head) count is a multiple of 8, head bh belongs to XCD bh % 8, so
+  // every XCD gets the same mix of sequences (equal work even when lengths vary) and its
+  // L2 serves the K/V of its own heads only; an XCD's slots go through the query tiles
+  // heaviest first, across its heads, so that its CUs read the same K/V rows at about the
+  // same time. Otherwise each XCD takes a contiguous range of logical ids (heads in
+  // order, heaviest tile first within a head).
   const int hw = blockIdx.x;
   const int xcd = hw & 7, slot = hw >> 3;
-  const int per = a.nwg >> 3, extra = a.nwg & 7;
-  const int logical = xcd * per + min(xcd, extra) + slot;
-  const int bh = logical / a.ntq;
-  const int qt = a.ntq - 1 - (logical - bh * a.ntq);  // heaviest first within a head
+  const int nheads = a.nwg / a.ntq;
+  int bh, qt;
+  if ((nheads & 7) == 0) {
+    const int per_xcd = nheads >> 3;
+    qt = a.ntq - 1 - slot / per_xcd;
+    bh = xcd + 8 * (slot - (slot / per_xcd) * per_xcd);
+  } else {
+    const int per = a.nwg >> 3, extra = a.nwg & 7;
+    const int logical = xcd * per + min(xcd, extra) + slot;
+    bh = logical / a.ntq;
+    qt = a.ntq - 1 - (logical - bh * a.ntq);
+  }
   const int b = bh / a.H;
   const int h = bh - b * a.H;
   const int kvh = h / a.group;
