@@ -34,28 +34,6 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4): lane i
-// lands at lds_byte_addr + 16 * i. Issued as inline assembly so that the compiler does not
-// track it: otherwise it cannot tell which LDS bytes are being written and stalls every
-// later LDS read until the load completes. Callers must therefore wait for completion
-// themselves (s_waitcnt vmcnt(0)) before the barrier that publishes the data. M0 carries
-// the LDS base; nothing else in these kernels uses M0.
-__device__ __forceinline__ void lds_dma16(const void* gptr, unsigned lds_byte_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(gptr), "s"(__builtin_amdgcn_readfirstlane(lds_byte_addr))
-               : "memory");
-}
-
-// The same load with a wave-uniform 64-bit base in SGPRs and a per-lane 32-bit byte offset
-// (the global "saddr" form): the address costs no VALU work when the offsets are fixed.
-__device__ __forceinline__ void lds_dma16_s(const void* sbase, unsigned voff, unsigned lds_byte_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_byte_addr))
-               : "memory");
-}
-
 // Raw buffer resource (gfx9 format: 48-bit base, stride 0, byte size in num_records, and
 // the format word used for untyped dword loads). Lanes whose byte offset is at or past
 // num_records are out of range: they read no memory.
@@ -71,7 +49,11 @@ __device__ __forceinline__ u32x4 raw_buffer_rsrc(const void* base, unsigned num_
 
 // 16 bytes per lane from a raw buffer straight into LDS (buffer_load_dwordx4 ... lds): lane
 // i lands at lds_byte_addr + 16 * i, read from byte voff of the buffer. Out-of-range lanes
-// read nothing; their LDS bytes are not relied on. Same completion rule as lds_dma16.
+// read nothing; their LDS bytes are not relied on. Issued as inline assembly so that the
+// compiler does not track it: otherwise it cannot tell which LDS bytes are being written and
+// stalls every later LDS read until the load completes. Callers must therefore wait for
+// completion themselves (s_waitcnt vmcnt) before the barrier that publishes the data. M0
+// carries the LDS base; nothing else in these kernels uses M0.
 __device__ __forceinline__ void lds_dma16_buf(u32x4 rsrc, unsigned voff, unsigned lds_byte_addr) {
   asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
@@ -86,6 +68,17 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// A wave-uniform pointer, held in SGPRs (the value must be the same in every lane).
+// readfirstlane returns int: each half goes through unsigned before widening, or a low
+// word with bit 31 set would be sign-extended over the high word.
+template <typename T>
+__device__ __forceinline__ const T* uniform_ptr(const T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint64_t lo = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)v);
+  const uint64_t hi = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
+  return reinterpret_cast<const T*>((hi << 32) | lo);
 }
 
 // Byte address of a pointer into LDS.

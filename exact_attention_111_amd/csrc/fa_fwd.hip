@@ -171,11 +171,12 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
     if (a.causal) kv_end = min(kv_end, min(q0 + C::BM, n_q) + delta);
     kv_end = max(kv_end, 0);
   }
+  kv_end = __builtin_amdgcn_readfirstlane(kv_end);  // uniform: keeps load setup in SGPRs
   const int ntk = (kv_end + C::BN - 1) / C::BN;
 
   const IT* __restrict__ qp = static_cast<const IT*>(a.q) + (size_t)(b * a.H + h) * a.Lq * D;
-  const IT* __restrict__ kp = static_cast<const IT*>(a.k) + (size_t)(b * a.Hkv + kvh) * a.Lk * D;
-  const IT* __restrict__ vp = static_cast<const IT*>(a.v) + (size_t)(b * a.Hkv + kvh) * a.Lk * D;
+  const IT* __restrict__ kp = uniform_ptr(static_cast<const IT*>(a.k) + (size_t)(b * a.Hkv + kvh) * a.Lk * D);
+  const IT* __restrict__ vp = uniform_ptr(static_cast<const IT*>(a.v) + (size_t)(b * a.Hkv + kvh) * a.Lk * D);
 
   // Q rows of this lane as MFMA B operands: element t of k-step ks is d = 16*ks + 8*half + t.
   bf16x8 qf[QB][C::QKS];
@@ -353,6 +354,15 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
   // operand just before its MFMA (a full LDS round trip per MFMA) or gathers the softmax
   // work into stretches with no MFMA beside them. `mid` runs at step kDmaStep (tile loads).
 
+  // Keep running sums where they are computed: without this, chains of adds are linearised
+  // after the region's last MFMA, where nothing else overlaps them. (Not for maxima: an
+  // opaque value must be canonicalised before each fmaxf, which costs more than it saves.)
+  auto pin_partials = [](float (&x)[QB][4]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(x[qb][i]));
+  };
   // p = 2^t of element e of tile `cu`, added to the row-sum partials and converted into the
   // bf16 P^T operands. Accumulator element r of key half h of row block qb is element
   // 32 qb + 16 h + r; P^T operand 2 h + r / 8 (k-step) holds its elements r % 8.
@@ -391,6 +401,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
       for (int qb = 0; qb < QB; ++qb) nx[qb][kb] = mfma_32x32x16(x, qf[qb][ks], ks == 0 ? zero : nx[qb][kb]);
 #pragma unroll
       for (int e = f * kExpX / NF; e < (f + 1) * kExpX / NF; ++e) exp_elem(cu, e, rs);
+      pin_partials(rs);
       if (f == kDmaStep) mid();
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -440,6 +451,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
       if (f < NM) {
 #pragma unroll
         for (int e = kExpX + f * NE / NM; e < kExpX + (f + 1) * NE / NM; ++e) exp_elem(cu, e, rs);
+        pin_partials(rs);
 #pragma unroll
         for (int e = f * EPM; e < (f + 1) * EPM; ++e) {
           const int qb = e / 32, h = (e % 32) / 16, r = e % 16;

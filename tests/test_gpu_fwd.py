@@ -115,6 +115,43 @@ def test_gqa_equals_repeated_kv_bitwise():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+def test_inputs_at_addresses_with_bit31_of_the_low_word_set():
+    """Regression: the kernel holds K/V base pointers in scalar registers, rebuilt from two
+    32-bit halves. Tensors whose address has bit 31 of the low word set must come through
+    unchanged (a sign-extended low half once turned them into wild addresses)."""
+    fa = _fa()
+    B, H, Hkv, L, d = 1, 8, 2, 1000, 128
+    announce(entry="fa_fwd", case="tensors at addresses with bit 31 of the low word set", B=B, H=H, Hkv=Hkv,
+             L=L, d=d)
+    x = fa_inputs.prefill_inputs(B, H, Hkv, L, L, d, seed=171, device=DEV)
+    shapes = [x["q"].shape, x["k"].shape, x["v"].shape, x["q"].shape]
+    nbytes = [2 * math.prod(sh) for sh in shapes]
+    total = sum((n + 255) // 256 * 256 for n in nbytes)
+    buf = torch.empty((3 << 31) + total + 256, dtype=torch.uint8, device=DEV)
+    low = buf.data_ptr() & 0xFFFFFFFF
+    if 0x80000000 <= low and low + total + 256 < (1 << 32):
+        off = 0
+    elif low < 0x80000000:
+        off = 0x80000000 - low
+    else:
+        off = (1 << 32) - low + 0x80000000
+    off = (off + 255) // 256 * 256
+    views = []
+    for n, sh in zip(nbytes, shapes):
+        views.append(buf[off:off + n].view(torch.bfloat16).view(sh))
+        off += (n + 255) // 256 * 256
+    q, k, v, o = views
+    q.copy_(x["q"]); k.copy_(x["k"]); v.copy_(x["v"])
+    for t in (q, k, v, o):
+        assert (t.data_ptr() >> 31) & 1 == 1
+    scale = 1.0 / math.sqrt(d)
+    _, lse = fa.fwd(q, k, v, causal=True, scale=scale, out=o)
+    torch.cuda.synchronize()
+    O, LSE = oracle.attention(*(fa_inputs.as_oracle_f64(x[n]) for n in ("q", "k", "v")), scale=scale, causal=True)
+    compare(o, lse, O, LSE, bf16_out=True, what="high-address tensors")
+    del buf
+
+
 def test_varlen_sequence_equals_fresh_call_and_nan_padding():
     fa = _fa()
     announce(entry="fa_fwd", case="varlen vs fresh + NaN padding", B=3, H=4, Hkv=2, L=500, d=128)
