@@ -354,6 +354,11 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
   // operand just before its MFMA (a full LDS round trip per MFMA) or gathers the softmax
   // work into stretches with no MFMA beside them. `mid` runs at step kDmaStep (tile loads).
 
+  // The exp work of a tile is split between the two regions so that both carry about the
+  // same VALU load: region X takes elements [0, kExpX), region Y the last quarter (their
+  // operands belong to the last P V k-step, which region Y reaches only in its second half).
+  constexpr int kElems = 32 * QB;
+  constexpr int kExpX = kElems - kElems / 4;
   // Keep running sums where they are computed: without this, chains of adds are linearised
   // after the region's last MFMA, where nothing else overlaps them. (Not for maxima: an
   // opaque value must be canonicalised before each fmaxf, which costs more than it saves.)
@@ -362,6 +367,13 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(x[qb][i]));
+  };
+  // Row-sum partial and bf16 P^T operand of element e, whose p is in pv[e] (element
+  // numbering as below).
+  auto sum_elem = [&](const float (&pv)[kElems], int e, float (&rs)[QB][4]) {
+    const int qb = e / 32, h = (e % 32) / 16, r = e % 16;
+    rs[qb][e & 3] += pv[e];
+    pb[qb][2 * h + (r >> 3)][r & 7] = (__bf16)pv[e];
   };
   // p = 2^t of element e of tile `cu`, added to the row-sum partials and converted into the
   // bf16 P^T operands. Accumulator element r of key half h of row block qb is element
@@ -372,17 +384,12 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
     rs[qb][e & 3] += p;
     pb[qb][2 * h + (r >> 3)][r & 7] = (__bf16)p;
   };
-  // The exp work of a tile is split between the two regions so that both carry about the
-  // same VALU load: region X takes elements [0, kExpX), region Y the last quarter (their
-  // operands belong to the last P V k-step, which region Y reaches only in its second half).
-  constexpr int kElems = 32 * QB;
-  constexpr int kExpX = kElems - kElems / 4;
-
   // Region X: S^T of the next tile into `nx`, beside p = 2^t, the row sums and the bf16 P^T
   // operands of most of the current tile `cu` (whose scores were shifted in region Y).
   auto region_x = [&](int ksl, f32x16 (&nx)[QB][2], f32x16 (&cu)[QB][2], auto&& mid) {
     constexpr int NF = C::NKF;
     const f32x16 zero = {};
+    float pv[kElems];  // p of element e, between its exp and its sum / conversion
     float rs[QB][4];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
@@ -399,12 +406,18 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
       const int kb = f / C::QKS, ks = f % C::QKS;
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) nx[qb][kb] = mfma_32x32x16(x, qf[qb][ks], ks == 0 ? zero : nx[qb][kb]);
+      // This step's exps; the sums and conversions of the previous step's (their results
+      // are ready by now, so the wave does not stall on them).
 #pragma unroll
-      for (int e = f * kExpX / NF; e < (f + 1) * kExpX / NF; ++e) exp_elem(cu, e, rs);
+      for (int e = (f - 1) * kExpX / NF; f > 0 && e < f * kExpX / NF; ++e) sum_elem(pv, e, rs);
+#pragma unroll
+      for (int e = f * kExpX / NF; e < (f + 1) * kExpX / NF; ++e) pv[e] = exp2_hw(cu[e / 32][(e % 32) / 16][e % 16]);
       pin_partials(rs);
       if (f == kDmaStep) mid();
     }
     __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int e = (NF - 1) * kExpX / NF; e < kExpX; ++e) sum_elem(pv, e, rs);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       l[qb] += (rs[qb][0] + rs[qb][1]) + (rs[qb][2] + rs[qb][3]);
