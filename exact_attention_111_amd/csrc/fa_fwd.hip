@@ -11,22 +11,21 @@
 // gfx950 mapping. One workgroup = one 256-row query tile of one head. At d = 128 it is 8
 // wave64s of 32 query rows (two waves per SIMD, so a wave fits in 256 VGPRs); at d = 64 it
 // is 4 wave64s of 64 rows (two 32-row blocks each, one wave per SIMD).
-//   * Software pipeline inside each wave, one workgroup barrier per 64-key tile. The body
-//     for tile j has two regions, each a single straight run of code that the scheduler
-//     interleaves: (X) the MFMAs of S for tile j + 1 beside the exp / row-sum / bf16
-//     conversion of tile j, then (Y) the MFMAs of P V for tile j beside the mask / row-max /
-//     scale-and-shift of tile j + 1. The matrix cores run while the same wave issues its
-//     softmax arithmetic, so the softmax costs issue slots, not a serial phase.
-//   * Q rows stay in registers as the B operand of v_mfma_f32_32x32x16_bf16; every K or V
-//     operand read from LDS feeds both 32-row blocks (two MFMAs), halving LDS reads per MFMA
-//     compared with 32 rows per wave.
-//   * K/V tiles go HBM -> LDS with 16-byte direct-to-LDS loads (global_load_lds_dwordx4; no
-//     VGPR staging, no VALU work), double buffered, K one tile ahead of V. They are issued
-//     so that the compiler does not see them (it would otherwise make every LDS read wait
-//     for them); each wave waits for its own loads before the barrier that closes a tile.
+//   * One body per 64-key tile j, one workgroup barrier each, in two regions: (X) the MFMAs
+//     of S for tile j + 1 beside exp / row sum / bf16 conversion of most of tile j, then
+//     (Y) the MFMAs of P V for tile j beside the rest of tile j's exps and the scale-and-
+//     shift of tile j + 1. Each region is written out one step per MFMA (operand read four
+//     steps ahead, a fixed slice of softmax work, a scheduling fence), so the matrix cores
+//     run while the wave issues its softmax arithmetic.
+//   * Q rows stay in registers as the B operand of v_mfma_f32_32x32x16_bf16.
+//   * K/V tiles go HBM -> LDS with 16-byte buffer loads straight into LDS (no VGPR staging,
+//     no VALU work), three slots each, two tiles ahead. The buffer resource ends at the
+//     last visible key, so the loads need no bounds branch. They are issued so that the
+//     compiler does not see them (it would otherwise make every LDS read wait for them);
+//     each wave waits for its own loads before the barrier that closes a tile.
 //   * S^T = K Q^T (keys down, queries across): in the 32x32 accumulator layout a lane holds
-//     one query column, so a row's max, sum and rescale factor live in that lane (plus
-//     lane ^ 32, exchanged with v_permlane32_swap).
+//     one query column, so a row's reference, sum and rescale factor live in that lane
+//     (plus lane ^ 32, exchanged with v_permlane32_swap).
 //   * O^T = V^T P^T with P taken straight from the accumulators (converted to bf16) and the
 //     V^T operand read from the row-major V tile with ds_read_b64_tr_b16 (its 16-lane
 //     transpose turns 4 rows x 4 dims into the 4-keys-per-lane operand layout). The
@@ -34,16 +33,16 @@
 //   * LDS rows are XOR-swizzled in 16-byte chunks so that both operand reads are free of
 //     bank conflicts on gfx950's LDS (128-bit reads are served 16 lanes at a time); every
 //     operand address is computed once per lane and reused with immediate offsets.
-//   * exp is 2^x on v_exp_f32 with scale*log2(e) folded into one FMA. A row's reference
-//     maximum is raised only when a tile's maximum exceeds it by more than 2^8 (then o and
-//     l are rescaled); o / l does not depend on the reference, so this only skips work.
+//   * exp is 2^x on v_exp_f32 with scale*log2(e) folded into one FMA. Tiles are shifted by
+//     the row's current reference m without computing their maximum; only a part whose p
+//     went past 2^32 (or a row's first visible keys) raises m and rescales l and o. o / l
+//     does not depend on the reference, so this only skips work.
 //   * Causal and padding masks are applied element-wise only on tiles that straddle the
 //     diagonal or the sequence end, and key tiles past the query tile's last visible key are
-//     never loaded. Tiles a wave cannot see at all are still multiplied (with P = 0): the
-//     pipeline stays branch-free at the price of a few MFMAs near the diagonal.
-//   * Workgroups are renumbered so that the ones dispatched to the same XCD (dispatch is
-//     round-robin over the 8 XCDs) work on the same head at the same time and share its
-//     K/V through that XCD's L2; within a head the heaviest (latest) query tiles go first.
+//     never loaded.
+//   * Heads are dealt round-robin to the 8 XCDs (dispatch is round-robin over them), and
+//     each XCD works through its heads one at a time, heaviest query tile first, so that its
+//     CUs share that head's K/V in the XCD's L2.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -78,7 +77,6 @@ struct FwdCfg {
   static_assert(SEGS % NW == 0, "tile must split evenly over the waves");
 };
 
-constexpr float kLazyRescale = 8.0f;  // log2 of the largest probability allowed before rescaling
 constexpr int kPF = 4;                // operand reads issued this many operands ahead
 constexpr int kDmaStep = 2;           // step of each region at which its tile loads are issued
 
@@ -223,14 +221,12 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
     for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[qb][nb][r] = 0.f;
-  float m[QB], l[QB], alpha[QB];  // reference max (scaled, base 2), this lane's part of the sum
+  float m[QB], l[QB];  // reference (scaled, base 2) and this lane's part of the row sum
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     m[qb] = kNegInf;
     l[qb] = 0.f;
-    alpha[qb] = 1.f;
   }
-  bool rescale = false;  // o must be multiplied by alpha before the next P V
   f32x16 sa[QB][2], sb[QB][2];  // S^T (then scaled, shifted scores) of two consecutive tiles
   bf16x8 pb[QB][4];              // P^T of the tile whose P V runs next
 
@@ -316,10 +312,9 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
     }
   };
 
-  // Softmax, first half (branch-free): row max, lazy reference update, and the shift
-  // t = s * scale*log2(e) - m in place. `valid` = false turns it into a no-op on the state.
-  auto softmax_max = [&](bool valid, f32x16 (&sx)[QB][2]) {
-    bool any_raise = false;
+  // First tile only: the row's reference m is its maximum (exact), then the shift
+  // t = s * scale*log2(e) - m in place. A row that sees nothing keeps m = -inf and t = s.
+  auto first_shift = [&](f32x16 (&sx)[QB][2]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float mp[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
@@ -331,21 +326,13 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
       // lanes l and l ^ 32 hold the same row: exchange halves with v_permlane32_swap
       const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, mx),
                                                        __builtin_bit_cast(unsigned, mx), false, false);
-      mx = fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1])) * a.scale_log2;
-      const bool raise = valid && (mx > m[qb] + kLazyRescale);  // also true for the first visible tile
-      const float m_new = raise ? mx : m[qb];
-      const float al = raise ? exp2_hw(m[qb] - m_new) : 1.f;
-      alpha[qb] = rescale ? alpha[qb] * al : al;
-      l[qb] *= al;
-      m[qb] = m_new;
-      any_raise |= raise;
-      const float neg_m = (m_new == kNegInf) ? 0.f : -m_new;  // a row that has seen nothing keeps p = 0
+      m[qb] = fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1])) * a.scale_log2;
+      const float neg_m = (m[qb] == kNegInf) ? 0.f : -m[qb];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) sx[qb][kb][r] = fmaf(sx[qb][kb][r], a.scale_log2, neg_m);
     }
-    rescale = rescale || (__builtin_amdgcn_ballot_w64(any_raise) != 0);
   };
   // The two halves of a body, written out step by step. A region is one step per MFMA
   // operand: step f takes the operand read kPF steps earlier, issues the read for step
@@ -357,35 +344,89 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
   // The exp work of a tile is split between the two regions so that both carry about the
   // same VALU load: region X takes elements [0, kExpX), region Y the last quarter (their
   // operands belong to the last P V k-step, which region Y reaches only in its second half).
+  // Accumulator element r of key half h of row block qb is element e = 32 qb + 16 h + r; P^T
+  // operand 2 h + r / 8 (k-step) holds its elements r % 8.
   constexpr int kElems = 32 * QB;
   constexpr int kExpX = kElems - kElems / 4;
+  auto elem = [](const f32x16 (&x)[QB][2], int e) { return x[e / 32][(e % 32) / 16][e % 16]; };
   // Keep running sums where they are computed: without this, chains of adds are linearised
-  // after the region's last MFMA, where nothing else overlaps them. (Not for maxima: an
-  // opaque value must be canonicalised before each fmaxf, which costs more than it saves.)
+  // after the region's last MFMA, where nothing else overlaps them.
   auto pin_partials = [](float (&x)[QB][4]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(x[qb][i]));
   };
-  // Row-sum partial and bf16 P^T operand of element e, whose p is in pv[e] (element
-  // numbering as below).
+  // Row-sum partial and bf16 P^T operand of element e, whose p is in pv[e].
   auto sum_elem = [&](const float (&pv)[kElems], int e, float (&rs)[QB][4]) {
     const int qb = e / 32, h = (e % 32) / 16, r = e % 16;
     rs[qb][e & 3] += pv[e];
     pb[qb][2 * h + (r >> 3)][r & 7] = (__bf16)pv[e];
   };
-  // p = 2^t of element e of tile `cu`, added to the row-sum partials and converted into the
-  // bf16 P^T operands. Accumulator element r of key half h of row block qb is element
-  // 32 qb + 16 h + r; P^T operand 2 h + r / 8 (k-step) holds its elements r % 8.
-  auto exp_elem = [&](f32x16 (&cu)[QB][2], int e, float (&rs)[QB][4]) {
-    const int qb = e / 32, h = (e % 32) / 16, r = e % 16;
-    const float p = exp2_hw(cu[qb][h][r]);
-    rs[qb][e & 3] += p;
-    pb[qb][2 * h + (r >> 3)][r & 7] = (__bf16)p;
+
+  // Softmax without a per-tile maximum. Scores are shifted by the row's current reference m
+  // before anyone looks at the tile, p = 2^(s*scale*log2(e) - m) is formed, and only then is
+  // the part checked: it stands unless some p went past kMaxP (or is not a number), or the
+  // row had no reference yet. Otherwise (rare after a row's first tile; a wave-uniform
+  // branch) the row's reference is raised to the part's maximum, l and o are rescaled at
+  // once, and the part's p are recomputed. Parts whose p stayed at or below 2^32 keep fp32
+  // far from overflow (l <= keys * 2^32). Elements [E0, E1) of `cu` have been exponentiated
+  // (sums in rs); [E1, E2) are still to be, and are shifted along with them.
+  constexpr float kMaxP = 4294967296.f;
+  auto fix_part = [&](f32x16 (&cu)[QB][2], auto e0c, auto e1c, auto e2c, float (&rs)[QB][4]) {
+    constexpr int E0 = decltype(e0c)::value, E1 = decltype(e1c)::value, E2 = decltype(e2c)::value;
+    bool need[QB], any = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float sum = (rs[qb][0] + rs[qb][1]) + (rs[qb][2] + rs[qb][3]);
+      need[qb] = !(sum <= kMaxP) || (m[qb] == kNegInf && sum > 0.f);
+      any |= need[qb];
+    }
+    if (__builtin_amdgcn_ballot_w64(any) == 0) return;  // the fast path holds for every row
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int e = E0; e < E1; ++e)
+        if (e / 32 == qb) mx = fmaxf(mx, elem(cu, e));
+      // lanes l and l ^ 32 hold the same row: combine their halves
+      const auto sm = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, mx),
+                                                       __builtin_bit_cast(unsigned, mx), false, false);
+      mx = fmaxf(__builtin_bit_cast(float, sm[0]), __builtin_bit_cast(float, sm[1]));
+      const auto sn = __builtin_amdgcn_permlane32_swap((unsigned)need[qb], (unsigned)need[qb], false, false);
+      const bool row_need = (sn[0] | sn[1]) != 0u && mx != kNegInf;
+      float d = 0.f, al = 1.f;
+      if (row_need) {
+        const float base = (m[qb] == kNegInf) ? 0.f : m[qb];  // the scores were shifted by -base
+        const float m_new = base + mx;
+        al = exp2_hw(m[qb] - m_new);  // 0 for a row without a reference (l, o are 0 then)
+        m[qb] = m_new;
+        d = mx;
+      }
+      l[qb] *= al;
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[qb][nb][r] *= al;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rs[qb][i] = 0.f;
+#pragma unroll
+      for (int e = E0; e < E2; ++e) {
+        if (e / 32 != qb) continue;
+        const int h = (e % 32) / 16, r = e % 16;
+        cu[qb][h][r] -= d;
+        if (e < E1) {
+          const float pe = exp2_hw(cu[qb][h][r]);
+          rs[qb][e & 3] += pe;
+          pb[qb][2 * h + (r >> 3)][r & 7] = (__bf16)pe;
+        }
+      }
+    }
   };
+
   // Region X: S^T of the next tile into `nx`, beside p = 2^t, the row sums and the bf16 P^T
-  // operands of most of the current tile `cu` (whose scores were shifted in region Y).
+  // operands of most of the current tile `cu` (whose scores were shifted in region Y), and
+  // the check of that part.
   auto region_x = [&](int ksl, f32x16 (&nx)[QB][2], f32x16 (&cu)[QB][2], auto&& mid) {
     constexpr int NF = C::NKF;
     const f32x16 zero = {};
@@ -411,44 +452,41 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
 #pragma unroll
       for (int e = (f - 1) * kExpX / NF; f > 0 && e < f * kExpX / NF; ++e) sum_elem(pv, e, rs);
 #pragma unroll
-      for (int e = f * kExpX / NF; e < (f + 1) * kExpX / NF; ++e) pv[e] = exp2_hw(cu[e / 32][(e % 32) / 16][e % 16]);
+      for (int e = f * kExpX / NF; e < (f + 1) * kExpX / NF; ++e) pv[e] = exp2_hw(elem(cu, e));
       pin_partials(rs);
       if (f == kDmaStep) mid();
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int e = (NF - 1) * kExpX / NF; e < kExpX; ++e) sum_elem(pv, e, rs);
+    fix_part(cu, std::integral_constant<int, 0>{}, std::integral_constant<int, kExpX>{},
+             std::integral_constant<int, kElems>{}, rs);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       l[qb] += (rs[qb][0] + rs[qb][1]) + (rs[qb][2] + rs[qb][3]);
       asm volatile("" : "+v"(l[qb]));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(pb[qb][i]));
+      for (int i = 0; i < 4; ++i)  // operands completed here (the rest are written in region Y)
+        if (32 * qb + 8 * i + 8 <= kExpX) asm volatile("" : "+v"(pb[qb][i]));
     }
     __builtin_amdgcn_sched_barrier(0);
   };
 
   // Region Y: O^T += V^T P^T of the current tile `cu` (V tile at byte `vs` of the V slots),
-  // beside the rest of `cu`'s exp work (first half of the steps) and the softmax's first half
-  // for the next tile `nx`: row maximum over the first half of the steps, the lazy reference
-  // update at the middle step, then t = s * scale*log2(e) - m in place. `valid` = false
-  // leaves the row state untouched.
-  auto region_y = [&](int vs, f32x16 (&nx)[QB][2], f32x16 (&cu)[QB][2], bool valid, auto&& mid) {
+  // beside the rest of `cu`'s exp work and its check (first half of the steps), then
+  // t = s * scale*log2(e) - m in place for the next tile `nx` (second half).
+  auto region_y = [&](int vs, f32x16 (&nx)[QB][2], f32x16 (&cu)[QB][2], auto&& mid) {
     constexpr int NF = C::NVF;
-    constexpr int NM = NF / 2;                       // steps of the row maximum
-    constexpr int EPM = 32 * QB / NM;                // elements per maximum step
+    constexpr int NM = NF / 2;                       // steps of the leftover exps; the check
     constexpr int NS = NF - NM - 1;                  // steps of the shift
     constexpr int EPF = (32 * QB + NS - 1) / NS;     // elements per shift step
     constexpr int NE = kElems - kExpX;               // exp elements left over from region X
-    float mp[QB][4], neg_m[QB], rs[QB][4];
+    float pv[kElems], rs[QB][4], neg_m[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       neg_m[qb] = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        mp[qb][i] = kNegInf;
-        rs[qb][i] = 0.f;
-      }
+      for (int i = 0; i < 4; ++i) rs[qb][i] = 0.f;
     }
     bf16x8 buf[kPF];
 #pragma unroll
@@ -456,6 +494,19 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       __builtin_amdgcn_sched_barrier(0);
+      if (f == NM) {
+        // The leftover part is complete: check it before the P V k-steps that read it.
+#pragma unroll
+        for (int e = kExpX + (NM - 1) * NE / NM; e < kElems; ++e) sum_elem(pv, e, rs);
+        fix_part(cu, std::integral_constant<int, kExpX>{}, std::integral_constant<int, kElems>{},
+                 std::integral_constant<int, kElems>{}, rs);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          l[qb] += (rs[qb][0] + rs[qb][1]) + (rs[qb][2] + rs[qb][3]);
+          neg_m[qb] = (m[qb] == kNegInf) ? 0.f : -m[qb];  // a row without a reference shifts by 0
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
       const bf16x8 x = buf[f % kPF];
       if (f + kPF < NF) buf[f % kPF] = read_v(vs, f + kPF);
       const int ks = f / C::NB, nb = f % C::NB;
@@ -463,38 +514,14 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
       for (int qb = 0; qb < QB; ++qb) oacc[qb][nb] = mfma_32x32x16(x, pb[qb][ks], oacc[qb][nb]);
       if (f < NM) {
 #pragma unroll
-        for (int e = kExpX + f * NE / NM; e < kExpX + (f + 1) * NE / NM; ++e) exp_elem(cu, e, rs);
+        for (int e = kExpX + (f - 1) * NE / NM; f > 0 && e < kExpX + f * NE / NM; ++e) sum_elem(pv, e, rs);
+#pragma unroll
+        for (int e = kExpX + f * NE / NM; e < kExpX + (f + 1) * NE / NM; ++e) pv[e] = exp2_hw(elem(cu, e));
         pin_partials(rs);
-#pragma unroll
-        for (int e = f * EPM; e < (f + 1) * EPM; ++e) {
-          const int qb = e / 32, h = (e % 32) / 16, r = e % 16;
-          mp[qb][e & 3] = fmaxf(mp[qb][e & 3], nx[qb][h][r]);
-        }
-      } else if (f == NM) {
-        bool any_raise = false;
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          // the current tile's sum joins l before l is rescaled to a new reference
-          l[qb] += (rs[qb][0] + rs[qb][1]) + (rs[qb][2] + rs[qb][3]);
-          float mx = fmaxf(fmaxf(mp[qb][0], mp[qb][1]), fmaxf(mp[qb][2], mp[qb][3]));
-          // lanes l and l ^ 32 hold the same row: exchange halves with v_permlane32_swap
-          const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, mx),
-                                                           __builtin_bit_cast(unsigned, mx), false, false);
-          mx = fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1])) * a.scale_log2;
-          const bool raise = valid && (mx > m[qb] + kLazyRescale);  // also true for the first visible tile
-          const float m_new = raise ? mx : m[qb];
-          const float al = raise ? exp2_hw(m[qb] - m_new) : 1.f;
-          alpha[qb] = rescale ? alpha[qb] * al : al;
-          l[qb] *= al;
-          m[qb] = m_new;
-          any_raise |= raise;
-          neg_m[qb] = (m_new == kNegInf) ? 0.f : -m_new;  // a row that has seen nothing keeps p = 0
-        }
-        rescale = rescale || (__builtin_amdgcn_ballot_w64(any_raise) != 0);
-      } else {
+      } else if (f > NM) {
         const int s0 = (f - NM - 1) * EPF;
 #pragma unroll
-        for (int e = s0; e < s0 + EPF && e < 32 * QB; ++e) {
+        for (int e = s0; e < s0 + EPF && e < kElems; ++e) {
           const int qb = e / 32, h = (e % 32) / 16, r = e % 16;
           nx[qb][h][r] = fmaf(nx[qb][h][r], a.scale_log2, neg_m[qb]);
         }
@@ -504,7 +531,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      asm volatile("" : "+v"(l[qb]), "+v"(m[qb]), "+v"(alpha[qb]));
+      asm volatile("" : "+v"(l[qb]), "+v"(m[qb]));
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) asm volatile("" : "+v"(nx[qb][kb]));
     }
@@ -535,20 +562,13 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
     const bool ld_k = kAll || j + 3 < ntk, ld_v = kAll || j + 2 < ntk;
     auto load_k = [&] { if (ld_k) stage(j + 3, 0, (u % 3) * C::TILE_BYTES); };        // slot of tile j + 3
     auto load_v = [&] { if (ld_v) stage(j + 2, 1, (3 + (u + 2) % 3) * C::TILE_BYTES); };  // slot of tile j + 2
-    if (rescale) {  // wave-uniform; rare once a row's maximum has settled
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[qb][nb][r] *= alpha[qb];
-      rescale = false;
-    }
     __builtin_amdgcn_sched_barrier(0);
     region_x(ksl_next, nxt, cur, load_k);
     if (j + 1 < ntk) mask_tile(j + 1, nxt);
     __builtin_amdgcn_sched_barrier(0);
-    region_y(vsl_cur, nxt, cur, j + 1 < ntk, load_v);
+    if (w >= C::NW / 2) __builtin_amdgcn_s_setprio(1);  // the wave that finished region X later goes first
+    region_y(vsl_cur, nxt, cur, load_v);
+    __builtin_amdgcn_s_setprio(0);
     // Wait for this wave's loads issued one iteration ago (K tile j + 2, V tile j + 1; the
     // ones just issued may stay in flight), then the barrier makes everyone's visible and
     // frees the slots read in this iteration.
@@ -573,7 +593,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
     if (1 < ntk) stage(1, 1, v_slot(1));
     s_mfmas(0, sa);
     mask_tile(0, sa);
-    softmax_max(true, sa);
+    first_shift(sa);
     // Six bodies per trip, leaving after the body of the last tile.
     using std::integral_constant;
     for (int j = 0;; j += 6) {
@@ -595,14 +615,6 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
 
   // Epilogue: O = o / l and LSE = ln(2) * (m + log2 l); padding rows and rows that saw
   // no key get O = 0 and LSE = -inf.
-  if (rescale) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[qb][nb][r] *= alpha[qb];
-  }
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float lt = l[qb] + __shfl_xor(l[qb], 32);

@@ -183,6 +183,29 @@ def test_causal_row0_bitwise_and_determinism():
     assert torch.equal(o, o2) and torch.equal(lse, lse2)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_scores_growing_across_tiles(d, causal):
+    """Scores that climb by about 46 in base 2 per 64-key tile, so every tile raises each
+    row's reference (the rarely taken path of the softmax); plus random components."""
+    fa = _fa()
+    B, H, L = 1, 2, 700
+    announce(entry="fa_fwd", case="scores growing across tiles", B=B, H=H, L=L, d=d, causal=causal)
+    g = torch.Generator().manual_seed(181)
+    q = torch.randn(B, H, L, d, generator=g) * 0.5
+    k = torch.randn(B, H, L, d, generator=g) * 0.5
+    v = torch.randn(B, H, L, d, generator=g)
+    scale = 1.0 / math.sqrt(d)
+    q[..., 0] = 4.0 / scale                                   # exact in bf16 for d = 64 and 128
+    k[..., 0] = torch.arange(L, dtype=torch.float32) / 8.0   # j / 8: exact in bf16 for j < 2048
+    q, k, v = (t.to(torch.bfloat16).to(DEV) for t in (q, k, v))
+    o, lse = fa.fwd(q, k, v, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    O, LSE = oracle.attention(*(fa_inputs.as_oracle_f64(t) for t in (q, k, v)), scale=scale, causal=causal)
+    assert np.isfinite(LSE).all()
+    compare(o, lse, O, LSE, bf16_out=True, what=f"growing scores d{d} c{int(causal)}")
+
+
 def test_uniform_attention_closed_form():
     """Q = 0: every visible key has weight 1/#visible, so O_i is a prefix mean of V and
     LSE_i = ln(i + 1) under the causal mask."""
