@@ -6,3 +6,4 @@ binding) never does.
 """
 from .attention import (attention, attention_head, decode, merge, online_softmax_rows,  # noqa: F401
                         part_state)
+from .backward import attention_backward, attention_backward_head  # noqa: F401
