@@ -37,7 +37,7 @@ PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
 PREFILL = "causal_prefill_B1_H32_L16384_d128"
 DECODE = "decode_B64_H32_Hkv8_ctx32768_d128"
 # Sources whose compiled kernels a committed counter profile describes.
-KERNEL_SOURCES = {"prefill": ["fa_fwd.hip", "fa_device.h", "fa_launch.h"],
+KERNEL_SOURCES = {"prefill": ["fa_fwd.hip", "fa_tiles.h", "fa_device.h", "fa_launch.h"],
                   "decode": ["fa_decode.hip", "fa_device.h", "fa_launch.h"]}
 
 

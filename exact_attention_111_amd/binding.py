@@ -48,6 +48,11 @@ def lib() -> ctypes.CDLL:
     L.fa_decode_workspace_bytes.restype = ctypes.c_size_t
     L.fa_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, vp, vp, ctypes.c_size_t, vp]
     L.fa_decode.restype = i32
+    L.fa_bwd_workspace_bytes.argtypes = [i32, i32, i32]
+    L.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
+    L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp, vp,
+                         ctypes.c_size_t, vp]
+    L.fa_bwd.restype = i32
     L.fa_status_string.argtypes = [i32]
     L.fa_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -134,3 +139,40 @@ def decode(q, k_cache, v_cache, ctx_lens, *, scale: float | None = None, workspa
                          _stream(q.device))
     _check(st, "fa_decode")
     return out, lse
+
+
+def bwd_workspace_bytes(B: int, H: int, Lq: int) -> int:
+    return int(lib().fa_bwd_workspace_bytes(B, H, Lq))
+
+
+def bwd(q, k, v, o, dout, lse, *, causal: bool = False, scale: float | None = None, seqlens=None, workspace=None,
+        dq=None, dk=None, dv=None):
+    """Gradients through ``fa_bwd`` (bf16): (dq, dk, dv) for upstream gradient ``dout``.
+
+    q, o, dout: [B, H, Lq, d]; k, v: [B, Hkv, Lk, d], bf16, contiguous; lse: [B, H, Lq] fp32
+    from ``fwd``; causal, scale and seqlens as passed to ``fwd``.
+    """
+    B, H, Lq, d = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = bwd_workspace_bytes(B, H, Lq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    for t in (q, k, v, o, dout, lse, dq, dk, dv, workspace):
+        if not t.is_contiguous():
+            raise ValueError("libfa needs contiguous tensors")
+    if not all(t.dtype == torch.bfloat16 for t in (q, k, v, o, dout, dq, dk, dv)):
+        raise ValueError("bwd needs bfloat16 q, k, v, o, dout and gradients")
+    if lse.dtype != torch.float32:
+        raise ValueError("lse must be float32")
+    if seqlens is not None and seqlens.dtype != torch.int32:
+        raise ValueError("seqlens must be int32")
+    st = lib().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                      B, H, Hkv, Lq, Lk, d, float(scale), int(bool(causal)), _ptr(seqlens), _ptr(workspace),
+                      workspace.numel() * workspace.element_size(), _stream(q.device))
+    _check(st, "fa_bwd")
+    return dq, dk, dv

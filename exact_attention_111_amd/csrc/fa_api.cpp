@@ -54,6 +54,21 @@ fa_status validate_decode(const void* q, const void* kc, const void* vc, const v
   return FA_OK;
 }
 
+fa_status validate_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                       const void* lse, const void* dq, const void* dk, const void* dv, int B, int H, int Hkv, int Lq,
+                       int Lk, int d, float scale, int causal, const int32_t* seqlens, const void* ws,
+                       size_t ws_bytes) {
+  const fa_status s = validate_fwd(q, k, v, o, lse, B, H, Hkv, Lq, Lk, d, scale, causal, seqlens);
+  if (s == FA_ERR_INVALID) return s;
+  const long long nq = (long long)B * H * Lq * d;
+  const long long nkv = (long long)B * Hkv * Lk * d;
+  if (!tensor_ok(dout, nq) || !tensor_ok(dq, nq) || !tensor_ok(dk, nkv) || !tensor_ok(dv, nkv)) return FA_ERR_INVALID;
+  if (s != FA_OK) return s;
+  const size_t need = fa_bwd_workspace_bytes(B, H, Lq);
+  if (need > 0 && (ws == nullptr || !aligned16(ws) || ws_bytes < need)) return FA_ERR_INVALID;
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -95,6 +110,23 @@ fa_status fa_decode(const void* q, const void* k_cache, const void* v_cache, voi
   float* ws_ml = ws_o + (size_t)B * H * nc * d;
   fa::DecodeParams p{q, k_cache, v_cache, o, lse, B, H, Hkv, Lmax, d, scale, ctx_lens, ws_o, ws_ml};
   return fa::launch_decode(p, static_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int Lq) {
+  if (B < 0 || H < 0 || Lq < 0) return 0;
+  return (size_t)B * H * Lq * sizeof(float);  // D = rowsum(dO * O) per query row
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                 void* dq, void* dk, void* dv, int B, int H, int Hkv, int Lq, int Lk, int d, float scale, int causal,
+                 const int32_t* seqlens, void* workspace, size_t workspace_bytes, void* stream) {
+  const fa_status s = validate_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, Hkv, Lq, Lk, d, scale, causal, seqlens,
+                                   workspace, workspace_bytes);
+  if (s != FA_OK) return s;
+  if (B == 0) return FA_OK;  // otherwise dK/dV are written even when there are no query rows (then zero)
+  fa::BwdParams p{q, k, v, o, dout, lse, dq, dk, dv, B, H, Hkv, Lq, Lk, d, scale, causal, seqlens,
+                  static_cast<float*>(workspace)};
+  return fa::launch_bwd(p, static_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 const char* fa_status_string(fa_status s) {

@@ -47,6 +47,7 @@
 
 #include "fa_device.h"
 #include "fa_launch.h"
+#include "fa_tiles.h"
 
 namespace fa {
 namespace {
@@ -94,19 +95,6 @@ struct FwdArgs {
   int causal;
   const int32_t* seqlens;
 };
-
-// XOR applied to the 16-byte chunk index of tile row r.
-//   K (read by 16 lanes = 16 consecutive rows, same logical chunk): every row of a 16-row
-//   group must land on a different 16-byte bank slot of the 256-byte bank window.
-//   V (read transposed: a 16-lane group touches 4 consecutive rows x one 32-byte chunk pair,
-//   two groups per access): the 8 (row, pair) slots of an access must differ.
-template <int D>
-__device__ __forceinline__ int k_xor(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
-template <int D>
-__device__ __forceinline__ int v_xor(int r) {
-  const int j = r & 3;
-  return D == 128 ? 2 * (j ^ ((j & 1) << 2)) : ((j & 2) << 1);
-}
 
 template <int D, typename IT, typename OT>
 __global__ __launch_bounds__(FwdCfg<D>::NT)

@@ -39,4 +39,24 @@ struct DecodeParams {
 inline int decode_num_chunks(int Lmax) { return (Lmax + kDecodeChunk - 1) / kDecodeChunk; }
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 
+// Backward (bf16): row dots D = rowsum(dO * O), then dK/dV per key block and dQ per query
+// block, both recomputing P from Q, K and the saved LSE.
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  int B, H, Hkv, Lq, Lk, d;
+  float scale;
+  int causal;
+  const int32_t* seqlens;
+  float* ws_d;  // [B, H, Lq]
+};
+hipError_t launch_bwd(const BwdParams& p, hipStream_t stream);
+
 }  // namespace fa

@@ -104,6 +104,35 @@ fa_status fa_decode(const void* q, const void* k_cache, const void* v_cache, voi
                     int B, int H, int Hkv, int Lmax, int d, float scale, const int32_t* ctx_lens,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * fa_bwd_workspace_bytes — bytes of device workspace fa_bwd needs: one fp32 per query row
+ * (D = rowsum(dO * O)), i.e. B * H * Lq * 4. Returns 0 for invalid sizes.
+ */
+size_t fa_bwd_workspace_bytes(int B, int H, int Lq);
+
+/*
+ * fa_bwd — gradients of fa_fwd with respect to q, k and v, given the upstream gradient dout
+ * of o. "FlashAttention 与长上下文：先分清三张账", section "FlashAttention 的关键是 online
+ * softmax": the backward pass keeps only the forward's per-row statistic and recomputes the
+ * score tiles instead of storing them. With P = softmax(scale Q K^T + M) (M as in fa_fwd):
+ *   dV = P^T dO,  dS = P * (dO V^T - rowsum(dO * O)),  dQ = scale dS K,  dK = scale dS^T Q,
+ * with dK and dV of a KV head summed over its query heads (GQA).
+ *
+ *   q, o, dout, dq : bf16 [B, H, Lq, d]      k, v, dk, dv : bf16 [B, Hkv, Lk, d]
+ *   lse            : fp32 [B, H, Lq], the natural-log LSE fa_fwd returned for this o
+ *   o              : the fa_fwd output for these inputs (used only through rowsum(dO * O))
+ *   causal, scale, seqlens: exactly as passed to fa_fwd.
+ *   workspace      : device memory of at least fa_bwd_workspace_bytes(B, H, Lq) bytes,
+ *                    16-byte aligned, owned by the caller; its contents are scratch.
+ * dq, dk, dv are overwritten (not accumulated into). Padding rows and keys outside a
+ * sequence get zero gradients; they are never read. dout and o must be finite on the rows
+ * inside each sequence. Accumulation is fp32; results are rounded to bf16 (RNE).
+ * Requirements and errors as for fa_fwd, plus the workspace size.
+ */
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                 void* dq, void* dk, void* dv, int B, int H, int Hkv, int Lq, int Lk, int d, float scale, int causal,
+                 const int32_t* seqlens, void* workspace, size_t workspace_bytes, void* stream);
+
 /* fa_status_string — a static, human-readable name for a status code. */
 const char* fa_status_string(fa_status s);
 

@@ -21,7 +21,8 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     L = fa.lib()
     names = _declared_functions()
-    assert set(names) == {"fa_fwd", "fa_fwd_f32", "fa_decode", "fa_decode_workspace_bytes", "fa_status_string"}
+    assert set(names) == {"fa_fwd", "fa_fwd_f32", "fa_decode", "fa_decode_workspace_bytes", "fa_bwd",
+                          "fa_bwd_workspace_bytes", "fa_status_string"}
     for name in names:
         assert hasattr(L, name), name
 
@@ -105,3 +106,31 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(binding, "_LIB_PATH", str(tmp_path / "missing" / "libfa.so"))
     with pytest.raises(ImportError):
         binding.lib()
+
+
+def test_bwd_workspace_bytes():
+    L = fa.lib()
+    assert L.fa_bwd_workspace_bytes(1, 32, 16384) == 32 * 16384 * 4
+    assert L.fa_bwd_workspace_bytes(2, 3, 0) == 0
+    assert L.fa_bwd_workspace_bytes(-1, 3, 5) == 0
+
+
+def test_bwd_validation():
+    L = fa.lib()
+    INV, UNS = fa.binding.FA_ERR_INVALID, fa.binding.FA_ERR_UNSUPPORTED
+    need = L.fa_bwd_workspace_bytes(2, 4, 100)
+
+    def call(q=A, k=A, v=A, o=A, do=A, lse=A, dq=A, dk=A, dv=A, B=2, H=4, Hkv=2, Lq=100, Lk=100, d=128,
+             scale=0.125, causal=1, seqlens=None, ws=A2, ws_bytes=need):
+        return L.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, B, H, Hkv, Lq, Lk, d, scale, causal, seqlens, ws, ws_bytes,
+                        None)
+    assert call(dk=None) == INV
+    assert call(do=MIS) == INV
+    assert call(H=5) == INV
+    assert call(scale=-1.0) == INV
+    assert call(causal=3) == INV
+    assert call(Lq=4, Lk=5, seqlens=A) == INV
+    assert call(ws=None) == INV
+    assert call(ws_bytes=need - 4) == INV
+    assert call(d=96) == UNS
+    assert call(B=0) == 0  # empty: nothing to write, nothing enqueued

@@ -1,0 +1,186 @@
+"""GPU parity of fa_bwd against the fp64 backward oracle (through the C ABI).
+
+Gradients have no tolerance of their own on the pages; the bound used here comes from the
+arithmetic of the kernels: P and dS enter the products as bf16 (relative rounding 2^-9 per
+element) with fp32 accumulation, and dQ, dK, dV are rounded to bf16 (2^-9). Errors are
+therefore judged relative to the size of each gradient: max |err| <= 2^-5 max |ref| and
+mean |err| <= 2^-7 mean |ref| (several bf16 ulps of headroom; the measured values are a fifth
+to a third of those bounds).
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import fa_inputs
+import oracle
+from oracle.attention import attention_head
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+MAX_REL = 2.0 ** -5
+MEAN_REL = 2.0 ** -7
+
+
+def _fa():
+    import exact_attention_111_amd as fa
+    return fa
+
+
+def announce(**case):
+    print("\n[case] " + " ".join(f"{k}={v}" for k, v in case.items()), flush=True)
+    sys.stdout.flush()
+
+
+def _close(got, ref, what, floor=1e-30):
+    """``floor``: the size below which a gradient counts as zero (then the bound is absolute)."""
+    got = got.float().cpu().numpy().astype(np.float64)
+    err = np.abs(got - ref)
+    scale_max = max(np.abs(ref).max(), floor)
+    scale_mean = max(np.abs(ref).mean(), floor)
+    mx, mn = err.max() / scale_max, err.mean() / scale_mean
+    print(f"  {what}: max|err|/max|ref| = {mx:.2e}, mean|err|/mean|ref| = {mn:.2e}", flush=True)
+    assert np.isfinite(got).all(), f"{what}: non-finite values"
+    assert mx <= MAX_REL and mn <= MEAN_REL, f"{what}: {mx:.3e} / {mn:.3e}"
+
+
+def _dout(shape, seed):
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    return torch.randn(shape, generator=g, device=DEV, dtype=torch.float32).to(torch.bfloat16)
+
+
+def run_bwd(B, H, Hkv, Lq, Lk, d, *, causal, seed, len_range=None):
+    fa = _fa()
+    announce(entry="fa_bwd", B=B, H=H, Hkv=Hkv, Lq=Lq, Lk=Lk, d=d, causal=causal, seed=seed, len_range=len_range)
+    x = fa_inputs.prefill_inputs(B, H, Hkv, Lq, Lk, d, seed=seed, device=DEV, len_range=len_range)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = fa.fwd(x["q"], x["k"], x["v"], causal=causal, scale=scale, seqlens=x["seqlens"])
+    do = _dout(o.shape, seed + 1000)
+    dq, dk, dv = fa.bwd(x["q"], x["k"], x["v"], o, do, lse, causal=causal, scale=scale, seqlens=x["seqlens"])
+    torch.cuda.synchronize()
+    sl = None if x["seqlens_cpu"] is None else x["seqlens_cpu"].numpy()
+    q64, k64, v64, do64 = (fa_inputs.as_oracle_f64(t) for t in (x["q"], x["k"], x["v"], do))
+    dQ, dK, dV = oracle.attention_backward(q64, k64, v64, do64, scale=scale, causal=causal, seqlens=sl)
+    tag = f"B{B} H{H}/{Hkv} L{Lq}x{Lk} d{d} c{int(causal)}"
+    # With a single key every row that sees anything has P = 1 whatever its score, so the
+    # exact dQ and dK are zero; what the kernel returns is rounding of dP - D, held to an
+    # absolute bound.
+    floor = 1.0 if Lk == 1 else 1e-30
+    _close(dq, dQ, "dQ " + tag, floor)
+    _close(dk, dK, "dK " + tag, floor)
+    _close(dv, dV, "dV " + tag)
+    return x, dq, dk, dv
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_ragged_multi_tile_gqa(d, causal):
+    # 300 rows = 2 x 128 + 44 (dQ blocks) and 2 x 128 + 44 keys (dK/dV blocks); 2 query heads per KV head
+    run_bwd(2, 4, 2, 300, 300, d, causal=causal, seed=200 + d + int(causal))
+
+
+@pytest.mark.parametrize("Lq,Lk", [(100, 333), (200, 70), (1, 257), (257, 1)])
+def test_bwd_unequal_lengths(Lq, Lk):
+    run_bwd(1, 2, 1, Lq, Lk, 128, causal=True, seed=210 + Lq)
+
+
+def test_bwd_varlen_padding_is_zero():
+    x, dq, dk, dv = run_bwd(3, 4, 2, 300, 300, 128, causal=True, seed=220, len_range=(1, 300))
+    for b, n in enumerate(x["seqlens_cpu"].tolist()):
+        assert torch.all(dq[b, :, n:] == 0) and torch.all(dk[b, :, n:] == 0) and torch.all(dv[b, :, n:] == 0)
+
+
+def test_bwd_gqa_matches_repeated_kv():
+    fa = _fa()
+    announce(entry="fa_bwd", case="GQA vs repeated KV", B=1, H=8, Hkv=2, L=260, d=128)
+    x = fa_inputs.prefill_inputs(1, 8, 2, 260, 260, 128, seed=230, device=DEV)
+    o, lse = fa.fwd(x["q"], x["k"], x["v"], causal=True)
+    do = _dout(o.shape, 231)
+    dq, dk, dv = fa.bwd(x["q"], x["k"], x["v"], o, do, lse, causal=True)
+    kr = x["k"].repeat_interleave(4, dim=1).contiguous()
+    vr = x["v"].repeat_interleave(4, dim=1).contiguous()
+    dq2, dk2, dv2 = fa.bwd(x["q"], kr, vr, o, do, lse, causal=True)
+    assert torch.equal(dq, dq2)  # dQ does not depend on how K/V are shared
+    for g, g2 in ((dk, dk2), (dv, dv2)):
+        summed = g2.float().view(1, 2, 4, 260, 128).sum(dim=2)
+        err = (g.float() - summed).abs().max() / summed.abs().max()
+        assert err < 2.0 ** -7, float(err)
+
+
+def test_bwd_empty_calls():
+    fa = _fa()
+    announce(entry="fa_bwd", case="empty and degenerate")
+    # no query rows: dK = dV = 0
+    q = torch.zeros(1, 2, 0, 64, device=DEV, dtype=torch.bfloat16)
+    k = torch.randn(1, 2, 70, 64, device=DEV).to(torch.bfloat16)
+    lse = torch.zeros(1, 2, 0, device=DEV)
+    dq, dk, dv = fa.bwd(q, k, k, q, q, lse, causal=False)
+    torch.cuda.synchronize()
+    assert torch.all(dk == 0) and torch.all(dv == 0)
+    # no keys: dQ = 0
+    q = torch.randn(1, 2, 50, 64, device=DEV).to(torch.bfloat16)
+    k = torch.zeros(1, 2, 0, 64, device=DEV, dtype=torch.bfloat16)
+    o, lse = fa.fwd(q, k, k)
+    dq, dk, dv = fa.bwd(q, k, k, o, q, lse)
+    torch.cuda.synchronize()
+    assert torch.all(dq == 0)
+
+
+def _rows_oracle(q, k, v, do, rows, *, scale, causal):
+    """dQ rows exactly: each row needs only its own P and dP rows."""
+    dQ = []
+    for i in rows:
+        O, _, P = attention_head(q, k, v, scale=scale, causal=causal, rows=[i], return_p=True)
+        dP = do[i] @ v.T
+        D = float(do[i] @ O[0])
+        dQ.append(scale * ((P[0] * (dP - D)) @ k))
+    return np.stack(dQ)
+
+
+def _keys_oracle(q, k, v, do, keys, *, scale, causal, block=1024):
+    """dK, dV rows of the given keys exactly: O and LSE of every row first (in row blocks),
+    then the columns of P and dS for those keys."""
+    L = q.shape[0]
+    O = np.empty_like(q)
+    LSE = np.empty(L)
+    for r0 in range(0, L, block):
+        rows = np.arange(r0, min(L, r0 + block))
+        O[rows], LSE[rows] = attention_head(q, k, v, scale=scale, causal=causal, rows=rows)
+    D = (do * O).sum(axis=1)
+    dK, dV = [], []
+    for j in keys:
+        s = scale * (q @ k[j])
+        vis = (np.arange(L) >= j) if causal else np.ones(L, bool)
+        p = np.where(vis, np.exp(np.where(vis, s, 0.0) - LSE), 0.0)
+        dp = do @ v[j]
+        ds = p * (dp - D)
+        dK.append(scale * (ds @ q))
+        dV.append(p @ do)
+    return np.stack(dK), np.stack(dV)
+
+
+def test_bwd_full_size_causal_L16384_d128_sampled():
+    """The 16,384-token causal workload at full size: sampled dQ rows of two heads and
+    sampled dK/dV keys of one head against the oracle."""
+    fa = _fa()
+    w = fa_inputs.WORKLOADS["causal_prefill_B1_H32_L16384_d128"]
+    announce(entry="fa_bwd", workload=w.name, case="sampled rows and keys")
+    x = fa_inputs.workload_inputs(w, device=DEV)
+    o, lse = fa.fwd(x["q"], x["k"], x["v"], causal=True, scale=w.scale)
+    do = _dout(o.shape, 240)
+    dq, dk, dv = fa.bwd(x["q"], x["k"], x["v"], o, do, lse, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(241)
+    rows = np.sort(np.concatenate([[0, 1, 127, 128, w.L - 1], rng.choice(w.L, 27, replace=False)]))
+    keys = np.sort(np.concatenate([[0, 1, 63, 64, w.L - 1], rng.choice(w.L, 11, replace=False)]))
+    for h in (0, 21):
+        q64, k64, v64, do64 = (fa_inputs.as_oracle_f64(t[0, h]) for t in (x["q"], x["k"], x["v"], do))
+        _close(dq[0, h, rows], _rows_oracle(q64, k64, v64, do64, rows, scale=w.scale, causal=True),
+               f"dQ rows head {h}")
+        if h == 0:
+            dK, dV = _keys_oracle(q64, k64, v64, do64, keys, scale=w.scale, causal=True)
+            _close(dk[0, h, keys], dK, "dK keys head 0")
+            _close(dv[0, h, keys], dV, "dV keys head 0")
