@@ -34,6 +34,9 @@ sys.path.insert(0, ROOT)
 METRIC = "bf16 attn-fwd TFLOP/s & % MFMA peak at L=16k d=128; decode KV-read GB/s"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
+# Backward work counted as five products of the forward's size (S, dP, dV, dK, dQ):
+# 2.5 times the forward's FLOP, whatever the kernels recompute.
+BWD_FLOP_PER_FWD = 2.5
 PREFILL = "causal_prefill_B1_H32_L16384_d128"
 DECODE = "decode_B64_H32_Hkv8_ctx32768_d128"
 # Sources whose compiled kernels a committed counter profile describes.
@@ -49,8 +52,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
     ap.add_argument("--only", default=None,
-                    help="time one part alone (for profiling): prefill, decode, copy, or any workload name of "
-                         "fa_inputs.WORKLOADS; prints a short JSON line instead of the bench line")
+                    help="time one part alone (for profiling): prefill, decode, backward, copy, any workload name of "
+                         "fa_inputs.WORKLOADS, or backward:<prefill workload>; prints a short JSON line "
+                         "instead of the bench line")
     return ap.parse_args()
 
 
@@ -131,9 +135,25 @@ def run_only(part, steps, warmup):
     import exact_attention_111_amd as fa
     import fa_inputs
     dev = torch.device("cuda:0")
-    name = {"prefill": PREFILL, "decode": DECODE}.get(part, part)
+    name = {"prefill": PREFILL, "decode": DECODE, "backward": "backward:" + PREFILL}.get(part, part)
     rate = None
-    if name == "copy":  # a plain copy of 1 GiB: reads 1 GiB and writes 1 GiB per launch
+    if name.startswith("backward:") and name[len("backward:"):] in fa_inputs.WORKLOADS:
+        w = fa_inputs.WORKLOADS[name[len("backward:"):]]
+        if w.kind != "prefill" or w.io != "bf16":
+            raise SystemExit(f"no backward for {w.name}")
+        x = fa_inputs.workload_inputs(w, device=dev)
+        sl = x.get("seqlens")
+        o, lse = fa.fwd(x["q"], x["k"], x["v"], causal=w.causal, scale=w.scale, seqlens=sl)
+        g = torch.Generator(device=dev).manual_seed(w.seed + 1000)
+        do = torch.randn(o.shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        ws = torch.empty(max(16, fa.bwd_workspace_bytes(w.B, w.H, w.L)), dtype=torch.uint8, device=dev)
+        dq, dk, dv = torch.empty_like(x["q"]), torch.empty_like(x["k"]), torch.empty_like(x["v"])
+        fn = lambda: fa.bwd(x["q"], x["k"], x["v"], o, do, lse, causal=w.causal, scale=w.scale,  # noqa: E731
+                            seqlens=sl, workspace=ws, dq=dq, dk=dk, dv=dv)
+        lens = x["seqlens_cpu"].to(torch.float64) if sl is not None else torch.full((w.B,), float(w.L))
+        pairs = float((lens * lens).sum()) * (0.5 if w.causal else 1.0)
+        rate = (BWD_FLOP_PER_FWD * 4.0 * w.H * w.d * pairs, "TFLOP/s")
+    elif name == "copy":  # a plain copy of 1 GiB: reads 1 GiB and writes 1 GiB per launch
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         fn = lambda: dst.copy_(src)  # noqa: E731

@@ -114,7 +114,7 @@ fa_status fa_decode(const void* q, const void* k_cache, const void* v_cache, voi
 
 size_t fa_bwd_workspace_bytes(int B, int H, int Lq) {
   if (B < 0 || H < 0 || Lq < 0) return 0;
-  return (size_t)B * H * Lq * sizeof(float);  // D = rowsum(dO * O) per query row
+  return (size_t)B * H * Lq * 2 * sizeof(float);  // (exp2 offset of the LSE, D = rowsum(dO * O)) per row
 }
 
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,

@@ -10,19 +10,24 @@
 // and P is recomputed as exp2(s * scale*log2(e) - LSE*log2(e)) from the natural-log LSE.
 //
 // gfx950 mapping (all products are v_mfma_f32_32x32x16_bf16 with fp32 accumulation):
-//   * bwd_dot: D per query row (0 on padding rows); d / 8 lanes per row.
-//   * bwd_dkdv: one workgroup per (batch, KV head, 128 keys): 4 waves x 32 keys. A wave
-//     keeps its keys' K and V rows in registers as B operands. Blocks of 32 query rows of
-//     every query head of the group go through LDS, each tile stored twice (swizzled for
-//     128-bit row reads and for transposed reads). Per block: S = Q K^T and dP = dO V^T
-//     (row reads; the accumulators hold one key column per lane), P and dS from them, then
-//     dV^T += dO^T P and dK^T += Q^T dS (transposed reads; P and dS go from the
-//     accumulators straight into B operands).
-//   * bwd_dq: one workgroup per (batch, head, 128 query rows): 4 waves x 32 rows with their
-//     Q and dO rows in registers; 64-key K/V tiles go through LDS. S^T = K Q^T and
-//     dP^T = V dO^T leave one query column per lane, then dQ^T += K^T dS^T.
-//   Rows and keys outside the sequence are loaded as zeros and masked entries get P = 0 and
-//   dP = 0, so dS is exactly 0 there: nothing outside the sequence is read or contributes.
+//   * bwd_dot: per query row, the exp2 offset LSE*log2(e) and D, as one (offset, D) pair
+//     (+inf and 0 on padding rows); d / 8 lanes per row.
+//   * bwd_dkdv: one workgroup per (batch, KV head, 128 keys): 4 waves x 32 keys, whose K
+//     and V rows stay in registers as B operands. Steps of 64 query rows of every query head
+//     of the group stream through a ring of LDS stages (Q tile, dO tile, the rows' pairs),
+//     filled by direct buffer-to-LDS loads issued three steps ahead. Per step: S = Q K^T and
+//     dP = dO V^T (row reads; the accumulators hold one key column per lane), P and dS, then
+//     dV^T += dO^T P and dK^T += Q^T dS (transposed reads; P and dS go from the accumulators
+//     straight into B operands).
+//   * bwd_dq: one workgroup per (batch, head, 256 query rows): 4 waves x 64 rows, with their
+//     Q and dO rows in registers. 32-key K/V tiles stream through a ring of LDS stages loaded
+//     five steps ahead. S^T = K Q^T and dP^T = V dO^T leave one query column per lane, then
+//     dQ^T += K^T dS^T; every K/V operand read from LDS serves both 32-row halves of a wave.
+//   Each tile sits in LDS once, in a layout (kv_xor) that serves both its row and its
+//   transposed reads without bank conflicts. Rows past the sequence are not read: their LDS
+//   rows keep earlier input rows or the zeros the kernels start from, and the mask gives
+//   them P = 0 and dP = 0, so dS is exactly 0 there and nothing outside a sequence counts.
+//   A wave skips the steps whose rows and keys it cannot see under the causal mask.
 #include "fa_device.h"
 #include "fa_launch.h"
 #include "fa_tiles.h"
@@ -35,16 +40,29 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 template <int D>
 struct BwdCfg {
-  static constexpr int NW = 4;                // waves per workgroup
+  static constexpr int NW = 4;        // waves per workgroup
   static constexpr int NT = 64 * NW;
-  static constexpr int ROWB = 2 * D;          // bytes per row
-  static constexpr int CH = D / 8;            // 16-byte chunks per row
-  static constexpr int QKS = D / 16;          // 32x32x16 k-steps over d
-  static constexpr int NB = D / 32;           // 32-row blocks over d
-  static constexpr int KEYS = 32 * NW;        // keys per dK/dV workgroup
-  static constexpr int QROWS = 32 * NW;       // query rows per dQ workgroup
-  static constexpr int QBLK = 32;             // query rows per dK/dV step
-  static constexpr int KT = 64;               // keys per dQ step
+  static constexpr int ROWB = 2 * D;  // bytes per row
+  static constexpr int QKS = D / 16;  // 32x32x16 k-steps over d
+  static constexpr int NB = D / 32;   // 32-wide blocks over d
+  // dK/dV: 32 keys per wave, 64 query rows per step.
+  static constexpr int KEYS = 32 * NW;
+  static constexpr int QSTEP = 64;
+  static constexpr int QTILE = QSTEP * ROWB;              // bytes of a Q or dO tile
+  static constexpr int KV_STAGE = 2 * QTILE + QSTEP * 8;  // Q | dO | (offset, D) per row
+  static constexpr int KV_NS = 4;                         // stages in the ring
+  static constexpr int KV_SEGS = QTILE / 1024 / NW;       // 1 KB direct loads per wave and tile
+  static constexpr int KV_LOADS = 2 * KV_SEGS + 1;        // direct loads per wave and stage
+  // dQ: 64 query rows per wave, 32 keys per step.
+  static constexpr int WROWS = 64;
+  static constexpr int QROWS = WROWS * NW;
+  static constexpr int KSTEP = 32;
+  static constexpr int KTILE = KSTEP * ROWB;  // bytes of a K or V tile
+  static constexpr int Q_STAGE = 2 * KTILE;   // K | V
+  static constexpr int Q_NS = 6;
+  static constexpr int Q_SEGS = KTILE / 1024 / NW;
+  static constexpr int Q_LOADS = 2 * Q_SEGS;
+  static_assert(KV_SEGS >= 1 && Q_SEGS >= 1, "tile smaller than one load per wave");
 };
 
 struct BwdArgs {
@@ -57,7 +75,7 @@ struct BwdArgs {
   __bf16* dq;
   __bf16* dk;
   __bf16* dv;
-  float* ws_d;
+  float* ws;  // [B, H, Lq] x (offset, D)
   int B, H, Hkv, Lq, Lk;
   int group;
   float scale, scale_log2;
@@ -76,24 +94,31 @@ __device__ __forceinline__ void seq_extent(const BwdArgs& a, int b, int& n_q, in
   }
 }
 
-// rows [row0, row0 + NR) of a row-major [*, D] bf16 matrix (zero past n_valid) into an
-// LDS tile, chunks of row r permuted by `swz`; one or two destination layouts.
-template <int D, int NR>
-__device__ __forceinline__ void stage_rows(char* dst_k, char* dst_v, const __bf16* src, int row0, int n_valid,
-                                           int tid) {
-  using C = BwdCfg<D>;
+// Zero a workgroup's LDS buffer (so rows that are never loaded hold finite values).
+template <int BYTES, int NT>
+__device__ __forceinline__ void zero_lds(char* smem, int tid) {
+  static_assert(BYTES % 16 == 0, "16-byte stores");
+#pragma unroll 4
+  for (int i = tid; i < BYTES / 16; i += NT) reinterpret_cast<u32x4*>(smem)[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
+// Byte offsets, relative to a tile's first row, that direct-load segment i of wave w reads
+// so that LDS byte (w * SEGS + i) * 1024 + 16 * lane receives row r's logical chunk
+// (physical chunk ^ kv_xor(r)).
+template <int D, int SEGS>
+__device__ __forceinline__ void tile_load_offsets(unsigned (&off)[SEGS], int w, int lane) {
+  constexpr int ROWB = 2 * D;
 #pragma unroll
-  for (int i = tid; i < NR * C::CH; i += C::NT) {
-    const int r = i / C::CH, c = i - r * C::CH;
-    u32x4 u = {0u, 0u, 0u, 0u};
-    if (row0 + r < n_valid) u = *reinterpret_cast<const u32x4*>(src + (size_t)(row0 + r) * D + 8 * c);
-    if (dst_k != nullptr) *reinterpret_cast<u32x4*>(dst_k + r * C::ROWB + ((c ^ k_xor<D>(r)) << 4)) = u;
-    if (dst_v != nullptr) *reinterpret_cast<u32x4*>(dst_v + r * C::ROWB + ((c ^ v_xor<D>(r)) << 4)) = u;
+  for (int i = 0; i < SEGS; ++i) {
+    const int byte = (w * SEGS + i) * 1024 + lane * 16;
+    const int r = byte / ROWB;
+    const int cp = (byte - r * ROWB) >> 4;
+    off[i] = (unsigned)(r * ROWB + ((cp ^ kv_xor<D>(r)) << 4));
   }
 }
 
-// Per-lane operand addresses inside a tile. Row reads: lane (col, half) reads row
-// 32 * blk + col, logical chunk 2 ks + half (the A operand of a 32x32x16 product over d).
+// Per-lane operand addresses inside a kv_xor tile. Row reads: lane (col, half) reads row
+// 32 blk + col, logical chunk 2 ks + half (the A operand of a 32x32x16 product over d).
 // Transposed reads: lane (g, sl) = (lane / 16, lane % 16) reads rows 16 ks + 4 (g / 2) +
 // sl / 4 (+ 8), dims 32 nb + 16 (g % 2) + 4 (sl % 4): output lane l then holds dim
 // 32 nb + l % 32 and rows 16 ks + 8 (t / 4) + 4 (l / 32) + t % 4, t = 0..7, the order of
@@ -101,18 +126,21 @@ __device__ __forceinline__ void stage_rows(char* dst_k, char* dst_v, const __bf1
 template <int D>
 struct TileAddr {
   int row[BwdCfg<D>::QKS];
-  int tr[BwdCfg<D>::NB];
+  int tr[2][BwdCfg<D>::NB];
   __device__ __forceinline__ void init(int lane) {
     using C = BwdCfg<D>;
     const int col = lane & 31, half = lane >> 5;
 #pragma unroll
-    for (int ks = 0; ks < C::QKS; ++ks) row[ks] = col * C::ROWB + (((2 * ks + half) ^ k_xor<D>(col)) << 4);
+    for (int ks = 0; ks < C::QKS; ++ks) row[ks] = col * C::ROWB + (((2 * ks + half) ^ kv_xor<D>(col)) << 4);
     const int g = lane >> 4, sl = lane & 15;
-    const int vrow = 4 * (g >> 1) + (sl >> 2);
 #pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb) {
-      const int dim = 32 * nb + 16 * (g & 1) + 4 * (sl & 3);
-      tr[nb] = vrow * C::ROWB + (((dim >> 3) ^ v_xor<D>(vrow)) << 4) + ((dim & 4) << 1);
+    for (int h = 0; h < 2; ++h) {
+      const int vrow = 4 * (g >> 1) + (sl >> 2) + 8 * h;
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb) {
+        const int dim = 32 * nb + 16 * (g & 1) + 4 * (sl & 3);
+        tr[h][nb] = vrow * C::ROWB + (((dim >> 3) ^ kv_xor<D>(vrow)) << 4) + ((dim & 4) << 1);
+      }
     }
   }
   __device__ __forceinline__ bf16x8 read_row(const char* tile, int blk, int ks) const {
@@ -120,17 +148,15 @@ struct TileAddr {
   }
   __device__ __forceinline__ bf16x8 read_tr(const char* tile, int ks, int nb) const {
     constexpr int RB = BwdCfg<D>::ROWB;
-    const s16x4 p0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + tr[nb] + 16 * ks * RB));
-    const s16x4 p1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + tr[nb] + (16 * ks + 8) * RB));
+    const s16x4 p0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + tr[0][nb] + 16 * ks * RB));
+    const s16x4 p1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + tr[1][nb] + 16 * ks * RB));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(p0, p1, 0, 1, 2, 3, 4, 5, 6, 7));
   }
 };
 
-// exp2 offset of a query row: LSE * log2(e), or +inf for a row that sees nothing (P = 0).
-__device__ __forceinline__ float row_offset(float lse) { return lse == kNegInf ? __builtin_inff() : lse * kLog2e; }
-
 // ---------------------------------------------------------------------------------------
-// D_i = sum_c dO_ic O_ic for every query row (0 on padding rows).
+// Per query row: exp2 offset LSE * log2(e) (+inf for a row that sees nothing, so P = 0)
+// and D = sum_c dO_ic O_ic; (+inf, 0) on padding rows.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_dot_kernel(const BwdArgs a) {
   constexpr int LPR = D / 8;  // lanes per row, 8 elements each
@@ -153,7 +179,12 @@ __global__ __launch_bounds__(256) void bwd_dot_kernel(const BwdArgs a) {
     const int i = (int)(row % a.Lq);
     int n_q, n_kv;
     seq_extent(a, b, n_q, n_kv);
-    a.ws_d[row] = i < n_q ? s : 0.f;
+    float2 out = make_float2(__builtin_inff(), 0.f);
+    if (i < n_q) {
+      const float lse = a.lse[row];
+      out = make_float2(lse == kNegInf ? __builtin_inff() : lse * kLog2e, s);
+    }
+    reinterpret_cast<float2*>(a.ws)[row] = out;
   }
 }
 
@@ -163,13 +194,7 @@ __global__ __launch_bounds__(BwdCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(1
 void bwd_dkdv_kernel(const BwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using C = BwdCfg<D>;
-  constexpr int QT = C::QBLK * C::ROWB;  // bytes of one 32-row tile
-  __shared__ __attribute__((aligned(1024))) char smem[4 * QT];  // Q rows | Q transposed | dO rows | dO transposed
-  __shared__ __attribute__((aligned(16))) float rowv[2][C::QBLK];  // exp2 offset, D
-  char* const q_row = smem;
-  char* const q_tr = smem + QT;
-  char* const d_row = smem + 2 * QT;
-  char* const d_tr = smem + 3 * QT;
+  __shared__ __attribute__((aligned(1024))) char smem[C::KV_NS * C::KV_STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -186,6 +211,8 @@ void bwd_dkdv_kernel(const BwdArgs a) {
   const int k0 = kbi * C::KEYS;
   const int kw0 = k0 + 32 * w;  // this wave's first key
   const int my_key = kw0 + col;
+
+  zero_lds<C::KV_NS * C::KV_STAGE, C::NT>(smem, tid);
 
   const size_t kv_off = (size_t)(b * a.Hkv + kvh) * a.Lk * D;
   bf16x8 kf[C::QKS], vf[C::QKS];
@@ -207,64 +234,116 @@ void bwd_dkdv_kernel(const BwdArgs a) {
 
   TileAddr<D> ta;
   ta.init(lane);
-  // The first query row that sees key k0 (bottom-right causal alignment: j <= i + delta).
+  unsigned toff[C::KV_SEGS];
+  tile_load_offsets<D, C::KV_SEGS>(toff, w, lane);
+
+  // Steps: (query head of the group, 64-row block) pairs, head-major. The first row that
+  // sees key k0 is k0 - delta (bottom-right causal alignment: j <= i + delta).
   const int q_first = (k0 < n_kv) ? (a.causal ? max(0, k0 - delta) : 0) : n_q;
-  const int qb_first = q_first / C::QBLK;
-  const int nqb = (n_q + C::QBLK - 1) / C::QBLK;
+  const int qs_first = q_first / C::QSTEP;
+  const int nqs = (n_q + C::QSTEP - 1) / C::QSTEP;
+  const int per_head = max(nqs - qs_first, 0);
+  const int T = a.group * per_head;
 
-  for (int hq = kvh * a.group; hq < (kvh + 1) * a.group; ++hq) {
-    const size_t q_off = (size_t)(b * a.H + hq) * a.Lq;
-    for (int qb = qb_first; qb < nqb; ++qb) {
-      const int q0 = qb * C::QBLK;
-      __syncthreads();  // the previous block's reads are done
-      stage_rows<D, C::QBLK>(q_row, q_tr, a.q + q_off * D, q0, n_q, tid);
-      stage_rows<D, C::QBLK>(d_row, d_tr, a.dout + q_off * D, q0, n_q, tid);
-      if (tid < C::QBLK) {
-        const int i = q0 + tid;
-        rowv[0][tid] = i < n_q ? row_offset(a.lse[q_off + i]) : __builtin_inff();
-        rowv[1][tid] = i < n_q ? a.ws_d[q_off + i] : 0.f;
-      }
-      __syncthreads();
+  // Stage the next step (ihq, iqs) into ring slot `slot`: the Q and dO tiles through
+  // buffer resources that end at row n_q (rows past it read nothing), and the rows'
+  // (offset, D) pairs, 16 rows per wave from lanes 0..7.
+  const char* const qsrc = reinterpret_cast<const char*>(a.q);
+  const char* const dsrc = reinterpret_cast<const char*>(a.dout);
+  const char* const wsrc = reinterpret_cast<const char*>(a.ws);
+  int ihq = kvh * a.group, iqs = qs_first;
+  auto issue = [&](int slot) {
+    const int q0 = iqs * C::QSTEP;
+    const size_t row0 = (size_t)(b * a.H + ihq) * a.Lq + q0;
+    const unsigned nrows = (unsigned)max(n_q - q0, 0);
+    char* st = smem + slot * C::KV_STAGE;
+    const u32x4 rq = raw_buffer_rsrc(qsrc + row0 * C::ROWB, nrows * C::ROWB);
+    const u32x4 rd = raw_buffer_rsrc(dsrc + row0 * C::ROWB, nrows * C::ROWB);
+#pragma unroll
+    for (int i = 0; i < C::KV_SEGS; ++i) lds_dma16_buf(rq, toff[i], lds_addr(st + (w * C::KV_SEGS + i) * 1024));
+#pragma unroll
+    for (int i = 0; i < C::KV_SEGS; ++i)
+      lds_dma16_buf(rd, toff[i], lds_addr(st + C::QTILE + (w * C::KV_SEGS + i) * 1024));
+    const u32x4 rr = raw_buffer_rsrc(wsrc + row0 * 8, nrows * 8);
+    if (lane < 8) lds_dma16_buf(rr, (unsigned)(128 * w + 16 * lane), lds_addr(st + 2 * C::QTILE + 128 * w));
+    if (++iqs == nqs) {
+      iqs = qs_first;
+      ++ihq;
+    }
+  };
 
-      f32x16 s = {}, dp = {};
+  __syncthreads();  // the zero fill is done before any direct load lands
+#pragma unroll
+  for (int t = 0; t < C::KV_NS - 1; ++t)
+    if (t < T) issue(t);
+
+  int qs = qs_first;  // block of the step being computed
+  for (int t = 0; t < T; ++t) {
+    // Step t's loads are done when at most the later staged steps' loads are outstanding.
+    if (t + C::KV_NS - 1 <= T) wait_vmcnt<(C::KV_NS - 2) * C::KV_LOADS>();
+    else wait_vmcnt<0>();
+    lds_barrier();  // every wave's loads of step t landed; step t - 1's reads are done
+    if (t + C::KV_NS - 1 < T) issue((t + C::KV_NS - 1) % C::KV_NS);
+
+    const int q0 = qs * C::QSTEP;
+    if (++qs == nqs) qs = qs_first;
+    const bool skip = kw0 >= n_kv || (a.causal && kw0 > q0 + C::QSTEP - 1 + delta);
+    if (skip) continue;
+    const char* qt = smem + (t % C::KV_NS) * C::KV_STAGE;
+    const char* dt = qt + C::QTILE;
+    const float* rv = reinterpret_cast<const float*>(qt + 2 * C::QTILE);
+
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      s[rb] = f32x16{};
+      dp[rb] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < C::QKS; ++ks) {
-        s = mfma_32x32x16(ta.read_row(q_row, 0, ks), kf[ks], s);
-        dp = mfma_32x32x16(ta.read_row(d_row, 0, ks), vf[ks], dp);
+        s[rb] = mfma_32x32x16(ta.read_row(qt, rb, ks), kf[ks], s[rb]);
+        dp[rb] = mfma_32x32x16(ta.read_row(dt, rb, ks), vf[ks], dp[rb]);
       }
-      // Accumulator element r: query row q0 + 8 (r / 4) + 4 half + r % 4, key my_key.
-      const bool need_mask = (q0 + C::QBLK > n_q) || (kw0 + 32 > n_kv) || (a.causal && kw0 + 31 > q0 + delta);
-      if (need_mask) {
+    }
+    // Element r of block rb: query row q0 + 32 rb + 8 (r / 4) + 4 half + r % 4, key my_key.
+    const bool need_mask =
+        (q0 + C::QSTEP > n_q) || (kw0 + 32 > n_kv) || (a.causal && kw0 + 31 > q0 + delta);
+    if (need_mask) {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int i = q0 + 8 * (r >> 2) + 4 * half + (r & 3);
+          const int i = q0 + 32 * rb + 8 * (r >> 2) + 4 * half + (r & 3);
           const bool vis = i < n_q && my_key < n_kv && (!a.causal || my_key <= i + delta);
-          s[r] = vis ? s[r] : kNegInf;
-          dp[r] = vis ? dp[r] : 0.f;
-        }
-      }
-      bf16x8 pb[2], dsb[2];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const f32x4 off = *reinterpret_cast<const f32x4*>(&rowv[0][8 * m + 4 * half]);
-        const f32x4 dd = *reinterpret_cast<const f32x4*>(&rowv[1][8 * m + 4 * half]);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int r = 4 * m + t;
-          const float p = exp2_hw(fmaf(s[r], a.scale_log2, -off[t]));
-          const float ds = p * (dp[r] - dd[t]);
-          pb[r >> 3][r & 7] = (__bf16)p;
-          dsb[r >> 3][r & 7] = (__bf16)ds;
-        }
-      }
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb) {
-          dva[nb] = mfma_32x32x16(ta.read_tr(d_tr, kk, nb), pb[kk], dva[nb]);
-          dka[nb] = mfma_32x32x16(ta.read_tr(q_tr, kk, nb), dsb[kk], dka[nb]);
+          s[rb][r] = vis ? s[rb][r] : kNegInf;
+          dp[rb][r] = vis ? dp[rb][r] : 0.f;
         }
     }
+    bf16x8 pb[4], dsb[4];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const float* pr = rv + 2 * (32 * rb + 8 * m + 4 * half);  // (offset, D) of 4 rows
+        const f32x4 lo = *reinterpret_cast<const f32x4*>(pr);
+        const f32x4 hi = *reinterpret_cast<const f32x4*>(pr + 4);
+        const float off[4] = {lo[0], lo[2], hi[0], hi[2]};
+        const float dd[4] = {lo[1], lo[3], hi[1], hi[3]};
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4) {
+          const int r = 4 * m + t4;
+          const float p = exp2_hw(fmaf(s[rb][r], a.scale_log2, -off[t4]));
+          const float ds = p * (dp[rb][r] - dd[t4]);
+          pb[2 * rb + (r >> 3)][r & 7] = (__bf16)p;
+          dsb[2 * rb + (r >> 3)][r & 7] = (__bf16)ds;
+        }
+      }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb) {
+        dva[nb] = mfma_32x32x16(ta.read_tr(dt, kk, nb), pb[kk], dva[nb]);
+        dka[nb] = mfma_32x32x16(ta.read_tr(qt, kk, nb), dsb[kk], dka[nb]);
+      }
   }
 
   // dK = scale * dK^T-accumulator, dV: lane holds key my_key, dims 32 nb + 8 (r / 4) +
@@ -291,11 +370,7 @@ __global__ __launch_bounds__(BwdCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(1
 void bwd_dq_kernel(const BwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using C = BwdCfg<D>;
-  constexpr int KTB = C::KT * C::ROWB;  // bytes of one 64-row tile
-  __shared__ __attribute__((aligned(1024))) char smem[3 * KTB];  // K rows | K transposed | V rows
-  char* const k_row = smem;
-  char* const k_tr = smem + KTB;
-  char* const v_row = smem + 2 * KTB;
+  __shared__ __attribute__((aligned(1024))) char smem[C::Q_NS * C::Q_STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -312,32 +387,45 @@ void bwd_dq_kernel(const BwdArgs a) {
   seq_extent(a, b, n_q, n_kv);
   const int delta = a.Lk - a.Lq;
   const int q0 = qt * C::QROWS;
-  const int qw0 = q0 + 32 * w;
-  const int my_q = qw0 + col;
+  const int qw0 = q0 + C::WROWS * w;  // this wave's first row
   const size_t q_off = (size_t)(b * a.H + h) * a.Lq;
-  const size_t kv_off = (size_t)(b * a.Hkv + kvh) * a.Lk * D;
+  const size_t kv_row0 = (size_t)(b * a.Hkv + kvh) * a.Lk;
 
-  bf16x8 qf[C::QKS], dof[C::QKS];
+  zero_lds<C::Q_NS * C::Q_STAGE, C::NT>(smem, tid);
+
+  bf16x8 qf[2][C::QKS], dof[2][C::QKS];
+  float off[2], dd[2];
 #pragma unroll
-  for (int ks = 0; ks < C::QKS; ++ks) {
-    u32x4 uq = {0u, 0u, 0u, 0u}, ud = {0u, 0u, 0u, 0u};
-    if (my_q < n_q) {
-      uq = *reinterpret_cast<const u32x4*>(a.q + (q_off + my_q) * D + 16 * ks + 8 * half);
-      ud = *reinterpret_cast<const u32x4*>(a.dout + (q_off + my_q) * D + 16 * ks + 8 * half);
+  for (int qb = 0; qb < 2; ++qb) {
+    const int my_q = qw0 + 32 * qb + col;
+#pragma unroll
+    for (int ks = 0; ks < C::QKS; ++ks) {
+      u32x4 uq = {0u, 0u, 0u, 0u}, ud = {0u, 0u, 0u, 0u};
+      if (my_q < n_q) {
+        uq = *reinterpret_cast<const u32x4*>(a.q + (q_off + my_q) * D + 16 * ks + 8 * half);
+        ud = *reinterpret_cast<const u32x4*>(a.dout + (q_off + my_q) * D + 16 * ks + 8 * half);
+      }
+      qf[qb][ks] = as_bf16x8(uq);
+      dof[qb][ks] = as_bf16x8(ud);
     }
-    qf[ks] = as_bf16x8(uq);
-    dof[ks] = as_bf16x8(ud);
+    float2 od = make_float2(__builtin_inff(), 0.f);
+    if (my_q < n_q) od = reinterpret_cast<const float2*>(a.ws)[q_off + my_q];
+    off[qb] = od.x;
+    dd[qb] = od.y;
   }
-  const float off = my_q < n_q ? row_offset(a.lse[q_off + my_q]) : __builtin_inff();
-  const float dd = my_q < n_q ? a.ws_d[q_off + my_q] : 0.f;
-  f32x16 dqa[C::NB];
+  f32x16 dqa[2][C::NB];
 #pragma unroll
-  for (int nb = 0; nb < C::NB; ++nb)
+  for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) dqa[nb][r] = 0.f;
+    for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dqa[qb][nb][r] = 0.f;
 
   TileAddr<D> ta;
   ta.init(lane);
+  unsigned toff[C::Q_SEGS];
+  tile_load_offsets<D, C::Q_SEGS>(toff, w, lane);
+
   // Keys any row of this block can see: [0, kv_end).
   int kv_end = 0;
   if (q0 < n_q) {
@@ -345,64 +433,105 @@ void bwd_dq_kernel(const BwdArgs a) {
     if (a.causal) kv_end = min(kv_end, min(q0 + C::QROWS, n_q) + delta);
     kv_end = max(kv_end, 0);
   }
-  const int ntk = (kv_end + C::KT - 1) / C::KT;
-  for (int t = 0; t < ntk; ++t) {
-    const int k0 = t * C::KT;
-    __syncthreads();  // the previous tile's reads are done
-    stage_rows<D, C::KT>(k_row, k_tr, a.k + kv_off, k0, kv_end, tid);
-    stage_rows<D, C::KT>(v_row, nullptr, a.v + kv_off, k0, kv_end, tid);
-    __syncthreads();
+  kv_end = __builtin_amdgcn_readfirstlane(kv_end);
+  const int T = (kv_end + C::KSTEP - 1) / C::KSTEP;
 
-    // S^T and dP^T for the two 32-key halves: element r of half kb is key
-    // k0 + 32 kb + 8 (r / 4) + 4 half + r % 4, query my_q.
-    f32x16 sx[2], dpx[2];
+  // Stage key tile t into ring slot t % Q_NS through buffer resources that end at key
+  // kv_end (keys past it read nothing).
+  const char* const ksrc = reinterpret_cast<const char*>(a.k) + kv_row0 * C::ROWB;
+  const char* const vsrc = reinterpret_cast<const char*>(a.v) + kv_row0 * C::ROWB;
+  auto issue = [&](int t) {
+    const int k0 = t * C::KSTEP;
+    const unsigned nrows = (unsigned)max(kv_end - k0, 0);
+    char* st = smem + (t % C::Q_NS) * C::Q_STAGE;
+    const u32x4 rk = raw_buffer_rsrc(ksrc + (size_t)k0 * C::ROWB, nrows * C::ROWB);
+    const u32x4 rv = raw_buffer_rsrc(vsrc + (size_t)k0 * C::ROWB, nrows * C::ROWB);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      sx[kb] = f32x16{};
-      dpx[kb] = f32x16{};
+    for (int i = 0; i < C::Q_SEGS; ++i) lds_dma16_buf(rk, toff[i], lds_addr(st + (w * C::Q_SEGS + i) * 1024));
 #pragma unroll
-      for (int ks = 0; ks < C::QKS; ++ks) {
-        sx[kb] = mfma_32x32x16(ta.read_row(k_row, kb, ks), qf[ks], sx[kb]);
-        dpx[kb] = mfma_32x32x16(ta.read_row(v_row, kb, ks), dof[ks], dpx[kb]);
+    for (int i = 0; i < C::Q_SEGS; ++i)
+      lds_dma16_buf(rv, toff[i], lds_addr(st + C::KTILE + (w * C::Q_SEGS + i) * 1024));
+  };
+
+  __syncthreads();  // the zero fill is done before any direct load lands
+#pragma unroll
+  for (int t = 0; t < C::Q_NS - 1; ++t)
+    if (t < T) issue(t);
+
+  for (int t = 0; t < T; ++t) {
+    if (t + C::Q_NS - 1 <= T) wait_vmcnt<(C::Q_NS - 2) * C::Q_LOADS>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+    if (t + C::Q_NS - 1 < T) issue(t + C::Q_NS - 1);
+
+    const int k0 = t * C::KSTEP;
+    const bool skip = qw0 >= n_q || (a.causal && k0 > qw0 + C::WROWS - 1 + delta);
+    if (skip) continue;
+    const char* kt = smem + (t % C::Q_NS) * C::Q_STAGE;
+    const char* vt = kt + C::KTILE;
+
+    // S^T and dP^T of both row blocks: element r is key k0 + 8 (r / 4) + 4 half + r % 4,
+    // query qw0 + 32 qb + col.
+    f32x16 sx[2] = {f32x16{}, f32x16{}}, dpx[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int ks = 0; ks < C::QKS; ++ks) {
+      const bf16x8 ka = ta.read_row(kt, 0, ks);
+      const bf16x8 va = ta.read_row(vt, 0, ks);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        sx[qb] = mfma_32x32x16(ka, qf[qb][ks], sx[qb]);
+        dpx[qb] = mfma_32x32x16(va, dof[qb][ks], dpx[qb]);
       }
     }
-    const bool need_mask = (k0 + C::KT > n_kv) || (qw0 + 32 > n_q) || (a.causal && k0 + C::KT - 1 > qw0 + delta);
+    const bool need_mask =
+        (k0 + C::KSTEP > n_kv) || (qw0 + C::WROWS > n_q) || (a.causal && k0 + C::KSTEP - 1 > qw0 + delta);
     if (need_mask) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int qb = 0; qb < 2; ++qb) {
+        const int my_q = qw0 + 32 * qb + col;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int j = k0 + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
+          const int j = k0 + 8 * (r >> 2) + 4 * half + (r & 3);
           const bool vis = my_q < n_q && j < n_kv && (!a.causal || j <= my_q + delta);
-          sx[kb][r] = vis ? sx[kb][r] : kNegInf;
-          dpx[kb][r] = vis ? dpx[kb][r] : 0.f;
+          sx[qb][r] = vis ? sx[qb][r] : kNegInf;
+          dpx[qb][r] = vis ? dpx[qb][r] : 0.f;
         }
+      }
     }
-    bf16x8 dsb[4];
+    bf16x8 dsb[2][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = exp2_hw(fmaf(sx[kb][r], a.scale_log2, -off));
-        dsb[2 * kb + (r >> 3)][r & 7] = (__bf16)(p * (dpx[kb][r] - dd));
+        const float p = exp2_hw(fmaf(sx[qb][r], a.scale_log2, -off[qb]));
+        dsb[qb][r >> 3][r & 7] = (__bf16)(p * (dpx[qb][r] - dd[qb]));
       }
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb) dqa[nb] = mfma_32x32x16(ta.read_tr(k_tr, ks, nb), dsb[ks], dqa[nb]);
+      for (int nb = 0; nb < C::NB; ++nb) {
+        const bf16x8 kta = ta.read_tr(kt, ks, nb);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) dqa[qb][nb] = mfma_32x32x16(kta, dsb[qb][ks], dqa[qb][nb]);
+      }
   }
 
-  // dQ = scale * accumulator: lane holds query my_q, dims 32 nb + 8 jj + 4 half + (0..3).
-  if (my_q < a.Lq) {
-    __bf16* dqp = a.dq + (q_off + my_q) * D;
+  // dQ = scale * accumulator: lane holds query qw0 + 32 qb + col, dims 32 nb + 8 jj +
+  // 4 half + (0..3).
 #pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb)
+  for (int qb = 0; qb < 2; ++qb) {
+    const int my_q = qw0 + 32 * qb + col;
+    if (my_q < a.Lq) {
+      __bf16* dqp = a.dq + (q_off + my_q) * D;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int d0 = 32 * nb + 8 * jj + 4 * half;
-        Store4<__bf16>::store(dqp + d0, dqa[nb][4 * jj] * a.scale, dqa[nb][4 * jj + 1] * a.scale,
-                              dqa[nb][4 * jj + 2] * a.scale, dqa[nb][4 * jj + 3] * a.scale);
-      }
+      for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int d0 = 32 * nb + 8 * jj + 4 * half;
+          Store4<__bf16>::store(dqp + d0, dqa[qb][nb][4 * jj] * a.scale, dqa[qb][nb][4 * jj + 1] * a.scale,
+                                dqa[qb][nb][4 * jj + 2] * a.scale, dqa[qb][nb][4 * jj + 3] * a.scale);
+        }
+    }
   }
 #endif
 }
@@ -420,7 +549,7 @@ hipError_t launch_b(const BwdParams& p, hipStream_t stream) {
   a.dq = static_cast<__bf16*>(p.dq);
   a.dk = static_cast<__bf16*>(p.dk);
   a.dv = static_cast<__bf16*>(p.dv);
-  a.ws_d = p.ws_d;
+  a.ws = p.ws;
   a.B = p.B; a.H = p.H; a.Hkv = p.Hkv; a.Lq = p.Lq; a.Lk = p.Lk;
   a.group = p.H / p.Hkv;
   a.scale = p.scale;
@@ -433,6 +562,9 @@ hipError_t launch_b(const BwdParams& p, hipStream_t stream) {
   const long long nkv = (long long)p.B * p.Hkv * ((p.Lk + C::KEYS - 1) / C::KEYS);
   const long long nq = (long long)p.B * p.H * ((p.Lq + C::QROWS - 1) / C::QROWS);
   if (ndot > 0x7fffffffLL || nkv > 0x7fffffffLL || nq > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  // Buffer resources address a sequence's rows with 32-bit byte counts.
+  if ((long long)p.Lq * C::ROWB > 0x7fffffffLL || (long long)p.Lk * C::ROWB > 0x7fffffffLL)
+    return hipErrorInvalidConfiguration;
   hipError_t e = hipSuccess;
   if (ndot > 0) {
     e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dot_kernel<D>), dim3((unsigned)ndot), dim3(256), args, 0,

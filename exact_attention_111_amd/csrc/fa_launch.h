@@ -39,8 +39,8 @@ struct DecodeParams {
 inline int decode_num_chunks(int Lmax) { return (Lmax + kDecodeChunk - 1) / kDecodeChunk; }
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 
-// Backward (bf16): row dots D = rowsum(dO * O), then dK/dV per key block and dQ per query
-// block, both recomputing P from Q, K and the saved LSE.
+// Backward (bf16): per query row the exp2 offset of the saved LSE and D = rowsum(dO * O),
+// then dK/dV per key block and dQ per query block, both recomputing P from Q, K and the LSE.
 struct BwdParams {
   const void* q;
   const void* k;
@@ -55,7 +55,7 @@ struct BwdParams {
   float scale;
   int causal;
   const int32_t* seqlens;
-  float* ws_d;  // [B, H, Lq]
+  float* ws;  // [B, H, Lq] x (exp2 offset, D) per query row
 };
 hipError_t launch_bwd(const BwdParams& p, hipStream_t stream);
 

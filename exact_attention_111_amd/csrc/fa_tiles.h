@@ -19,4 +19,17 @@ __device__ __forceinline__ int v_xor(int r) {
   return D == 128 ? 2 * (j ^ ((j & 1) << 2)) : ((j & 2) << 1);
 }
 
+// kv_xor — one layout that serves both patterns, for tiles the backward reads both ways
+// (rows for products over d, transposed for products over rows):
+//   128-bit row reads: the 16 consecutive rows of a 16-lane group get 16 different values
+//   of the permutation (d = 128), or 8 different ones among the even and among the odd rows,
+//   which share a bank window two rows at a time (d = 64);
+//   transposed reads: 4 consecutive rows x 4 consecutive chunks per 32 lanes; the rows of
+//   such a group differ in bits 2..3 of the permutation (d = 128), or the two rows of the
+//   group that share a bank window differ in bit 2 (d = 64), so the 16 slots are distinct.
+template <int D>
+__device__ __forceinline__ int kv_xor(int r) {
+  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+
 }  // namespace fa

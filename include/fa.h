@@ -105,8 +105,9 @@ fa_status fa_decode(const void* q, const void* k_cache, const void* v_cache, voi
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * fa_bwd_workspace_bytes — bytes of device workspace fa_bwd needs: one fp32 per query row
- * (D = rowsum(dO * O)), i.e. B * H * Lq * 4. Returns 0 for invalid sizes.
+ * fa_bwd_workspace_bytes — bytes of device workspace fa_bwd needs: two fp32 per query row
+ * (the row's LSE in base 2 and D = rowsum(dO * O)), i.e. B * H * Lq * 8. Returns 0 for
+ * invalid sizes.
  */
 size_t fa_bwd_workspace_bytes(int B, int H, int Lq);
 

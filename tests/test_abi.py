@@ -110,7 +110,7 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
 
 def test_bwd_workspace_bytes():
     L = fa.lib()
-    assert L.fa_bwd_workspace_bytes(1, 32, 16384) == 32 * 16384 * 4
+    assert L.fa_bwd_workspace_bytes(1, 32, 16384) == 32 * 16384 * 8
     assert L.fa_bwd_workspace_bytes(2, 3, 0) == 0
     assert L.fa_bwd_workspace_bytes(-1, 3, 5) == 0
 
