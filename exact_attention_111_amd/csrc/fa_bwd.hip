@@ -27,7 +27,9 @@
 //   transposed reads without bank conflicts. Rows past the sequence are not read: their LDS
 //   rows keep earlier input rows or the zeros the kernels start from, and the mask gives
 //   them P = 0 and dP = 0, so dS is exactly 0 there and nothing outside a sequence counts.
-//   A wave skips the steps whose rows and keys it cannot see under the causal mask.
+//   Every wave computes every step of its workgroup, masked or not: the step's barrier holds
+//   a wave that skipped anyway, and a skip branch makes the compiler copy the loop-carried
+//   accumulators between register files on every step.
 #include "fa_device.h"
 #include "fa_launch.h"
 #include "fa_tiles.h"
@@ -38,6 +40,22 @@ namespace {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
+#ifndef FA_BWD_RB
+#define FA_BWD_RB 1
+#endif
+#ifndef FA_BWD_QB
+#define FA_BWD_QB 1
+#endif
+#ifndef FA_BWD_WPE
+#define FA_BWD_WPE 2
+#endif
+#ifndef FA_BWD_KVNS
+#define FA_BWD_KVNS 4
+#endif
+#ifndef FA_BWD_QNS
+#define FA_BWD_QNS 4
+#endif
+
 template <int D>
 struct BwdCfg {
   static constexpr int NW = 4;        // waves per workgroup
@@ -45,24 +63,28 @@ struct BwdCfg {
   static constexpr int ROWB = 2 * D;  // bytes per row
   static constexpr int QKS = D / 16;  // 32x32x16 k-steps over d
   static constexpr int NB = D / 32;   // 32-wide blocks over d
-  // dK/dV: 32 keys per wave, 64 query rows per step.
+  // dK/dV: 32 keys per wave, RB blocks of 32 query rows per step.
   static constexpr int KEYS = 32 * NW;
-  static constexpr int QSTEP = 64;
+  static constexpr int RB = FA_BWD_RB;
+  static constexpr int QSTEP = 32 * RB;
   static constexpr int QTILE = QSTEP * ROWB;              // bytes of a Q or dO tile
   static constexpr int KV_STAGE = 2 * QTILE + QSTEP * 8;  // Q | dO | (offset, D) per row
-  static constexpr int KV_NS = 4;                         // stages in the ring
+  static constexpr int KV_NS = FA_BWD_KVNS;               // stages in the ring
   static constexpr int KV_SEGS = QTILE / 1024 / NW;       // 1 KB direct loads per wave and tile
+  static constexpr int RV_LANES = QSTEP / NW / 2;         // lanes loading two rows' pairs each
   static constexpr int KV_LOADS = 2 * KV_SEGS + 1;        // direct loads per wave and stage
-  // dQ: 64 query rows per wave, 32 keys per step.
-  static constexpr int WROWS = 64;
+  // dQ: QB blocks of 32 query rows per wave, 32 keys per step.
+  static constexpr int QB = FA_BWD_QB;
+  static constexpr int WROWS = 32 * QB;
   static constexpr int QROWS = WROWS * NW;
   static constexpr int KSTEP = 32;
   static constexpr int KTILE = KSTEP * ROWB;  // bytes of a K or V tile
   static constexpr int Q_STAGE = 2 * KTILE;   // K | V
-  static constexpr int Q_NS = 6;
+  static constexpr int Q_NS = FA_BWD_QNS;
   static constexpr int Q_SEGS = KTILE / 1024 / NW;
   static constexpr int Q_LOADS = 2 * Q_SEGS;
   static_assert(KV_SEGS >= 1 && Q_SEGS >= 1, "tile smaller than one load per wave");
+  static_assert(RV_LANES >= 1 && RV_LANES * 2 * NW == QSTEP, "pair loads cover the step's rows");
 };
 
 struct BwdArgs {
@@ -126,30 +148,35 @@ __device__ __forceinline__ void tile_load_offsets(unsigned (&off)[SEGS], int w, 
 template <int D>
 struct TileAddr {
   int row[BwdCfg<D>::QKS];
-  int tr[2][BwdCfg<D>::NB];
+  int tr[BwdCfg<D>::NB];  // rows 16 ks + 4 (g / 2) + sl / 4
+  int tr_hi;              // + this for the same dims 8 rows further on
   __device__ __forceinline__ void init(int lane) {
     using C = BwdCfg<D>;
     const int col = lane & 31, half = lane >> 5;
 #pragma unroll
     for (int ks = 0; ks < C::QKS; ++ks) row[ks] = col * C::ROWB + (((2 * ks + half) ^ kv_xor<D>(col)) << 4);
     const int g = lane >> 4, sl = lane & 15;
+    const int vrow = 4 * (g >> 1) + (sl >> 2);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int vrow = 4 * (g >> 1) + (sl >> 2) + 8 * h;
-#pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb) {
-        const int dim = 32 * nb + 16 * (g & 1) + 4 * (sl & 3);
-        tr[h][nb] = vrow * C::ROWB + (((dim >> 3) ^ kv_xor<D>(vrow)) << 4) + ((dim & 4) << 1);
-      }
+    for (int nb = 0; nb < C::NB; ++nb) {
+      const int dim = 32 * nb + 16 * (g & 1) + 4 * (sl & 3);
+      tr[nb] = vrow * C::ROWB + (((dim >> 3) ^ kv_xor<D>(vrow)) << 4) + ((dim & 4) << 1);
     }
+    // kv_xor(vrow + 8) = kv_xor(vrow) ^ 2 (vrow < 8), so the chunk moves by +-2 the same
+    // way for every nb: its bit 1 is (g & 1) ^ bit 1 of kv_xor(vrow).
+    const int bit1 = ((g & 1) ^ (kv_xor<D>(vrow) >> 1)) & 1;
+    tr_hi = 8 * C::ROWB + (bit1 ? -32 : 32);
   }
   __device__ __forceinline__ bf16x8 read_row(const char* tile, int blk, int ks) const {
     return *reinterpret_cast<const bf16x8*>(tile + row[ks] + blk * 32 * BwdCfg<D>::ROWB);
   }
-  __device__ __forceinline__ bf16x8 read_tr(const char* tile, int ks, int nb) const {
+  // `hi`: tr_hi passed through the loop so that the sums are formed per step instead of
+  // being held in registers across it.
+  __device__ __forceinline__ bf16x8 read_tr(const char* tile, int ks, int nb, int hi) const {
     constexpr int RB = BwdCfg<D>::ROWB;
-    const s16x4 p0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + tr[0][nb] + 16 * ks * RB));
-    const s16x4 p1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + tr[1][nb] + 16 * ks * RB));
+    const char* p = tile + tr[nb] + 16 * ks * RB;
+    const s16x4 p0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+    const s16x4 p1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + hi));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(p0, p1, 0, 1, 2, 3, 4, 5, 6, 7));
   }
 };
@@ -190,7 +217,7 @@ __global__ __launch_bounds__(256) void bwd_dot_kernel(const BwdArgs a) {
 
 // ---------------------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(BwdCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(BwdCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(FA_BWD_WPE, FA_BWD_WPE)))
 void bwd_dkdv_kernel(const BwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using C = BwdCfg<D>;
@@ -247,7 +274,7 @@ void bwd_dkdv_kernel(const BwdArgs a) {
 
   // Stage the next step (ihq, iqs) into ring slot `slot`: the Q and dO tiles through
   // buffer resources that end at row n_q (rows past it read nothing), and the rows'
-  // (offset, D) pairs, 16 rows per wave from lanes 0..7.
+  // (offset, D) pairs, QSTEP / NW rows per wave from its first RV_LANES lanes.
   const char* const qsrc = reinterpret_cast<const char*>(a.q);
   const char* const dsrc = reinterpret_cast<const char*>(a.dout);
   const char* const wsrc = reinterpret_cast<const char*>(a.ws);
@@ -265,7 +292,8 @@ void bwd_dkdv_kernel(const BwdArgs a) {
     for (int i = 0; i < C::KV_SEGS; ++i)
       lds_dma16_buf(rd, toff[i], lds_addr(st + C::QTILE + (w * C::KV_SEGS + i) * 1024));
     const u32x4 rr = raw_buffer_rsrc(wsrc + row0 * 8, nrows * 8);
-    if (lane < 8) lds_dma16_buf(rr, (unsigned)(128 * w + 16 * lane), lds_addr(st + 2 * C::QTILE + 128 * w));
+    if (lane < C::RV_LANES)
+      lds_dma16_buf(rr, (unsigned)(16 * (C::RV_LANES * w + lane)), lds_addr(st + 2 * C::QTILE + 16 * C::RV_LANES * w));
     if (++iqs == nqs) {
       iqs = qs_first;
       ++ihq;
@@ -287,15 +315,15 @@ void bwd_dkdv_kernel(const BwdArgs a) {
 
     const int q0 = qs * C::QSTEP;
     if (++qs == nqs) qs = qs_first;
-    const bool skip = kw0 >= n_kv || (a.causal && kw0 > q0 + C::QSTEP - 1 + delta);
-    if (skip) continue;
+    int hi = ta.tr_hi;
+    asm volatile("" : "+v"(hi));  // a per-step value: tile + tr + hi is not hoisted out of the loop
     const char* qt = smem + (t % C::KV_NS) * C::KV_STAGE;
     const char* dt = qt + C::QTILE;
     const float* rv = reinterpret_cast<const float*>(qt + 2 * C::QTILE);
 
-    f32x16 s[2], dp[2];
+    f32x16 s[C::RB], dp[C::RB];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < C::RB; ++rb) {
       s[rb] = f32x16{};
       dp[rb] = f32x16{};
 #pragma unroll
@@ -309,7 +337,7 @@ void bwd_dkdv_kernel(const BwdArgs a) {
         (q0 + C::QSTEP > n_q) || (kw0 + 32 > n_kv) || (a.causal && kw0 + 31 > q0 + delta);
     if (need_mask) {
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
+      for (int rb = 0; rb < C::RB; ++rb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int i = q0 + 32 * rb + 8 * (r >> 2) + 4 * half + (r & 3);
@@ -318,9 +346,9 @@ void bwd_dkdv_kernel(const BwdArgs a) {
           dp[rb][r] = vis ? dp[rb][r] : 0.f;
         }
     }
-    bf16x8 pb[4], dsb[4];
+    bf16x8 pb[2 * C::RB], dsb[2 * C::RB];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < C::RB; ++rb)
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const float* pr = rv + 2 * (32 * rb + 8 * m + 4 * half);  // (offset, D) of 4 rows
@@ -338,11 +366,11 @@ void bwd_dkdv_kernel(const BwdArgs a) {
         }
       }
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
+    for (int kk = 0; kk < 2 * C::RB; ++kk)
 #pragma unroll
       for (int nb = 0; nb < C::NB; ++nb) {
-        dva[nb] = mfma_32x32x16(ta.read_tr(dt, kk, nb), pb[kk], dva[nb]);
-        dka[nb] = mfma_32x32x16(ta.read_tr(qt, kk, nb), dsb[kk], dka[nb]);
+        dva[nb] = mfma_32x32x16(ta.read_tr(dt, kk, nb, hi), pb[kk], dva[nb]);
+        dka[nb] = mfma_32x32x16(ta.read_tr(qt, kk, nb, hi), dsb[kk], dka[nb]);
       }
   }
 
@@ -366,7 +394,7 @@ void bwd_dkdv_kernel(const BwdArgs a) {
 
 // ---------------------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(BwdCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(BwdCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(FA_BWD_WPE, FA_BWD_WPE)))
 void bwd_dq_kernel(const BwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using C = BwdCfg<D>;
@@ -393,10 +421,10 @@ void bwd_dq_kernel(const BwdArgs a) {
 
   zero_lds<C::Q_NS * C::Q_STAGE, C::NT>(smem, tid);
 
-  bf16x8 qf[2][C::QKS], dof[2][C::QKS];
-  float off[2], dd[2];
+  bf16x8 qf[C::QB][C::QKS], dof[C::QB][C::QKS];
+  float off[C::QB], dd[C::QB];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < C::QB; ++qb) {
     const int my_q = qw0 + 32 * qb + col;
 #pragma unroll
     for (int ks = 0; ks < C::QKS; ++ks) {
@@ -413,9 +441,9 @@ void bwd_dq_kernel(const BwdArgs a) {
     off[qb] = od.x;
     dd[qb] = od.y;
   }
-  f32x16 dqa[2][C::NB];
+  f32x16 dqa[C::QB][C::NB];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
+  for (int qb = 0; qb < C::QB; ++qb)
 #pragma unroll
     for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
@@ -465,20 +493,22 @@ void bwd_dq_kernel(const BwdArgs a) {
     if (t + C::Q_NS - 1 < T) issue(t + C::Q_NS - 1);
 
     const int k0 = t * C::KSTEP;
-    const bool skip = qw0 >= n_q || (a.causal && k0 > qw0 + C::WROWS - 1 + delta);
-    if (skip) continue;
+    int hi = ta.tr_hi;
+    asm volatile("" : "+v"(hi));  // a per-step value: tile + tr + hi is not hoisted out of the loop
     const char* kt = smem + (t % C::Q_NS) * C::Q_STAGE;
     const char* vt = kt + C::KTILE;
 
     // S^T and dP^T of both row blocks: element r is key k0 + 8 (r / 4) + 4 half + r % 4,
     // query qw0 + 32 qb + col.
-    f32x16 sx[2] = {f32x16{}, f32x16{}}, dpx[2] = {f32x16{}, f32x16{}};
+    f32x16 sx[C::QB], dpx[C::QB];
+#pragma unroll
+    for (int qb = 0; qb < C::QB; ++qb) sx[qb] = dpx[qb] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < C::QKS; ++ks) {
       const bf16x8 ka = ta.read_row(kt, 0, ks);
       const bf16x8 va = ta.read_row(vt, 0, ks);
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
+      for (int qb = 0; qb < C::QB; ++qb) {
         sx[qb] = mfma_32x32x16(ka, qf[qb][ks], sx[qb]);
         dpx[qb] = mfma_32x32x16(va, dof[qb][ks], dpx[qb]);
       }
@@ -487,7 +517,7 @@ void bwd_dq_kernel(const BwdArgs a) {
         (k0 + C::KSTEP > n_kv) || (qw0 + C::WROWS > n_q) || (a.causal && k0 + C::KSTEP - 1 > qw0 + delta);
     if (need_mask) {
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
+      for (int qb = 0; qb < C::QB; ++qb) {
         const int my_q = qw0 + 32 * qb + col;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -498,9 +528,9 @@ void bwd_dq_kernel(const BwdArgs a) {
         }
       }
     }
-    bf16x8 dsb[2][2];
+    bf16x8 dsb[C::QB][2];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int qb = 0; qb < C::QB; ++qb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float p = exp2_hw(fmaf(sx[qb][r], a.scale_log2, -off[qb]));
@@ -510,16 +540,16 @@ void bwd_dq_kernel(const BwdArgs a) {
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int nb = 0; nb < C::NB; ++nb) {
-        const bf16x8 kta = ta.read_tr(kt, ks, nb);
+        const bf16x8 kta = ta.read_tr(kt, ks, nb, hi);
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) dqa[qb][nb] = mfma_32x32x16(kta, dsb[qb][ks], dqa[qb][nb]);
+        for (int qb = 0; qb < C::QB; ++qb) dqa[qb][nb] = mfma_32x32x16(kta, dsb[qb][ks], dqa[qb][nb]);
       }
   }
 
   // dQ = scale * accumulator: lane holds query qw0 + 32 qb + col, dims 32 nb + 8 jj +
   // 4 half + (0..3).
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < C::QB; ++qb) {
     const int my_q = qw0 + 32 * qb + col;
     if (my_q < a.Lq) {
       __bf16* dqp = a.dq + (q_off + my_q) * D;
