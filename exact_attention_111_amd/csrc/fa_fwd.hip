@@ -58,11 +58,12 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 template <int D>
 struct FwdCfg {
-  // d = 128: 32 rows per wave (a wave fits in 256 VGPRs) and 8 waves, two per SIMD.
-  // d = 64: 64 rows per wave and 4 waves, one per SIMD. Either way a workgroup covers 256
-  // query rows, which sets how often each K/V tile is streamed from L2 into LDS.
-  static constexpr int QB = D == 128 ? 1 : 2;     // 32-row query blocks per wave
-  static constexpr int NW = D == 128 ? 8 : 4;     // waves per workgroup
+  // 32 rows per wave and 8 waves, two per SIMD: a wave fits in 256 registers, which also
+  // keeps the compiler's MFMA results in VGPRs (with a 512-register budget it picks the
+  // AGPR form and copies every score tile into VGPRs for the softmax). A workgroup covers
+  // 256 query rows, which sets how often each K/V tile is streamed from L2 into LDS.
+  static constexpr int QB = 1;                    // 32-row query blocks per wave
+  static constexpr int NW = 8;                    // waves per workgroup
   static constexpr int BM = 32 * QB * NW;         // query rows per workgroup (256)
   static constexpr int WAVES_PER_SIMD = NW / 4;
   static constexpr int BN = 64;                   // keys per tile
