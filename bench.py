@@ -8,7 +8,8 @@ One step is one pass of the whole path over resident synthetic inputs:
   * decode:  fa_decode (split-K + combine) on B=64 requests, 32 query / 8 KV heads,
     d=128, bf16 cache with per-request context lengths uniform in [8192, 32768],
     counted as the K and V bytes of every request's context.
-The headline ``value`` is the prefill TFLOP/s; decode KV GB/s is reported beside it.
+The headline ``value`` is the prefill TFLOP/s; decode KV GB/s is reported beside it, and the
+backward of the same prefill (fa_bwd, timed on its own after the step) beside that.
 Kernel durations come from HIP events on the stream the kernels run on (torch's
 current stream), over exactly K timed steps after W warm-up steps.
 
@@ -41,7 +42,8 @@ PREFILL = "causal_prefill_B1_H32_L16384_d128"
 DECODE = "decode_B64_H32_Hkv8_ctx32768_d128"
 # Sources whose compiled kernels a committed counter profile describes.
 KERNEL_SOURCES = {"prefill": ["fa_fwd.hip", "fa_tiles.h", "fa_device.h", "fa_launch.h"],
-                  "decode": ["fa_decode.hip", "fa_device.h", "fa_launch.h"]}
+                  "decode": ["fa_decode.hip", "fa_device.h", "fa_launch.h"],
+                  "backward": ["fa_bwd.hip", "fa_tiles.h", "fa_device.h", "fa_launch.h"]}
 
 
 def parse():
@@ -253,8 +255,32 @@ def main():
     kv_bytes = float(2 * wd.Hkv * wd.d * 2 * int(ctx.sum()))
     gbps = kv_bytes / (dec_avg * 1e-3) / 1e9
 
+    # Backward of the same prefill (the gradients of that step for a synthetic dO), timed on
+    # its own after the step: K launches of fa_bwd after W warm-up launches.
+    g = torch.Generator(device=dev).manual_seed(wp.seed + 1000)
+    do_p = torch.randn(o_p.shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    ws_b = torch.empty(max(16, fa.bwd_workspace_bytes(wp.B, wp.H, wp.L)), dtype=torch.uint8, device=dev)
+    grads = (torch.empty_like(xp["q"]), torch.empty_like(xp["k"]), torch.empty_like(xp["v"]))
+
+    def bwd_call():
+        fa.bwd(xp["q"], xp["k"], xp["v"], o_p, do_p, lse_p, causal=True, scale=wp.scale, workspace=ws_b,
+               dq=grads[0], dk=grads[1], dv=grads[2])
+
+    for _ in range(args.warmup):
+        bwd_call()
+    torch.cuda.synchronize()
+    bev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a_, b_ in bev:
+        a_.record(); bwd_call(); b_.record()
+    torch.cuda.synchronize()
+    bwd_ms = [a_.elapsed_time(b_) for a_, b_ in bev]
+    bwd_avg = sum(bwd_ms) / len(bwd_ms)
+    bwd_flop = BWD_FLOP_PER_FWD * 4.0 * wp.B * wp.H * wp.L * wp.L * wp.d / 2.0
+    bwd_tflops = bwd_flop / (bwd_avg * 1e-3) / 1e12
+
     tr_p, src_p = traffic_record("prefill")
     tr_d, src_d = traffic_record("decode")
+    tr_b, src_b = traffic_record("backward")
     alg_p = float(3 * wp.B * wp.H * wp.L * wp.d * 2 + wp.B * wp.H * wp.L * wp.d * 2 + wp.B * wp.H * wp.L * 4)
     line = {
         "metric": METRIC,
@@ -278,6 +304,12 @@ def main():
                     "pct_mfma_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2), "flop_per_launch": flop},
         "decode": {"value": round(gbps, 1), "unit": "GB/s", "ms": round(dec_avg, 4), "ms_min": round(min(dec_ms), 4),
                    "pct_hbm_peak": round(100 * gbps / PEAK_HBM_GBPS, 2), "kv_bytes_per_launch": kv_bytes},
+        "backward": {"ms": round(bwd_avg, 4), "ms_min": round(min(bwd_ms), 4), "tflops": round(bwd_tflops, 2),
+                     "pct_mfma_peak": round(100 * bwd_tflops / PEAK_BF16_TFLOPS, 2), "flop_per_launch": bwd_flop,
+                     "flop_counting": "5 products of the forward's size (2.5x forward FLOP)",
+                     "kernels": "bwd_dot_kernel<128> + bwd_dkdv_kernel<128> + bwd_dq_kernel<128>",
+                     "traffic": tr_b["bytes_per_launch"] if tr_b else None, "traffic_unit": "bytes/launch",
+                     "traffic_source": src_b},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": tr_p["bytes_per_launch"] if tr_p else None, "traffic_unit": "bytes/launch",
