@@ -30,6 +30,11 @@ Readings where the pages are silent (each is listed in the design doc):
 * With per-sequence lengths n_b (self-attention, Lq = Lk), keys j >= n_b are
   masked and query rows i >= n_b are padding: O = 0 and LSE = -inf there.
 * A row that sees no key at all gets O = 0 and LSE = -inf (no NaN).
+* Sliding window ("FlashAttention 与长上下文", section on prefill and decode,
+  which lists the sliding window among the context-trimming methods without
+  defining it): with window W >= 1 and the causal mask, query i sees only the
+  W newest keys it is allowed to see, i + (Lk - Lq) - W < j <= i + (Lk - Lq);
+  a decode query of context n sees keys max(0, n - W) .. n - 1.
 
 Parity pins for every function here are in ``tests/test_oracle.py``; no
 function in this module is "parity unpinned".
@@ -41,26 +46,31 @@ import numpy as np
 NEG_INF = -np.inf
 
 
-def _visible(Lq: int, Lk: int, causal: bool, n_valid: int, rows=None) -> np.ndarray:
+def _visible(Lq: int, Lk: int, causal: bool, n_valid: int, rows=None, window=None) -> np.ndarray:
     """Boolean [len(rows), Lk]: key j visible to query row i.
 
     Padding: keys at or beyond ``n_valid`` are masked. Causal (bottom-right
-    aligned): key j is masked when j > i + (Lk - Lq).
+    aligned): key j is masked when j > i + (Lk - Lq). Sliding window W (with
+    causal): key j is also masked when j <= i + (Lk - Lq) - W.
     """
     i = np.arange(Lq) if rows is None else np.asarray(rows)
     j = np.arange(Lk)
     vis = np.broadcast_to(j[None, :] < n_valid, (len(i), Lk)).copy()
     if causal:
         vis &= j[None, :] <= (i[:, None] + (Lk - Lq))
+    if window is not None:
+        assert causal and window >= 1, "a sliding window needs the causal mask and W >= 1"
+        vis &= j[None, :] > (i[:, None] + (Lk - Lq) - window)
     return vis
 
 
-def attention_head(q, k, v, *, scale, causal=False, n_valid=None, rows=None, return_p=False):
+def attention_head(q, k, v, *, scale, causal=False, n_valid=None, rows=None, return_p=False, window=None):
     """Exact attention for one (batch, head) pair, the naive materialised way.
 
     q: [Lq, d]; k, v: [Lk, d] (float64). ``n_valid``: valid sequence length for
     both query rows and keys (None = no padding). ``rows``: optional subset of
     query rows to evaluate (the result is identical to slicing the full result).
+    ``window``: sliding-window size W (needs ``causal``), None for none.
     Returns (O [r, d], LSE [r]) and optionally P [r, Lk].
     """
     q = np.asarray(q, dtype=np.float64)
@@ -71,7 +81,7 @@ def attention_head(q, k, v, *, scale, causal=False, n_valid=None, rows=None, ret
     n = Lk if n_valid is None else int(n_valid)
     # Step 1: score matrix S = scale * Q K^T, with -inf where the mask hides a key.
     S = scale * (q[row_idx] @ k.T)
-    vis = _visible(Lq, Lk, causal, n, row_idx)
+    vis = _visible(Lq, Lk, causal, n, row_idx, window)
     S = np.where(vis, S, NEG_INF)
     # Padding query rows (i >= n_valid) attend to nothing.
     if n_valid is not None:
@@ -92,12 +102,12 @@ def attention_head(q, k, v, *, scale, causal=False, n_valid=None, rows=None, ret
     return O, lse
 
 
-def attention(q, k, v, *, scale, causal=False, seqlens=None, heads=None, rows=None):
+def attention(q, k, v, *, scale, causal=False, seqlens=None, heads=None, rows=None, window=None):
     """Exact attention over [B, H, Lq, d] queries and [B, Hkv, Lk, d] keys/values.
 
     ``seqlens``: optional per-batch valid lengths (requires Lq == Lk).
     ``heads``: optional list of (b, h) pairs to evaluate; ``rows``: optional
-    query-row subset applied to every evaluated head.
+    query-row subset applied to every evaluated head. ``window``: sliding window W.
     Returns (O, LSE) with shapes [B, H, r, d] and [B, H, r] (entries of heads not
     evaluated are NaN).
     """
@@ -115,16 +125,17 @@ def attention(q, k, v, *, scale, causal=False, seqlens=None, heads=None, rows=No
         kvh = h // group
         n = None if seqlens is None else int(seqlens[b])
         O[b, h], LSE[b, h] = attention_head(q[b, h], k[b, kvh], v[b, kvh], scale=scale, causal=causal,
-                                            n_valid=n, rows=rows)
+                                            n_valid=n, rows=rows, window=window)
     return O, LSE
 
 
-def decode(q, k_cache, v_cache, ctx_lens, *, scale, heads=None):
+def decode(q, k_cache, v_cache, ctx_lens, *, scale, heads=None, window=None):
     """Single-token decode: query [B, H, d] against cache [B, Hkv, Lmax, d].
 
     Request b sees cached keys 0 .. ctx_lens[b]-1 and nothing else (the new
     token is the newest position, so bottom-right causal alignment leaves every
-    cached key visible). Returns (O [B, H, d], LSE [B, H]).
+    cached key visible). With a sliding window W it sees keys
+    max(0, n - W) .. n - 1 of its context n. Returns (O [B, H, d], LSE [B, H]).
     """
     B, H, d = q.shape
     Hkv = k_cache.shape[1]
@@ -135,7 +146,8 @@ def decode(q, k_cache, v_cache, ctx_lens, *, scale, heads=None):
     for b, h in pairs:
         n = int(ctx_lens[b])
         kvh = h // group
-        o, lse = attention_head(q[b, h][None, :], k_cache[b, kvh, :n], v_cache[b, kvh, :n], scale=scale)
+        o, lse = attention_head(q[b, h][None, :], k_cache[b, kvh, :n], v_cache[b, kvh, :n], scale=scale,
+                                causal=window is not None, window=window)
         O[b, h], LSE[b, h] = o[0], lse[0]
     return O, LSE
 

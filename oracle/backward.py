@@ -38,10 +38,10 @@ import numpy as np
 from .attention import attention_head
 
 
-def attention_backward_head(q, k, v, do, *, scale, causal=False, n_valid=None):
+def attention_backward_head(q, k, v, do, *, scale, causal=False, n_valid=None, window=None):
     """Gradients (dQ [Lq, d], dK [Lk, d], dV [Lk, d]) of one head, given dO [Lq, d]."""
     q, k, v, do = (np.asarray(t, dtype=np.float64) for t in (q, k, v, do))
-    O, _, P = attention_head(q, k, v, scale=scale, causal=causal, n_valid=n_valid, return_p=True)
+    O, _, P = attention_head(q, k, v, scale=scale, causal=causal, n_valid=n_valid, return_p=True, window=window)
     dV = P.T @ do
     dP = do @ v.T
     D = (do * O).sum(axis=1)
@@ -51,7 +51,7 @@ def attention_backward_head(q, k, v, do, *, scale, causal=False, n_valid=None):
     return dQ, dK, dV
 
 
-def attention_backward(q, k, v, do, *, scale, causal=False, seqlens=None):
+def attention_backward(q, k, v, do, *, scale, causal=False, seqlens=None, window=None):
     """Gradients over [B, H, Lq, d] queries and [B, Hkv, Lk, d] keys/values.
 
     Returns (dQ [B, H, Lq, d], dK [B, Hkv, Lk, d], dV [B, Hkv, Lk, d]); dK and dV
@@ -71,7 +71,7 @@ def attention_backward(q, k, v, do, *, scale, causal=False, seqlens=None):
         for h in range(H):
             kvh = h // group
             gq, gk, gv = attention_backward_head(q[b, h], k[b, kvh], v[b, kvh], do[b, h], scale=scale,
-                                                 causal=causal, n_valid=n)
+                                                 causal=causal, n_valid=n, window=window)
             dQ[b, h] = gq
             dK[b, kvh] += gk
             dV[b, kvh] += gv
