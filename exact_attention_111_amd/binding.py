@@ -15,7 +15,9 @@ import torch
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
 FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
-SYMBOLS = ("fa_fwd", "fa_fwd_f32", "fa_decode", "fa_decode_workspace_bytes", "fa_status_string")
+SYMBOLS = ("fa_fwd", "fa_fwd_sliding_window", "fa_fwd_f32", "fa_decode", "fa_decode_sliding_window",
+           "fa_decode_workspace_bytes", "fa_bwd", "fa_bwd_sliding_window", "fa_bwd_workspace_bytes",
+           "fa_status_string")
 
 
 class FaError(RuntimeError):
@@ -44,15 +46,22 @@ def lib() -> ctypes.CDLL:
     L.fa_fwd.restype = i32
     L.fa_fwd_f32.argtypes = fwd_args
     L.fa_fwd_f32.restype = i32
+    L.fa_fwd_sliding_window.argtypes = fwd_args  # the int after scale is the window
+    L.fa_fwd_sliding_window.restype = i32
     L.fa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
     L.fa_decode_workspace_bytes.restype = ctypes.c_size_t
     L.fa_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, vp, vp, ctypes.c_size_t, vp]
     L.fa_decode.restype = i32
+    L.fa_decode_sliding_window.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, vp, i32, vp,
+                                           ctypes.c_size_t, vp]
+    L.fa_decode_sliding_window.restype = i32
     L.fa_bwd_workspace_bytes.argtypes = [i32, i32, i32]
     L.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
     L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp, vp,
                          ctypes.c_size_t, vp]
     L.fa_bwd.restype = i32
+    L.fa_bwd_sliding_window.argtypes = L.fa_bwd.argtypes  # the int after scale is the window
+    L.fa_bwd_sliding_window.restype = i32
     L.fa_status_string.argtypes = [i32]
     L.fa_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -76,8 +85,10 @@ def _check(status: int, what: str):
         raise FaError(status, what)
 
 
-def fwd(q, k, v, *, causal: bool = False, scale: float | None = None, seqlens=None, out=None, lse=None):
-    """Attention forward through ``fa_fwd`` (bf16) or ``fa_fwd_f32`` (fp32 I/O).
+def fwd(q, k, v, *, causal: bool = False, scale: float | None = None, seqlens=None, out=None, lse=None,
+        window: int | None = None):
+    """Attention forward through ``fa_fwd`` (bf16), ``fa_fwd_f32`` (fp32 I/O) or, with
+    ``window``, ``fa_fwd_sliding_window`` (bf16, causal band of ``window`` keys).
 
     q: [B, H, Lq, d]; k, v: [B, Hkv, Lk, d], contiguous, on one GPU, all bf16 or all
     fp32. seqlens: optional int32 [B] on the same device (requires Lq == Lk).
@@ -98,10 +109,16 @@ def fwd(q, k, v, *, causal: bool = False, scale: float | None = None, seqlens=No
         raise ValueError("q, k, v, out must all be bfloat16 or all float32")
     if seqlens is not None and seqlens.dtype != torch.int32:
         raise ValueError("seqlens must be int32")
-    fn = lib().fa_fwd if q.dtype == torch.bfloat16 else lib().fa_fwd_f32
-    st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Hkv, Lq, Lk, d, float(scale), int(bool(causal)),
-            _ptr(seqlens), _stream(q.device))
-    _check(st, "fa_fwd" if q.dtype == torch.bfloat16 else "fa_fwd_f32")
+    if window is not None:
+        if q.dtype != torch.bfloat16 or not causal:
+            raise ValueError("a sliding window needs bfloat16 inputs and causal=True")
+        name, flag = "fa_fwd_sliding_window", int(window)
+    else:
+        name = "fa_fwd" if q.dtype == torch.bfloat16 else "fa_fwd_f32"
+        flag = int(bool(causal))
+    st = getattr(lib(), name)(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Hkv, Lq, Lk, d, float(scale),
+                              flag, _ptr(seqlens), _stream(q.device))
+    _check(st, name)
     return out, lse
 
 
@@ -109,8 +126,9 @@ def decode_workspace_bytes(B: int, H: int, Lmax: int, d: int) -> int:
     return int(lib().fa_decode_workspace_bytes(B, H, Lmax, d))
 
 
-def decode(q, k_cache, v_cache, ctx_lens, *, scale: float | None = None, workspace=None, out=None, lse=None):
-    """Single-token decode through ``fa_decode``.
+def decode(q, k_cache, v_cache, ctx_lens, *, scale: float | None = None, workspace=None, out=None, lse=None,
+           window: int | None = None):
+    """Single-token decode through ``fa_decode`` (or ``fa_decode_sliding_window`` with ``window``).
 
     q: [B, H, d] bf16; k_cache, v_cache: [B, Hkv, Lmax, d] bf16; ctx_lens: int32 [B].
     ``workspace``: optional uint8 device tensor of at least ``decode_workspace_bytes``.
@@ -134,10 +152,16 @@ def decode(q, k_cache, v_cache, ctx_lens, *, scale: float | None = None, workspa
         raise ValueError("decode needs bfloat16 q, caches and out")
     if ctx_lens.dtype != torch.int32:
         raise ValueError("ctx_lens must be int32")
-    st = lib().fa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), B, H, Hkv, Lmax, d,
-                         float(scale), _ptr(ctx_lens), _ptr(workspace), workspace.numel() * workspace.element_size(),
-                         _stream(q.device))
-    _check(st, "fa_decode")
+    wsb = workspace.numel() * workspace.element_size()
+    if window is None:
+        st = lib().fa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), B, H, Hkv, Lmax, d,
+                             float(scale), _ptr(ctx_lens), _ptr(workspace), wsb, _stream(q.device))
+        _check(st, "fa_decode")
+    else:
+        st = lib().fa_decode_sliding_window(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), B, H, Hkv,
+                                            Lmax, d, float(scale), _ptr(ctx_lens), int(window), _ptr(workspace), wsb,
+                                            _stream(q.device))
+        _check(st, "fa_decode_sliding_window")
     return out, lse
 
 
@@ -146,11 +170,12 @@ def bwd_workspace_bytes(B: int, H: int, Lq: int) -> int:
 
 
 def bwd(q, k, v, o, dout, lse, *, causal: bool = False, scale: float | None = None, seqlens=None, workspace=None,
-        dq=None, dk=None, dv=None):
-    """Gradients through ``fa_bwd`` (bf16): (dq, dk, dv) for upstream gradient ``dout``.
+        dq=None, dk=None, dv=None, window: int | None = None):
+    """Gradients through ``fa_bwd`` (bf16), or ``fa_bwd_sliding_window`` with ``window``:
+    (dq, dk, dv) for upstream gradient ``dout``.
 
     q, o, dout: [B, H, Lq, d]; k, v: [B, Hkv, Lk, d], bf16, contiguous; lse: [B, H, Lq] fp32
-    from ``fwd``; causal, scale and seqlens as passed to ``fwd``.
+    from ``fwd``; causal, scale, seqlens and window as passed to ``fwd``.
     """
     B, H, Lq, d = q.shape
     Hkv, Lk = k.shape[1], k.shape[2]
@@ -171,8 +196,14 @@ def bwd(q, k, v, o, dout, lse, *, causal: bool = False, scale: float | None = No
         raise ValueError("lse must be float32")
     if seqlens is not None and seqlens.dtype != torch.int32:
         raise ValueError("seqlens must be int32")
-    st = lib().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
-                      B, H, Hkv, Lq, Lk, d, float(scale), int(bool(causal)), _ptr(seqlens), _ptr(workspace),
-                      workspace.numel() * workspace.element_size(), _stream(q.device))
-    _check(st, "fa_bwd")
+    if window is not None:
+        if not causal:
+            raise ValueError("a sliding window needs causal=True")
+        name, flag = "fa_bwd_sliding_window", int(window)
+    else:
+        name, flag = "fa_bwd", int(bool(causal))
+    st = getattr(lib(), name)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+                              _ptr(dv), B, H, Hkv, Lq, Lk, d, float(scale), flag, _ptr(seqlens), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _stream(q.device))
+    _check(st, name)
     return dq, dk, dv

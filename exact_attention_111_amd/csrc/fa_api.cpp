@@ -69,17 +69,55 @@ fa_status validate_bwd(const void* q, const void* k, const void* v, const void* 
   return FA_OK;
 }
 
+fa_status fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int Lq,
+                   int Lk, int d, float scale, int causal, int window, const int32_t* seqlens, void* stream) {
+  const fa_status s = validate_fwd(q, k, v, o, lse, B, H, Hkv, Lq, Lk, d, scale, causal, seqlens);
+  if (s != FA_OK) return s;
+  if (B == 0 || H == 0 || Lq == 0) return FA_OK;
+  fa::FwdParams p{q, k, v, o, lse, B, H, Hkv, Lq, Lk, d, scale, causal, window, seqlens};
+  return fa::launch_fwd_bf16(p, static_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status decode_impl(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse, int B, int H,
+                      int Hkv, int Lmax, int d, float scale, const int32_t* ctx_lens, int window, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  const fa_status s = validate_decode(q, k_cache, v_cache, o, lse, B, H, Hkv, Lmax, d, scale, ctx_lens, workspace,
+                                      workspace_bytes);
+  if (s != FA_OK) return s;
+  if (B == 0 || H == 0) return FA_OK;
+  const size_t nc = (size_t)fa::decode_num_chunks(Lmax);
+  float* ws_o = static_cast<float*>(workspace);
+  float* ws_ml = ws_o + (size_t)B * H * nc * d;
+  fa::DecodeParams p{q, k_cache, v_cache, o, lse, B, H, Hkv, Lmax, d, scale, ctx_lens, window, ws_o, ws_ml};
+  return fa::launch_decode(p, static_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status bwd_impl(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                   void* dq, void* dk, void* dv, int B, int H, int Hkv, int Lq, int Lk, int d, float scale, int causal,
+                   int window, const int32_t* seqlens, void* workspace, size_t workspace_bytes, void* stream) {
+  const fa_status s = validate_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, Hkv, Lq, Lk, d, scale, causal, seqlens,
+                                   workspace, workspace_bytes);
+  if (s != FA_OK) return s;
+  if (B == 0) return FA_OK;  // otherwise dK/dV are written even when there are no query rows (then zero)
+  fa::BwdParams p{q, k, v, o, dout, lse, dq, dk, dv, B, H, Hkv, Lq, Lk, d, scale, causal, window, seqlens,
+                  static_cast<float*>(workspace)};
+  return fa::launch_bwd(p, static_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
 
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int Lq,
                  int Lk, int d, float scale, int causal, const int32_t* seqlens, void* stream) {
-  const fa_status s = validate_fwd(q, k, v, o, lse, B, H, Hkv, Lq, Lk, d, scale, causal, seqlens);
-  if (s != FA_OK) return s;
-  if (B == 0 || H == 0 || Lq == 0) return FA_OK;
-  fa::FwdParams p{q, k, v, o, lse, B, H, Hkv, Lq, Lk, d, scale, causal, seqlens};
-  return fa::launch_fwd_bf16(p, static_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_HIP;
+  return fwd_bf16(q, k, v, o, lse, B, H, Hkv, Lq, Lk, d, scale, causal, 0, seqlens, stream);
+}
+
+fa_status fa_fwd_sliding_window(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                                int Hkv, int Lq, int Lk, int d, float scale, int window, const int32_t* seqlens,
+                                void* stream) {
+  if (window < 1) return FA_ERR_INVALID;
+  return fwd_bf16(q, k, v, o, lse, B, H, Hkv, Lq, Lk, d, scale, 1, window, seqlens, stream);
 }
 
 fa_status fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int Hkv,
@@ -87,7 +125,7 @@ fa_status fa_fwd_f32(const float* q, const float* k, const float* v, float* o, f
   const fa_status s = validate_fwd(q, k, v, o, lse, B, H, Hkv, Lq, Lk, d, scale, causal, seqlens);
   if (s != FA_OK) return s;
   if (B == 0 || H == 0 || Lq == 0) return FA_OK;
-  fa::FwdParams p{q, k, v, o, lse, B, H, Hkv, Lq, Lk, d, scale, causal, seqlens};
+  fa::FwdParams p{q, k, v, o, lse, B, H, Hkv, Lq, Lk, d, scale, causal, 0, seqlens};
   return fa::launch_fwd_f32(p, static_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -101,15 +139,16 @@ size_t fa_decode_workspace_bytes(int B, int H, int Lmax, int d) {
 fa_status fa_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse, int B, int H,
                     int Hkv, int Lmax, int d, float scale, const int32_t* ctx_lens, void* workspace,
                     size_t workspace_bytes, void* stream) {
-  const fa_status s = validate_decode(q, k_cache, v_cache, o, lse, B, H, Hkv, Lmax, d, scale, ctx_lens, workspace,
-                                      workspace_bytes);
-  if (s != FA_OK) return s;
-  if (B == 0 || H == 0) return FA_OK;
-  const size_t nc = (size_t)fa::decode_num_chunks(Lmax);
-  float* ws_o = static_cast<float*>(workspace);
-  float* ws_ml = ws_o + (size_t)B * H * nc * d;
-  fa::DecodeParams p{q, k_cache, v_cache, o, lse, B, H, Hkv, Lmax, d, scale, ctx_lens, ws_o, ws_ml};
-  return fa::launch_decode(p, static_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_HIP;
+  return decode_impl(q, k_cache, v_cache, o, lse, B, H, Hkv, Lmax, d, scale, ctx_lens, 0, workspace, workspace_bytes,
+                     stream);
+}
+
+fa_status fa_decode_sliding_window(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                                   int B, int H, int Hkv, int Lmax, int d, float scale, const int32_t* ctx_lens,
+                                   int window, void* workspace, size_t workspace_bytes, void* stream) {
+  if (window < 1) return FA_ERR_INVALID;
+  return decode_impl(q, k_cache, v_cache, o, lse, B, H, Hkv, Lmax, d, scale, ctx_lens, window, workspace,
+                     workspace_bytes, stream);
 }
 
 size_t fa_bwd_workspace_bytes(int B, int H, int Lq) {
@@ -120,13 +159,17 @@ size_t fa_bwd_workspace_bytes(int B, int H, int Lq) {
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                  void* dq, void* dk, void* dv, int B, int H, int Hkv, int Lq, int Lk, int d, float scale, int causal,
                  const int32_t* seqlens, void* workspace, size_t workspace_bytes, void* stream) {
-  const fa_status s = validate_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, Hkv, Lq, Lk, d, scale, causal, seqlens,
-                                   workspace, workspace_bytes);
-  if (s != FA_OK) return s;
-  if (B == 0) return FA_OK;  // otherwise dK/dV are written even when there are no query rows (then zero)
-  fa::BwdParams p{q, k, v, o, dout, lse, dq, dk, dv, B, H, Hkv, Lq, Lk, d, scale, causal, seqlens,
-                  static_cast<float*>(workspace)};
-  return fa::launch_bwd(p, static_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_HIP;
+  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, Hkv, Lq, Lk, d, scale, causal, 0, seqlens, workspace,
+                  workspace_bytes, stream);
+}
+
+fa_status fa_bwd_sliding_window(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                                const float* lse, void* dq, void* dk, void* dv, int B, int H, int Hkv, int Lq, int Lk,
+                                int d, float scale, int window, const int32_t* seqlens, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (window < 1) return FA_ERR_INVALID;
+  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, Hkv, Lq, Lk, d, scale, 1, window, seqlens, workspace,
+                  workspace_bytes, stream);
 }
 
 const char* fa_status_string(fa_status s) {

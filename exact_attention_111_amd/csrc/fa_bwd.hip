@@ -102,6 +102,7 @@ struct BwdArgs {
   int group;
   float scale, scale_log2;
   int causal;
+  int window;  // sliding window W (0: none): key j needs j > i + Lk - Lq - W
   const int32_t* seqlens;
 };
 
@@ -266,10 +267,12 @@ void bwd_dkdv_kernel(const BwdArgs a) {
 
   // Steps: (query head of the group, 64-row block) pairs, head-major. The first row that
   // sees key k0 is k0 - delta (bottom-right causal alignment: j <= i + delta).
+  // With a sliding window the last row that sees key k0 + KEYS - 1 is k0 + KEYS - 2 - delta + W.
   const int q_first = (k0 < n_kv) ? (a.causal ? max(0, k0 - delta) : 0) : n_q;
+  const int q_end = a.window > 0 ? min(n_q, k0 + C::KEYS - 1 - delta + a.window) : n_q;  // exclusive
   const int qs_first = q_first / C::QSTEP;
-  const int nqs = (n_q + C::QSTEP - 1) / C::QSTEP;
-  const int per_head = max(nqs - qs_first, 0);
+  const int nqs = max((q_end + C::QSTEP - 1) / C::QSTEP, qs_first);  // end of the step range
+  const int per_head = nqs - qs_first;
   const int T = a.group * per_head;
 
   // Stage the next step (ihq, iqs) into ring slot `slot`: the Q and dO tiles through
@@ -333,15 +336,16 @@ void bwd_dkdv_kernel(const BwdArgs a) {
       }
     }
     // Element r of block rb: query row q0 + 32 rb + 8 (r / 4) + 4 half + r % 4, key my_key.
-    const bool need_mask =
-        (q0 + C::QSTEP > n_q) || (kw0 + 32 > n_kv) || (a.causal && kw0 + 31 > q0 + delta);
+    const bool need_mask = (q0 + C::QSTEP > n_q) || (kw0 + 32 > n_kv) || (a.causal && kw0 + 31 > q0 + delta) ||
+                           (a.window > 0 && kw0 <= q0 + C::QSTEP - 1 + delta - a.window);
     if (need_mask) {
 #pragma unroll
       for (int rb = 0; rb < C::RB; ++rb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int i = q0 + 32 * rb + 8 * (r >> 2) + 4 * half + (r & 3);
-          const bool vis = i < n_q && my_key < n_kv && (!a.causal || my_key <= i + delta);
+          const bool vis = i < n_q && my_key < n_kv && (!a.causal || my_key <= i + delta) &&
+                           (a.window <= 0 || my_key > i + delta - a.window);
           s[rb][r] = vis ? s[rb][r] : kNegInf;
           dp[rb][r] = vis ? dp[rb][r] : 0.f;
         }
@@ -462,14 +466,18 @@ void bwd_dq_kernel(const BwdArgs a) {
     kv_end = max(kv_end, 0);
   }
   kv_end = __builtin_amdgcn_readfirstlane(kv_end);
-  const int T = (kv_end + C::KSTEP - 1) / C::KSTEP;
+  // With a sliding window the block's first row sees nothing before q0 + delta - W + 1:
+  // step t holds keys kbase + KSTEP t ...
+  const int kbase = __builtin_amdgcn_readfirstlane(
+      a.window > 0 ? (max(q0 + delta - a.window + 1, 0) / C::KSTEP) * C::KSTEP : 0);
+  const int T = max((kv_end - kbase + C::KSTEP - 1) / C::KSTEP, 0);
 
   // Stage key tile t into ring slot t % Q_NS through buffer resources that end at key
   // kv_end (keys past it read nothing).
   const char* const ksrc = reinterpret_cast<const char*>(a.k) + kv_row0 * C::ROWB;
   const char* const vsrc = reinterpret_cast<const char*>(a.v) + kv_row0 * C::ROWB;
   auto issue = [&](int t) {
-    const int k0 = t * C::KSTEP;
+    const int k0 = kbase + t * C::KSTEP;
     const unsigned nrows = (unsigned)max(kv_end - k0, 0);
     char* st = smem + (t % C::Q_NS) * C::Q_STAGE;
     const u32x4 rk = raw_buffer_rsrc(ksrc + (size_t)k0 * C::ROWB, nrows * C::ROWB);
@@ -492,7 +500,7 @@ void bwd_dq_kernel(const BwdArgs a) {
     lds_barrier();
     if (t + C::Q_NS - 1 < T) issue(t + C::Q_NS - 1);
 
-    const int k0 = t * C::KSTEP;
+    const int k0 = kbase + t * C::KSTEP;
     int hi = ta.tr_hi;
     asm volatile("" : "+v"(hi));  // a per-step value: tile + tr + hi is not hoisted out of the loop
     const char* kt = smem + (t % C::Q_NS) * C::Q_STAGE;
@@ -513,8 +521,9 @@ void bwd_dq_kernel(const BwdArgs a) {
         dpx[qb] = mfma_32x32x16(va, dof[qb][ks], dpx[qb]);
       }
     }
-    const bool need_mask =
-        (k0 + C::KSTEP > n_kv) || (qw0 + C::WROWS > n_q) || (a.causal && k0 + C::KSTEP - 1 > qw0 + delta);
+    const bool need_mask = (k0 + C::KSTEP > n_kv) || (qw0 + C::WROWS > n_q) ||
+                           (a.causal && k0 + C::KSTEP - 1 > qw0 + delta) ||
+                           (a.window > 0 && k0 <= qw0 + C::WROWS - 1 + delta - a.window);
     if (need_mask) {
 #pragma unroll
       for (int qb = 0; qb < C::QB; ++qb) {
@@ -522,7 +531,8 @@ void bwd_dq_kernel(const BwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int j = k0 + 8 * (r >> 2) + 4 * half + (r & 3);
-          const bool vis = my_q < n_q && j < n_kv && (!a.causal || j <= my_q + delta);
+          const bool vis = my_q < n_q && j < n_kv && (!a.causal || j <= my_q + delta) &&
+                           (a.window <= 0 || j > my_q + delta - a.window);
           sx[qb][r] = vis ? sx[qb][r] : kNegInf;
           dpx[qb][r] = vis ? dpx[qb][r] : 0.f;
         }
@@ -585,6 +595,7 @@ hipError_t launch_b(const BwdParams& p, hipStream_t stream) {
   a.scale = p.scale;
   a.scale_log2 = p.scale * kLog2e;
   a.causal = p.causal;
+  a.window = p.window;
   a.seqlens = p.seqlens;
   void* args[] = {&a};
   const long long rows = (long long)p.B * p.H * p.Lq;

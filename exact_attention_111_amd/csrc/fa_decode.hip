@@ -43,6 +43,7 @@ struct DecArgs {
   int nsg;     // head slots of 4 per KV head
   int nchunk;  // chunks per request at capacity
   float scale_log2;
+  int window;  // sliding window W (0: none): the last W keys of the context
   const int32_t* ctx;
   float* ws_o;
   float* ws_ml;
@@ -65,9 +66,14 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecArgs a) {
   const int kvh = bk - b * a.Hkv;
 
   const int n = min(max(a.ctx[b], 0), a.Lmax);
+  const int w0 = a.window > 0 ? max(n - a.window, 0) : 0;  // first visible key
   const int c0 = chunk * kDecodeChunk;
-  if (c0 >= n) return;  // chunk past this request's context: nothing to write
   const int c1 = min(n, c0 + kDecodeChunk);
+  if (c0 >= n || c1 <= w0) return;  // chunk outside the visible keys: nothing to write
+  // First step: the 32-key step that holds the first visible key of the chunk, so every
+  // step holds at least one visible key; keys of that step before the window are neither
+  // loaded (zeros instead) nor counted (score -inf).
+  const int k_start = c0 + ((max(w0, c0) - c0) & ~(kKeysPerStep - 1));
   const int h0 = kvh * a.group + sg * kHeadsPerPass;
   const int nh = min(kHeadsPerPass, a.group - sg * kHeadsPerPass);
 
@@ -97,7 +103,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecArgs a) {
 #pragma unroll
       for (int s = 0; s < QS; ++s) {
         u32x4 u = {0u, 0u, 0u, 0u};
-        if (key < c1) u = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + (size_t)key * D + 32 * s + 8 * (lane >> 4)));
+        if (key < c1 && key >= w0) u = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + (size_t)key * D + 32 * s + 8 * (lane >> 4)));
         kr[blk][s] = u;
       }
     }
@@ -105,7 +111,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecArgs a) {
     for (int i = 0; i < VLOADS; ++i) {
       const int key = k0 + i * VKPL + vkey;
       u32x4 u = {0u, 0u, 0u, 0u};
-      if (key < c1) u = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + (size_t)key * D + 8 * vch));
+      if (key < c1 && key >= w0) u = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + (size_t)key * D + 8 * vch));
       vr[i] = u;
     }
   };
@@ -119,8 +125,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecArgs a) {
     for (int e = 0; e < 8; ++e) o[i][e] = 0.f;
   }
 
-  load_step(c0);
-  for (int k0 = c0; k0 < c1; k0 += kKeysPerStep) {
+  load_step(k_start);
+  for (int k0 = k_start; k0 < c1; k0 += kKeysPerStep) {
     // Scores for 32 keys: accumulator element i is head slot i, key k0 + 16 blk + lane % 16.
     f32x4 sc[2];
 #pragma unroll
@@ -135,8 +141,10 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecArgs a) {
     if (k0 + kKeysPerStep < c1) load_step(k0 + kKeysPerStep);  // prefetch the next 32 keys
 
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-      if (k0 + 16 * blk + (lane & 15) >= c1) sc[blk] = f32x4{kNegInf, kNegInf, kNegInf, kNegInf};
+    for (int blk = 0; blk < 2; ++blk) {
+      const int key = k0 + 16 * blk + (lane & 15);
+      if (key >= c1 || key < w0) sc[blk] = f32x4{kNegInf, kNegInf, kNegInf, kNegInf};
+    }
 
     float p[2][kHeadsPerPass];
 #pragma unroll
@@ -215,18 +223,20 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const DecArgs a) {
   const int b = bh / a.H;
   const int n = min(max(a.ctx[b], 0), a.Lmax);
   const int nc = (n + kDecodeChunk - 1) / kDecodeChunk;
+  // Chunks before the window's first key were not written.
+  const int cf = a.window > 0 ? max(n - a.window, 0) / kDecodeChunk : 0;
   const float* ml = a.ws_ml + (size_t)bh * a.nchunk * 2;
   const float* wo = a.ws_o + (size_t)bh * a.nchunk * D;
 
   float M = kNegInf;
-  for (int c = lane; c < nc; c += 64) M = fmaxf(M, ml[2 * c]);
+  for (int c = cf + lane; c < nc; c += 64) M = fmaxf(M, ml[2 * c]);
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
 
   float L = 0.f, acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-  for (int c = 0; c < nc; ++c) {
+  for (int c = cf; c < nc; ++c) {
     const float wgt = exp2_hw(ml[2 * c] - M);
     L += wgt * ml[2 * c + 1];
 #pragma unroll
@@ -254,6 +264,7 @@ hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
   a.nchunk = decode_num_chunks(p.Lmax);
   a.scale_log2 = p.scale * kLog2e;
   a.ctx = p.ctx_lens;
+  a.window = p.window;
   a.ws_o = p.ws_o;
   a.ws_ml = p.ws_ml;
   void* args[] = {&a};

@@ -81,6 +81,30 @@ __device__ __forceinline__ const T* uniform_ptr(const T* p) {
   return reinterpret_cast<const T*>((hi << 32) | lo);
 }
 
+// Both halves of a wave at once: v_permlane32_swap exchanges the upper 32 lanes of its
+// first operand with the lower 32 lanes of its second, so swapping a value with itself
+// leaves [x_lo, x_lo] and [x_hi, x_hi]: every lane then holds its own value and that of
+// lane ^ 32. The second operand passes through an empty asm: handed the same value twice,
+// the compiler kept only one of the two results (each lane then saw only the lower half's
+// value).
+__device__ __forceinline__ void wave_halves(unsigned x, unsigned& lo_half, unsigned& hi_half) {
+  unsigned y = x;
+  asm volatile("" : "+v"(y));
+  const auto sw = __builtin_amdgcn_permlane32_swap(x, y, false, false);
+  lo_half = sw[0];
+  hi_half = sw[1];
+}
+__device__ __forceinline__ float max_of_halves(float x) {
+  unsigned a, b;
+  wave_halves(__builtin_bit_cast(unsigned, x), a, b);
+  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+}
+__device__ __forceinline__ bool any_of_halves(bool x) {
+  unsigned a, b;
+  wave_halves((unsigned)x, a, b);
+  return (a | b) != 0u;
+}
+
 // Byte address of a pointer into LDS.
 __device__ __forceinline__ unsigned lds_addr(const void* p) {
   return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)p;

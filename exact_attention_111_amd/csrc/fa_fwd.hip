@@ -25,7 +25,7 @@
 //     each wave waits for its own loads before the barrier that closes a tile.
 //   * S^T = K Q^T (keys down, queries across): in the 32x32 accumulator layout a lane holds
 //     one query column, so a row's reference, sum and rescale factor live in that lane
-//     (plus lane ^ 32, exchanged with v_permlane32_swap).
+//     (plus lane ^ 32, combined with v_permlane32_swap).
 //   * O^T = V^T P^T with P taken straight from the accumulators (converted to bf16) and the
 //     V^T operand read from the row-major V tile with ds_read_b64_tr_b16 (its 16-lane
 //     transpose turns 4 rows x 4 dims into the 4-keys-per-lane operand layout). The
@@ -94,6 +94,7 @@ struct FwdArgs {
   int nwg;          // workgroups
   float scale_log2; // scale * log2(e)
   int causal;
+  int window;       // sliding window W (0: none): key j needs j > i + Lk - Lq - W
   const int32_t* seqlens;
 };
 
@@ -157,7 +158,9 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) my_q[qb] = qw0 + 32 * qb + col;
 
-  // Keys this query tile can see: [0, kv_end).
+  // Keys this query tile can see: [kv_begin, kv_end). With a sliding window the first row
+  // of the tile sees nothing before q0 + delta - W + 1, so the tiles before the one holding
+  // that key are never loaded; pipeline tile t holds keys kbase + 64 t ...
   int kv_end = 0;
   if (q0 < n_q) {
     kv_end = n_kv;
@@ -165,7 +168,9 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
     kv_end = max(kv_end, 0);
   }
   kv_end = __builtin_amdgcn_readfirstlane(kv_end);  // uniform: keeps load setup in SGPRs
-  const int ntk = (kv_end + C::BN - 1) / C::BN;
+  const int kbase = __builtin_amdgcn_readfirstlane(
+      a.window > 0 ? (max(q0 + delta - a.window + 1, 0) / C::BN) * C::BN : 0);
+  const int ntk = max((kv_end - kbase + C::BN - 1) / C::BN, 0);
 
   const IT* __restrict__ qp = static_cast<const IT*>(a.q) + (size_t)(b * a.H + h) * a.Lq * D;
   const IT* __restrict__ kp = uniform_ptr(static_cast<const IT*>(a.k) + (size_t)(b * a.Hkv + kvh) * a.Lk * D);
@@ -237,7 +242,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
   // buffers start zeroed and only ever hold input rows). fp32 input: rows past kv_end read
   // row kv_end - 1 instead.
   auto stage = [&](int t, int which, int slot) {
-    const int k0 = t * C::BN;
+    const int k0 = kbase + t * C::BN;
     char* dst = smem + slot;
     const IT* src = which ? vp : kp;
     if constexpr (sizeof(IT) == 2) {
@@ -293,17 +298,23 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
   // Mask of tile t (uniform branch; only boundary tiles). Accumulator element r of half kb
   // is key k0 + 4*half + (32*kb + 8*(r/4) + r%4) for query my_q[qb].
   auto mask_tile = [&](int t, f32x16 (&sx)[QB][2]) {
-    const int k0 = t * C::BN;
-    if (!((k0 + C::BN > n_kv) || (a.causal && k0 + C::BN - 1 > qw0 + delta))) return;  // uniform
+    const int k0 = kbase + t * C::BN;
+    if (!((k0 + C::BN > n_kv) || (a.causal && k0 + C::BN - 1 > qw0 + delta) ||
+          (a.window > 0 && k0 < qw0 + 32 * QB + delta - a.window)))
+      return;  // uniform
     const int base = k0 + 4 * half;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
+      // visible: lo <= (offset from base) < lim
       const int lim = min(n_kv - base, a.causal ? my_q[qb] + delta + 1 - base : n_kv - base);
+      const int lo = a.window > 0 ? my_q[qb] + delta - a.window + 1 - base : -C::BN;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (32 * kb + 8 * (r >> 2) + (r & 3) >= lim) sx[qb][kb][r] = kNegInf;
+        for (int r = 0; r < 16; ++r) {
+          const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
+          if (off >= lim || off < lo) sx[qb][kb][r] = kNegInf;
+        }
     }
   };
 
@@ -318,10 +329,8 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
 #pragma unroll
         for (int r = 0; r < 16; ++r) mp[r & 3] = fmaxf(mp[r & 3], sx[qb][kb][r]);
       float mx = fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
-      // lanes l and l ^ 32 hold the same row: exchange halves with v_permlane32_swap
-      const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, mx),
-                                                       __builtin_bit_cast(unsigned, mx), false, false);
-      m[qb] = fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1])) * a.scale_log2;
+      // lanes l and l ^ 32 hold the same row
+      m[qb] = max_of_halves(mx) * a.scale_log2;
       const float neg_m = (m[qb] == kNegInf) ? 0.f : -m[qb];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -385,11 +394,8 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
       for (int e = E0; e < E1; ++e)
         if (e / 32 == qb) mx = fmaxf(mx, elem(cu, e));
       // lanes l and l ^ 32 hold the same row: combine their halves
-      const auto sm = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, mx),
-                                                       __builtin_bit_cast(unsigned, mx), false, false);
-      mx = fmaxf(__builtin_bit_cast(float, sm[0]), __builtin_bit_cast(float, sm[1]));
-      const auto sn = __builtin_amdgcn_permlane32_swap((unsigned)need[qb], (unsigned)need[qb], false, false);
-      const bool row_need = (sn[0] | sn[1]) != 0u && mx != kNegInf;
+      mx = max_of_halves(mx);
+      const bool row_need = any_of_halves(need[qb]) && mx != kNegInf;
       float d = 0.f, al = 1.f;
       if (row_need) {
         const float base = (m[qb] == kNegInf) ? 0.f : m[qb];  // the scores were shifted by -base
@@ -644,6 +650,7 @@ hipError_t launch(const FwdParams& p, hipStream_t stream) {
   a.ntq = (p.Lq + C::BM - 1) / C::BM;
   a.scale_log2 = p.scale * kLog2e;
   a.causal = p.causal;
+  a.window = p.window;
   a.seqlens = p.seqlens;
   const long long nwg = (long long)a.ntq * p.B * p.H;
   if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;

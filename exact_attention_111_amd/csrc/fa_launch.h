@@ -17,6 +17,7 @@ struct FwdParams {
   int B, H, Hkv, Lq, Lk, d;
   float scale;
   int causal;
+  int window;  // sliding window W, 0 for none (needs causal)
   const int32_t* seqlens;
 };
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream);
@@ -33,6 +34,7 @@ struct DecodeParams {
   int B, H, Hkv, Lmax, d;
   float scale;
   const int32_t* ctx_lens;
+  int window;    // sliding window W, 0 for none
   float* ws_o;   // [B, H, nchunk, d]
   float* ws_ml;  // [B, H, nchunk, 2]
 };
@@ -54,6 +56,7 @@ struct BwdParams {
   int B, H, Hkv, Lq, Lk, d;
   float scale;
   int causal;
+  int window;  // sliding window W, 0 for none (needs causal)
   const int32_t* seqlens;
   float* ws;  // [B, H, Lq] x (exp2 offset, D) per query row
 };

@@ -70,6 +70,21 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  const int32_t* seqlens, void* stream);
 
 /*
+ * fa_fwd_sliding_window — fa_fwd with the causal mask cut to a sliding window:
+ * "FlashAttention 与长上下文：先分清三张账", in its section on prefill and decode,
+ * lists the sliding window among the methods that trim the context. Read here as
+ * the causal band of width `window`: key j is visible to query i iff
+ *     i + (Lk - Lq) - window < j <= i + (Lk - Lq)
+ * (and j < n_b with seqlens), so each query sees at most the `window` newest keys,
+ * its own position included. window >= 1 (else FA_ERR_INVALID); the mask is always
+ * causal. Key tiles wholly before a query tile's band are never read. Everything else
+ * (arguments, layouts, ownership, errors) is as for fa_fwd with causal = 1.
+ */
+fa_status fa_fwd_sliding_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int B, int H, int Hkv, int Lq, int Lk, int d, float scale, int window,
+                                const int32_t* seqlens, void* stream);
+
+/*
  * fa_fwd_f32 — the same contract with fp32 q, k, v and fp32 o. The kernel rounds
  * q, k, v to bf16 (round-to-nearest-even) as it loads them and multiplies them on the
  * bf16 matrix cores with fp32 accumulation; O and LSE are produced in fp32.
@@ -105,6 +120,17 @@ fa_status fa_decode(const void* q, const void* k_cache, const void* v_cache, voi
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * fa_decode_sliding_window — fa_decode with a sliding window (reading as for
+ * fa_fwd_sliding_window): request b attends to cache positions
+ * max(0, ctx_lens[b] - window) .. ctx_lens[b] - 1 only. Chunks wholly before that range
+ * are neither read nor merged. window >= 1, else FA_ERR_INVALID; the workspace is the
+ * same as fa_decode's.
+ */
+fa_status fa_decode_sliding_window(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                                   int B, int H, int Hkv, int Lmax, int d, float scale, const int32_t* ctx_lens,
+                                   int window, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * fa_bwd_workspace_bytes — bytes of device workspace fa_bwd needs: two fp32 per query row
  * (the row's LSE in base 2 and D = rowsum(dO * O)), i.e. B * H * Lq * 8. Returns 0 for
  * invalid sizes.
@@ -133,6 +159,15 @@ size_t fa_bwd_workspace_bytes(int B, int H, int Lq);
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                  void* dq, void* dk, void* dv, int B, int H, int Hkv, int Lq, int Lk, int d, float scale, int causal,
                  const int32_t* seqlens, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_bwd_sliding_window — gradients of fa_fwd_sliding_window (the same window, o and lse
+ * from that call); otherwise as fa_bwd with causal = 1. window >= 1, else FA_ERR_INVALID.
+ */
+fa_status fa_bwd_sliding_window(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                                const float* lse, void* dq, void* dk, void* dv, int B, int H, int Hkv, int Lq,
+                                int Lk, int d, float scale, int window, const int32_t* seqlens, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /* fa_status_string — a static, human-readable name for a status code. */
 const char* fa_status_string(fa_status s);

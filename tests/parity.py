@@ -55,3 +55,25 @@ def compare(o_gpu, lse_gpu, O_ref, LSE_ref, *, bf16_out: bool, what: str = ""):
     assert lerr <= LSE_MAX, f"{what}: LSE error {lerr:.3g} > {LSE_MAX}"
     stats.update(o_max=worst, o_mean=mean, lse_max=lerr, o_raw_max=float(err.max()))
     return stats
+
+
+# Gradients (fa_bwd): P and dS enter the products as bf16 (2^-9 relative rounding) with fp32
+# accumulation, and dQ, dK, dV are rounded to bf16, so each gradient is held relative to its
+# own size: max |err| <= 2^-5 max |ref| and mean |err| <= 2^-7 mean |ref|.
+G_MAX_REL = 2.0 ** -5
+G_MEAN_REL = 2.0 ** -7
+
+
+def compare_grad(got, ref, what, floor=1e-30):
+    """Assert gradient parity. ``floor``: the size below which a gradient counts as zero
+    (then the bound is absolute). Returns (max-rel, mean-rel)."""
+    got = got.detach().float().cpu().numpy().astype(np.float64) if torch.is_tensor(got) else np.asarray(got)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.isfinite(got).all(), f"{what}: non-finite values"
+    err = np.abs(got - ref)
+    mx = err.max() / max(np.abs(ref).max(), floor) if err.size else 0.0
+    mn = err.mean() / max(np.abs(ref).mean(), floor) if err.size else 0.0
+    print(f"  {what}: max|err|/max|ref| = {mx:.2e}, mean|err|/mean|ref| = {mn:.2e}", flush=True)
+    assert mx <= G_MAX_REL and mn <= G_MEAN_REL, f"{what}: {mx:.3e} / {mn:.3e}"
+    return mx, mn

@@ -21,8 +21,10 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     L = fa.lib()
     names = _declared_functions()
-    assert set(names) == {"fa_fwd", "fa_fwd_f32", "fa_decode", "fa_decode_workspace_bytes", "fa_bwd",
-                          "fa_bwd_workspace_bytes", "fa_status_string"}
+    assert set(names) == {"fa_fwd", "fa_fwd_sliding_window", "fa_fwd_f32", "fa_decode", "fa_decode_sliding_window",
+                          "fa_decode_workspace_bytes", "fa_bwd", "fa_bwd_sliding_window", "fa_bwd_workspace_bytes",
+                          "fa_status_string"}
+    assert set(names) == set(fa.binding.SYMBOLS)
     for name in names:
         assert hasattr(L, name), name
 
@@ -134,3 +136,25 @@ def test_bwd_validation():
     assert call(ws_bytes=need - 4) == INV
     assert call(d=96) == UNS
     assert call(B=0) == 0  # empty: nothing to write, nothing enqueued
+
+
+def test_sliding_window_validation():
+    """window < 1 is rejected by all three sliding-window entry points; everything else is
+    validated as for the plain entry points."""
+    L = fa.lib()
+    INV = fa.binding.FA_ERR_INVALID
+    for w in (0, -3):
+        assert _fwd(causal=w, fn="fa_fwd_sliding_window") == INV
+    assert _fwd(causal=4, fn="fa_fwd_sliding_window", H=3, Hkv=2) == INV  # H % Hkv
+    assert _fwd(causal=4, fn="fa_fwd_sliding_window", d=96) == fa.binding.FA_ERR_UNSUPPORTED
+    assert _fwd(causal=4, fn="fa_fwd_sliding_window", B=0) == fa.binding.FA_OK  # empty call, nothing enqueued
+    need = L.fa_decode_workspace_bytes(2, 4, 100, 128)
+    for w in (0, -1):
+        assert L.fa_decode_sliding_window(A, A, A, A2, A2, 2, 4, 2, 100, 128, 0.1, A, w, A2, need, None) == INV
+    assert L.fa_decode_sliding_window(A, A, A, A2, A2, 2, 4, 2, 100, 128, 0.1, A, 8, A2, need - 1, None) == INV
+    bneed = L.fa_bwd_workspace_bytes(2, 4, 100)
+    for w in (0, -2):
+        assert L.fa_bwd_sliding_window(A, A, A, A, A, A, A2, A2, A2, 2, 4, 2, 100, 100, 128, 0.1, w, None, A2, bneed,
+                                       None) == INV
+    assert L.fa_bwd_sliding_window(A, A, A, A, A, A, A2, A2, A2, 2, 4, 2, 100, 100, 128, 0.1, 5, None, A2,
+                                   bneed - 1, None) == INV

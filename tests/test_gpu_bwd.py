@@ -1,11 +1,11 @@
 """GPU parity of fa_bwd against the fp64 backward oracle (through the C ABI).
 
-Gradients have no tolerance of their own on the pages; the bound used here comes from the
-arithmetic of the kernels: P and dS enter the products as bf16 (relative rounding 2^-9 per
-element) with fp32 accumulation, and dQ, dK, dV are rounded to bf16 (2^-9). Errors are
-therefore judged relative to the size of each gradient: max |err| <= 2^-5 max |ref| and
-mean |err| <= 2^-7 mean |ref| (several bf16 ulps of headroom; the measured values are a fifth
-to a third of those bounds).
+Gradients have no tolerance of their own on the pages; the bound (``parity.compare_grad``)
+comes from the arithmetic of the kernels: P and dS enter the products as bf16 (relative
+rounding 2^-9 per element) with fp32 accumulation, and dQ, dK, dV are rounded to bf16
+(2^-9). Errors are therefore judged relative to the size of each gradient: max |err| <=
+2^-5 max |ref| and mean |err| <= 2^-7 mean |ref| (several bf16 ulps of headroom; the
+measured values are a fifth to a third of those bounds).
 """
 import math
 import sys
@@ -17,12 +17,11 @@ import torch
 import fa_inputs
 import oracle
 from oracle.attention import attention_head
+from parity import compare_grad as _close
 
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
-MAX_REL = 2.0 ** -5
-MEAN_REL = 2.0 ** -7
 
 
 def _fa():
@@ -33,18 +32,6 @@ def _fa():
 def announce(**case):
     print("\n[case] " + " ".join(f"{k}={v}" for k, v in case.items()), flush=True)
     sys.stdout.flush()
-
-
-def _close(got, ref, what, floor=1e-30):
-    """``floor``: the size below which a gradient counts as zero (then the bound is absolute)."""
-    got = got.float().cpu().numpy().astype(np.float64)
-    err = np.abs(got - ref)
-    scale_max = max(np.abs(ref).max(), floor)
-    scale_mean = max(np.abs(ref).mean(), floor)
-    mx, mn = err.max() / scale_max, err.mean() / scale_mean
-    print(f"  {what}: max|err|/max|ref| = {mx:.2e}, mean|err|/mean|ref| = {mn:.2e}", flush=True)
-    assert np.isfinite(got).all(), f"{what}: non-finite values"
-    assert mx <= MAX_REL and mn <= MEAN_REL, f"{what}: {mx:.3e} / {mn:.3e}"
 
 
 def _dout(shape, seed):
