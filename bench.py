@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--window", type=int, default=None,
+                    help="with --only: a sliding window of this many keys (prefill, backward and decode workloads); "
+                         "work is counted over the keys inside the window")
     ap.add_argument("--only", default=None,
                     help="time one part alone (for profiling): prefill, decode, backward, copy, any workload name of "
                          "fa_inputs.WORKLOADS, or backward:<prefill workload>; prints a short JSON line "
@@ -127,7 +130,18 @@ def cpu_baseline(w, x, seconds):
             "seconds": round(dt, 2)}
 
 
-def run_only(part, steps, warmup):
+def _window_pairs(lens, W):
+    """Visible (query, key) pairs of causal self-attention with a window of W keys per query,
+    summed over sequences of the given lengths: sum over i < n of min(W, i + 1)."""
+    tot = 0
+    for n in lens:
+        n = int(n)
+        m = min(n, W)
+        tot += m * (m + 1) // 2 + (n - m) * W
+    return float(tot)
+
+
+def run_only(part, steps, warmup, window=None):
     """Time one part alone (for profiling): the prefill or decode part of the step, a plain
     1 GiB device copy, or any named workload. Prints the kernel time and, for workloads,
     the algorithmic rate (prefill: TFLOP/s over visible pairs as in the metric; decode: K/V
@@ -145,15 +159,17 @@ def run_only(part, steps, warmup):
             raise SystemExit(f"no backward for {w.name}")
         x = fa_inputs.workload_inputs(w, device=dev)
         sl = x.get("seqlens")
-        o, lse = fa.fwd(x["q"], x["k"], x["v"], causal=w.causal, scale=w.scale, seqlens=sl)
+        o, lse = fa.fwd(x["q"], x["k"], x["v"], causal=w.causal, scale=w.scale, seqlens=sl, window=window)
         g = torch.Generator(device=dev).manual_seed(w.seed + 1000)
         do = torch.randn(o.shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
         ws = torch.empty(max(16, fa.bwd_workspace_bytes(w.B, w.H, w.L)), dtype=torch.uint8, device=dev)
         dq, dk, dv = torch.empty_like(x["q"]), torch.empty_like(x["k"]), torch.empty_like(x["v"])
         fn = lambda: fa.bwd(x["q"], x["k"], x["v"], o, do, lse, causal=w.causal, scale=w.scale,  # noqa: E731
-                            seqlens=sl, workspace=ws, dq=dq, dk=dk, dv=dv)
+                            seqlens=sl, workspace=ws, dq=dq, dk=dk, dv=dv, window=window)
         lens = x["seqlens_cpu"].to(torch.float64) if sl is not None else torch.full((w.B,), float(w.L))
         pairs = float((lens * lens).sum()) * (0.5 if w.causal else 1.0)
+        if window is not None:
+            pairs = _window_pairs(lens.tolist(), window)
         rate = (BWD_FLOP_PER_FWD * 4.0 * w.H * w.d * pairs, "TFLOP/s")
     elif name == "copy":  # a plain copy of 1 GiB: reads 1 GiB and writes 1 GiB per launch
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
@@ -167,16 +183,21 @@ def run_only(part, steps, warmup):
             lse = torch.empty((w.B, w.H), dtype=torch.float32, device=dev)
             ws = torch.empty(max(16, fa.decode_workspace_bytes(w.B, w.H, w.L, w.d)), dtype=torch.uint8, device=dev)
             fn = lambda: fa.decode(x["q"], x["k_cache"], x["v_cache"], x["ctx_lens"], scale=w.scale,  # noqa: E731
-                                   workspace=ws, out=o, lse=lse)
-            work, unit = float(2 * w.Hkv * w.d * 2 * int(x["ctx_lens_cpu"].to(torch.int64).sum())), "GB/s"
+                                   workspace=ws, out=o, lse=lse, window=window)
+            ctx = x["ctx_lens_cpu"].to(torch.int64)
+            if window is not None:
+                ctx = ctx.clamp(max=window)
+            work, unit = float(2 * w.Hkv * w.d * 2 * int(ctx.sum())), "GB/s"
         else:
             o = torch.empty_like(x["q"])
             lse = torch.empty((w.B, w.H, w.L), dtype=torch.float32, device=dev)
             sl = x.get("seqlens")
             fn = lambda: fa.fwd(x["q"], x["k"], x["v"], causal=w.causal, scale=w.scale, seqlens=sl,  # noqa: E731
-                                out=o, lse=lse)
+                                out=o, lse=lse, window=window)
             lens = x["seqlens_cpu"].to(torch.float64) if sl is not None else torch.full((w.B,), float(w.L))
             pairs = float((lens * lens).sum()) * (0.5 if w.causal else 1.0)
+            if window is not None:
+                pairs = _window_pairs(lens.tolist(), window)
             work, unit = 4.0 * w.H * w.d * pairs, "TFLOP/s"
         rate = (work, unit)
     else:
@@ -189,7 +210,7 @@ def run_only(part, steps, warmup):
         a.record(); fn(); b.record()
     torch.cuda.synchronize()
     ms = sorted(a.elapsed_time(b) for a, b in ev)
-    line = {"only": name, "steps": steps, "ms_avg": sum(ms) / len(ms), "ms_min": ms[0], "ms_median": ms[len(ms) // 2]}
+    line = {"only": name, "window": window, "steps": steps, "ms_avg": sum(ms) / len(ms), "ms_min": ms[0], "ms_median": ms[len(ms) // 2]}
     if rate is not None:
         work, unit = rate
         scale = 1e12 if unit == "TFLOP/s" else 1e9
@@ -203,7 +224,7 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only; run with --gpus 1"}))
         sys.exit(2)
     if args.only:
-        run_only(args.only, args.steps, args.warmup)
+        run_only(args.only, args.steps, args.warmup, args.window)
         return
     import torch
 
