@@ -127,6 +127,26 @@ def decode_inputs(B, H, Hkv, Lmax, d, *, seed, device="cpu", len_range=(1, None)
     return {"q": q, "k_cache": kc, "v_cache": vc, "ctx_lens": ctx.to(device), "ctx_lens_cpu": ctx}
 
 
+def paged_decode_inputs(B, H, Hkv, Lmax, d, page_size, *, seed, device="cpu", len_range=(1, None), spare_pages=3):
+    """Decode inputs with the KV cache in pages: pools k_pages, v_pages [num_pages, Hkv, P, d]
+    (bf16) and an int32 block table [B, ceil(Lmax / P)] whose entries are a random
+    permutation of the pool's pages (scattered, as an allocator leaves them after churn),
+    plus ``spare_pages`` pages that no table row names. Context lengths as decode_inputs."""
+    lo, hi = len_range
+    hi = Lmax if hi is None else hi
+    ctx = draw_lengths(B, lo, hi, seed)
+    max_pages = (Lmax + page_size - 1) // page_size
+    num_pages = B * max_pages + spare_pages
+    g = torch.Generator(device="cpu").manual_seed(seed + 2)
+    table = torch.randperm(num_pages, generator=g)[:B * max_pages].reshape(B, max_pages).to(torch.int32)
+    gen = torch.Generator(device=device).manual_seed(seed + 1)
+    q = _normal_bf16((B, H, d), gen, device)
+    kp = _normal_bf16((num_pages, Hkv, page_size, d), gen, device)
+    vp = _normal_bf16((num_pages, Hkv, page_size, d), gen, device)
+    return {"q": q, "k_pages": kp, "v_pages": vp, "block_table": table.to(device), "block_table_cpu": table,
+            "ctx_lens": ctx.to(device), "ctx_lens_cpu": ctx, "page_size": page_size, "num_pages": num_pages}
+
+
 def workload_inputs(w: Workload, device="cpu"):
     """Inputs for a named workload at its full size."""
     if w.kind == "prefill":

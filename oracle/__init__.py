@@ -4,6 +4,6 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s ``cpu_baseline``
 leg may import this package. The product (the HIP library and its Python
 binding) never does.
 """
-from .attention import (attention, attention_head, decode, merge, online_softmax_rows,  # noqa: F401
-                        part_state)
+from .attention import (attention, attention_head, decode, decode_paged, merge,  # noqa: F401
+                        online_softmax_rows, part_state)
 from .backward import attention_backward, attention_backward_head  # noqa: F401

@@ -152,6 +152,32 @@ def decode(q, k_cache, v_cache, ctx_lens, *, scale, heads=None, window=None):
     return O, LSE
 
 
+def decode_paged(q, k_pages, v_pages, block_table, ctx_lens, *, page_size, scale, heads=None, window=None):
+    """Decode against a paged KV cache (PagedAttention's layout, "FlashAttention 与长上下文",
+    prefill/decode section, which names paged KV allocation without fixing a layout).
+
+    k_pages, v_pages: [num_pages, Hkv, P, d]; block_table: int [B, max_pages]. Cache
+    position j of request b is row j % P of page block_table[b, j // P]. The pages of a
+    request are gathered into one contiguous cache and decoded as ``decode`` does.
+    Returns (O [B, H, d], LSE [B, H]).
+    """
+    B, H, d = q.shape
+    Hkv = k_pages.shape[1]
+    group = H // Hkv
+    O = np.full((B, H, d), np.nan)
+    LSE = np.full((B, H), np.nan)
+    pairs = [(b, h) for b in range(B) for h in range(H)] if heads is None else heads
+    for b, h in pairs:
+        n = int(ctx_lens[b])
+        kvh = h // group
+        pages = [int(p) for p in block_table[b, :(n + page_size - 1) // page_size]]
+        K = np.concatenate([k_pages[p, kvh] for p in pages], axis=0)[:n] if pages else np.zeros((0, d))
+        V = np.concatenate([v_pages[p, kvh] for p in pages], axis=0)[:n] if pages else np.zeros((0, d))
+        o, lse = attention_head(q[b, h][None, :], K, V, scale=scale, causal=window is not None, window=window)
+        O[b, h], LSE[b, h] = o[0], lse[0]
+    return O, LSE
+
+
 def online_softmax_rows(S, V, block):
     """Blockwise (online) softmax-times-V of one score row, in the pages' order.
 
