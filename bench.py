@@ -56,6 +56,9 @@ def parse():
     ap.add_argument("--window", type=int, default=None,
                     help="with --only: a sliding window of this many keys (prefill, backward and decode workloads); "
                          "work is counted over the keys inside the window")
+    ap.add_argument("--page", type=int, default=None,
+                    help="with --only and a decode workload: the KV cache in pages of this many positions, "
+                         "scattered through a pool by a random block table (fa_decode_paged)")
     ap.add_argument("--only", default=None,
                     help="time one part alone (for profiling): prefill, decode, backward, copy, any workload name of "
                          "fa_inputs.WORKLOADS, or backward:<prefill workload>; prints a short JSON line "
@@ -141,7 +144,7 @@ def _window_pairs(lens, W):
     return float(tot)
 
 
-def run_only(part, steps, warmup, window=None):
+def run_only(part, steps, warmup, window=None, page=None):
     """Time one part alone (for profiling): the prefill or decode part of the step, a plain
     1 GiB device copy, or any named workload. Prints the kernel time and, for workloads,
     the algorithmic rate (prefill: TFLOP/s over visible pairs as in the metric; decode: K/V
@@ -177,8 +180,23 @@ def run_only(part, steps, warmup, window=None):
         fn = lambda: dst.copy_(src)  # noqa: E731
     elif name in fa_inputs.WORKLOADS:
         w = fa_inputs.WORKLOADS[name]
-        x = fa_inputs.workload_inputs(w, device=dev)
-        if w.kind == "decode":
+        if w.kind == "decode" and page is not None:
+            x = fa_inputs.paged_decode_inputs(w.B, w.H, w.Hkv, w.L, w.d, page, seed=w.seed, device=dev,
+                                              len_range=w.len_range)
+        else:
+            x = fa_inputs.workload_inputs(w, device=dev)
+        if w.kind == "decode" and page is not None:
+            o = torch.empty_like(x["q"])
+            lse = torch.empty((w.B, w.H), dtype=torch.float32, device=dev)
+            cap = x["block_table"].shape[1] * page
+            ws = torch.empty(max(16, fa.decode_workspace_bytes(w.B, w.H, cap, w.d)), dtype=torch.uint8, device=dev)
+            fn = lambda: fa.decode_paged(x["q"], x["k_pages"], x["v_pages"], x["block_table"],  # noqa: E731
+                                         x["ctx_lens"], scale=w.scale, window=window, workspace=ws, out=o, lse=lse)
+            ctx = x["ctx_lens_cpu"].to(torch.int64)
+            if window is not None:
+                ctx = ctx.clamp(max=window)
+            work, unit = float(2 * w.Hkv * w.d * 2 * int(ctx.sum())), "GB/s"
+        elif w.kind == "decode":
             o = torch.empty_like(x["q"])
             lse = torch.empty((w.B, w.H), dtype=torch.float32, device=dev)
             ws = torch.empty(max(16, fa.decode_workspace_bytes(w.B, w.H, w.L, w.d)), dtype=torch.uint8, device=dev)
@@ -210,7 +228,7 @@ def run_only(part, steps, warmup, window=None):
         a.record(); fn(); b.record()
     torch.cuda.synchronize()
     ms = sorted(a.elapsed_time(b) for a, b in ev)
-    line = {"only": name, "window": window, "steps": steps, "ms_avg": sum(ms) / len(ms), "ms_min": ms[0], "ms_median": ms[len(ms) // 2]}
+    line = {"only": name, "window": window, "page": page, "steps": steps, "ms_avg": sum(ms) / len(ms), "ms_min": ms[0], "ms_median": ms[len(ms) // 2]}
     if rate is not None:
         work, unit = rate
         scale = 1e12 if unit == "TFLOP/s" else 1e9
@@ -224,7 +242,7 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only; run with --gpus 1"}))
         sys.exit(2)
     if args.only:
-        run_only(args.only, args.steps, args.warmup, args.window)
+        run_only(args.only, args.steps, args.warmup, args.window, args.page)
         return
     import torch
 

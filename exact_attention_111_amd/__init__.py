@@ -1,10 +1,12 @@
 """exact_attention_111_amd — exact scaled-dot-product attention for AMD MI355X (gfx950).
 
-FlashAttention-style prefill (``fwd``), its gradients (``bwd``) and split-K decode (``decode``) run in
+FlashAttention-style prefill (``fwd``), its gradients (``bwd``) and split-K decode (``decode``, and
+``decode_paged`` for a paged KV cache) run in
 hand-written HIP kernels behind the C ABI of ``libfa.so`` (``include/fa.h``); this
 package only marshals arguments to it.
 """
-from .binding import (FaError, bwd, bwd_workspace_bytes, decode, decode_workspace_bytes, fwd, lib,  # noqa: F401
-                      status_string)
+from .binding import (FaError, bwd, bwd_workspace_bytes, decode, decode_paged, decode_workspace_bytes,  # noqa: F401
+                      fwd, lib, status_string)
 
-__all__ = ["fwd", "bwd", "bwd_workspace_bytes", "decode", "decode_workspace_bytes", "FaError", "lib", "status_string"]
+__all__ = ["fwd", "bwd", "bwd_workspace_bytes", "decode", "decode_paged", "decode_workspace_bytes", "FaError", "lib",
+           "status_string"]

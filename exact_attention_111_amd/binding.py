@@ -15,7 +15,7 @@ import torch
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
 FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
-SYMBOLS = ("fa_fwd", "fa_fwd_sliding_window", "fa_fwd_f32", "fa_decode", "fa_decode_sliding_window",
+SYMBOLS = ("fa_fwd", "fa_fwd_sliding_window", "fa_fwd_f32", "fa_decode", "fa_decode_sliding_window", "fa_decode_paged",
            "fa_decode_workspace_bytes", "fa_bwd", "fa_bwd_sliding_window", "fa_bwd_workspace_bytes",
            "fa_status_string")
 
@@ -55,6 +55,9 @@ def lib() -> ctypes.CDLL:
     L.fa_decode_sliding_window.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, vp, i32, vp,
                                            ctypes.c_size_t, vp]
     L.fa_decode_sliding_window.restype = i32
+    L.fa_decode_paged.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, i32, vp, i32, vp, i32, vp,
+                                  ctypes.c_size_t, vp]
+    L.fa_decode_paged.restype = i32
     L.fa_bwd_workspace_bytes.argtypes = [i32, i32, i32]
     L.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
     L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp, vp,
@@ -162,6 +165,40 @@ def decode(q, k_cache, v_cache, ctx_lens, *, scale: float | None = None, workspa
                                             Lmax, d, float(scale), _ptr(ctx_lens), int(window), _ptr(workspace), wsb,
                                             _stream(q.device))
         _check(st, "fa_decode_sliding_window")
+    return out, lse
+
+
+def decode_paged(q, k_pages, v_pages, block_table, ctx_lens, *, scale: float | None = None, window: int | None = None,
+                 workspace=None, out=None, lse=None):
+    """Single-token decode against a paged cache through ``fa_decode_paged``.
+
+    q: [B, H, d] bf16; k_pages, v_pages: [num_pages, Hkv, P, d] bf16; block_table: int32
+    [B, max_pages]; ctx_lens: int32 [B]. Returns (o [B, H, d] bf16, lse [B, H] fp32).
+    """
+    B, H, d = q.shape
+    num_pages, Hkv, P = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
+    max_pages = block_table.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    need = decode_workspace_bytes(B, H, max_pages * P, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    for t in (q, k_pages, v_pages, block_table, out, lse, ctx_lens, workspace):
+        if not t.is_contiguous():
+            raise ValueError("libfa needs contiguous tensors")
+    if not (q.dtype == k_pages.dtype == v_pages.dtype == out.dtype == torch.bfloat16):
+        raise ValueError("decode_paged needs bfloat16 q, pages and out")
+    if ctx_lens.dtype != torch.int32 or block_table.dtype != torch.int32:
+        raise ValueError("ctx_lens and block_table must be int32")
+    st = lib().fa_decode_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(out), _ptr(lse), B, H, Hkv, d,
+                               float(scale), P, num_pages, _ptr(block_table), max_pages, _ptr(ctx_lens),
+                               0 if window is None else int(window), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _stream(q.device))
+    _check(st, "fa_decode_paged")
     return out, lse
 
 

@@ -78,17 +78,17 @@ fa_status fwd_bf16(const void* q, const void* k, const void* v, void* o, float* 
   return fa::launch_fwd_bf16(p, static_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-fa_status decode_impl(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse, int B, int H,
-                      int Hkv, int Lmax, int d, float scale, const int32_t* ctx_lens, int window, void* workspace,
-                      size_t workspace_bytes, void* stream) {
-  const fa_status s = validate_decode(q, k_cache, v_cache, o, lse, B, H, Hkv, Lmax, d, scale, ctx_lens, workspace,
-                                      workspace_bytes);
-  if (s != FA_OK) return s;
+// Launch of the decode kernels after validation. Paged calls pass the block table and the
+// page geometry (Lmax = max_pages * page_size); contiguous ones pass table == nullptr.
+fa_status decode_run(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv,
+                     int Lmax, int d, float scale, const int32_t* ctx_lens, int window, const int32_t* table,
+                     int page_size, int max_pages, int num_pages, void* workspace, void* stream) {
   if (B == 0 || H == 0) return FA_OK;
   const size_t nc = (size_t)fa::decode_num_chunks(Lmax);
   float* ws_o = static_cast<float*>(workspace);
   float* ws_ml = ws_o + (size_t)B * H * nc * d;
-  fa::DecodeParams p{q, k_cache, v_cache, o, lse, B, H, Hkv, Lmax, d, scale, ctx_lens, window, ws_o, ws_ml};
+  fa::DecodeParams p{q, k, v, o, lse, B, H, Hkv, Lmax, d, scale, ctx_lens, window, table, page_size, max_pages,
+                     num_pages, ws_o, ws_ml};
   return fa::launch_decode(p, static_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -139,16 +139,46 @@ size_t fa_decode_workspace_bytes(int B, int H, int Lmax, int d) {
 fa_status fa_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse, int B, int H,
                     int Hkv, int Lmax, int d, float scale, const int32_t* ctx_lens, void* workspace,
                     size_t workspace_bytes, void* stream) {
-  return decode_impl(q, k_cache, v_cache, o, lse, B, H, Hkv, Lmax, d, scale, ctx_lens, 0, workspace, workspace_bytes,
-                     stream);
+  const fa_status s = validate_decode(q, k_cache, v_cache, o, lse, B, H, Hkv, Lmax, d, scale, ctx_lens, workspace,
+                                      workspace_bytes);
+  if (s != FA_OK) return s;
+  return decode_run(q, k_cache, v_cache, o, lse, B, H, Hkv, Lmax, d, scale, ctx_lens, 0, nullptr, 0, 0, 0, workspace,
+                    stream);
 }
 
 fa_status fa_decode_sliding_window(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
                                    int B, int H, int Hkv, int Lmax, int d, float scale, const int32_t* ctx_lens,
                                    int window, void* workspace, size_t workspace_bytes, void* stream) {
   if (window < 1) return FA_ERR_INVALID;
-  return decode_impl(q, k_cache, v_cache, o, lse, B, H, Hkv, Lmax, d, scale, ctx_lens, window, workspace,
-                     workspace_bytes, stream);
+  const fa_status s = validate_decode(q, k_cache, v_cache, o, lse, B, H, Hkv, Lmax, d, scale, ctx_lens, workspace,
+                                      workspace_bytes);
+  if (s != FA_OK) return s;
+  return decode_run(q, k_cache, v_cache, o, lse, B, H, Hkv, Lmax, d, scale, ctx_lens, window, nullptr, 0, 0, 0,
+                    workspace, stream);
+}
+
+fa_status fa_decode_paged(const void* q, const void* k_pages, const void* v_pages, void* o, float* lse, int B, int H,
+                          int Hkv, int d, float scale, int page_size, int num_pages, const int32_t* block_table,
+                          int max_pages, const int32_t* ctx_lens, int window, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  if (page_size < 1 || (page_size & (page_size - 1)) != 0 || max_pages < 0 || num_pages < 0 || window < 0)
+    return FA_ERR_INVALID;
+  if ((long long)max_pages * page_size > 0x7fffffffLL) return FA_ERR_INVALID;
+  const int Lmax = max_pages * page_size;
+  // q, o, lse, ctx_lens, sizes and the workspace as for fa_decode (caches checked below)
+  fa_status s = validate_decode(q, nullptr, nullptr, o, lse, B, H, Hkv, 0, d, scale, ctx_lens, workspace,
+                                workspace_bytes);
+  if (s == FA_ERR_INVALID) return s;
+  const size_t need = fa_decode_workspace_bytes(B, H, Lmax, d);
+  if (need > 0 && (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need)) return FA_ERR_INVALID;
+  const long long npool = (long long)num_pages * Hkv * page_size * d;
+  if (!tensor_ok(k_pages, npool) || !tensor_ok(v_pages, npool)) return FA_ERR_INVALID;
+  if (B > 0 && (num_pages < 1 || block_table == nullptr || (reinterpret_cast<uintptr_t>(block_table) & 3u) != 0))
+    return FA_ERR_INVALID;
+  if (s != FA_OK) return s;
+  if (page_size < 16) return FA_ERR_UNSUPPORTED;  // a 16-key half step must lie in one page
+  return decode_run(q, k_pages, v_pages, o, lse, B, H, Hkv, Lmax, d, scale, ctx_lens, window, block_table,
+                    page_size, max_pages, num_pages, workspace, stream);
 }
 
 size_t fa_bwd_workspace_bytes(int B, int H, int Lq) {

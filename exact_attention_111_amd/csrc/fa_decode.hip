@@ -23,6 +23,11 @@
 //     keeping it in the caches only evicts lines that are still wanted (measured: +4-7%).
 //   * Chunks are 2048 keys: long enough that the exposed latency of a workgroup's first
 //     load is amortised, short enough that a 32k context still spreads over 16 workgroups.
+//   * Paged cache (PagedAttention's layout, which the same page names): position j of a
+//     request is row j % P of page table[j / P] of a pool [pages, Hkv, P, d]. With P a power
+//     of two >= 16, each 16-key half of a step lies in one page. A workgroup loads its
+//     chunk's page numbers once (two per lane, at most 128 pages) and takes each step's page
+//     with a uniform readlane, so the K/V loads stay 16-byte row loads.
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -45,11 +50,15 @@ struct DecArgs {
   float scale_log2;
   int window;  // sliding window W (0: none): the last W keys of the context
   const int32_t* ctx;
+  const int32_t* table;  // paged cache: [B, max_pages] page of each P-key span
+  int page_shift;        // log2(P)
+  int max_pages;
+  int num_pages;
   float* ws_o;
   float* ws_ml;
 };
 
-template <int D>
+template <int D, bool PAGED>
 __global__ __launch_bounds__(64) void decode_split_kernel(const DecArgs a) {
   constexpr int NCH = D / 8;            // 16-byte chunks per row
   constexpr int VKPL = 64 / NCH;        // keys per V load instruction
@@ -77,9 +86,27 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecArgs a) {
   const int h0 = kvh * a.group + sg * kHeadsPerPass;
   const int nh = min(kHeadsPerPass, a.group - sg * kHeadsPerPass);
 
-  const size_t kv_off = (size_t)(b * a.Hkv + kvh) * a.Lmax * D;
-  const __bf16* __restrict__ kp = a.k + kv_off;
-  const __bf16* __restrict__ vp = a.v + kv_off;
+  // Rows of the 16 keys from kb0 (a multiple of 16): contiguous cache, or the page that
+  // holds them. Paged: this lane holds page numbers first + lane and first + 64 + lane of the
+  // chunk (clamped into the pool, so a bad table cannot address outside it).
+  int pg_lo = 0, pg_hi = 0, first = 0;
+  if constexpr (PAGED) {
+    first = c0 >> a.page_shift;
+    const int npc = max(kDecodeChunk >> a.page_shift, 1);  // pages per chunk, <= 128
+    const int32_t* row = a.table + (size_t)b * a.max_pages;
+    if (lane < npc && first + lane < a.max_pages) pg_lo = min(max(row[first + lane], 0), a.num_pages - 1);
+    if (64 + lane < npc && first + 64 + lane < a.max_pages) pg_hi = min(max(row[first + 64 + lane], 0), a.num_pages - 1);
+  }
+  auto rows_at = [&](const __bf16* base, int kb0) -> const __bf16* {
+    if constexpr (PAGED) {
+      const int cp = (kb0 >> a.page_shift) - first;  // chunk-relative page, uniform
+      const int page = cp < 64 ? __builtin_amdgcn_readlane(pg_lo, cp) : __builtin_amdgcn_readlane(pg_hi, cp - 64);
+      const int in_page = kb0 & ((1 << a.page_shift) - 1);
+      return base + ((size_t)(page * a.Hkv + kvh) * ((size_t)1 << a.page_shift) + in_page) * D;
+    } else {
+      return base + ((size_t)(b * a.Hkv + kvh) * a.Lmax + kb0) * D;
+    }
+  };
 
   // A operand: row r = lane % 16 is head slot r % 4; element t of k-step s is d = 32 s + 8 (lane / 16) + t.
   const int slot_a = (lane & 15) & 3;
@@ -97,21 +124,27 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecArgs a) {
   const int vch = lane - vkey * NCH;
   u32x4 kr[2][QS], vr[VLOADS];
   auto load_step = [&](int k0) {
+    const __bf16* kb[2] = {rows_at(a.k, k0), rows_at(a.k, k0 + 16)};
+    const __bf16* vb[2] = {rows_at(a.v, k0), rows_at(a.v, k0 + 16)};
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       const int key = k0 + 16 * blk + (lane & 15);
 #pragma unroll
       for (int s = 0; s < QS; ++s) {
         u32x4 u = {0u, 0u, 0u, 0u};
-        if (key < c1 && key >= w0) u = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + (size_t)key * D + 32 * s + 8 * (lane >> 4)));
+        if (key < c1 && key >= w0)
+          u = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x4*>(kb[blk] + (size_t)(lane & 15) * D + 32 * s + 8 * (lane >> 4)));
         kr[blk][s] = u;
       }
     }
 #pragma unroll
     for (int i = 0; i < VLOADS; ++i) {
-      const int key = k0 + i * VKPL + vkey;
+      const int off = i * VKPL + vkey;  // key offset within the step
+      const int key = k0 + off;
       u32x4 u = {0u, 0u, 0u, 0u};
-      if (key < c1 && key >= w0) u = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + (size_t)key * D + 8 * vch));
+      if (key < c1 && key >= w0)
+        u = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb[off >> 4] + (size_t)(off & 15) * D + 8 * vch));
       vr[i] = u;
     }
   };
@@ -250,7 +283,7 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const DecArgs a) {
   if (lane == 0) a.lse[bh] = ok ? (M + __log2f(L)) * kLn2 : kNegInf;
 }
 
-template <int D>
+template <int D, bool PAGED>
 hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
   DecArgs a;
   a.q = static_cast<const __bf16*>(p.q);
@@ -265,6 +298,11 @@ hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
   a.scale_log2 = p.scale * kLog2e;
   a.ctx = p.ctx_lens;
   a.window = p.window;
+  a.table = p.table;
+  a.page_shift = 0;
+  while (PAGED && (1 << a.page_shift) < p.page_size) ++a.page_shift;
+  a.max_pages = p.max_pages;
+  a.num_pages = p.num_pages;
   a.ws_o = p.ws_o;
   a.ws_ml = p.ws_ml;
   void* args[] = {&a};
@@ -272,7 +310,7 @@ hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
   if (a.nchunk > 0) {
     const long long nx = (long long)p.B * p.Hkv * a.nsg;
     if (nx > 0x7fffffffLL || a.nchunk > 65535) return hipErrorInvalidConfiguration;
-    e = hipLaunchKernel(reinterpret_cast<const void*>(&decode_split_kernel<D>), dim3((unsigned)nx, a.nchunk),
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&decode_split_kernel<D, PAGED>), dim3((unsigned)nx, a.nchunk),
                         dim3(64), args, 0, stream);
     if (e != hipSuccess) return e;
   }
@@ -285,8 +323,8 @@ hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
-  if (p.d == 64) return launch_d<64>(p, stream);
-  return launch_d<128>(p, stream);
+  if (p.table != nullptr) return p.d == 64 ? launch_d<64, true>(p, stream) : launch_d<128, true>(p, stream);
+  return p.d == 64 ? launch_d<64, false>(p, stream) : launch_d<128, false>(p, stream);
 }
 
 }  // namespace fa

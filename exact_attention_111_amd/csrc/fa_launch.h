@@ -25,6 +25,8 @@ hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
 
 // Decode: split kernel over key chunks, then the combine kernel.
 constexpr int kDecodeChunk = 2048;  // keys per split partial
+// Paged cache: k and v are pools [num_pages, Hkv, page_size, d], table is int32
+// [B, max_pages] and Lmax = max_pages * page_size; table == nullptr for a contiguous cache.
 struct DecodeParams {
   const void* q;
   const void* k;
@@ -35,6 +37,8 @@ struct DecodeParams {
   float scale;
   const int32_t* ctx_lens;
   int window;    // sliding window W, 0 for none
+  const int32_t* table;
+  int page_size, max_pages, num_pages;
   float* ws_o;   // [B, H, nchunk, d]
   float* ws_ml;  // [B, H, nchunk, 2]
 };

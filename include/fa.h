@@ -131,6 +131,28 @@ fa_status fa_decode_sliding_window(const void* q, const void* k_cache, const voi
                                    int window, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * fa_decode_paged — fa_decode against a paged KV cache. "FlashAttention 与长上下文：先分清
+ * 三张账" names PagedAttention's paged KV allocation (section on prefill and decode) without
+ * a layout; the one read here:
+ *   k_pages, v_pages : bf16 [num_pages, Hkv, page_size, d]  (a page holds page_size
+ *                      consecutive positions of one sequence, for every KV head)
+ *   block_table      : device int32 [B, max_pages]; position j of request b is row
+ *                      j % page_size of page block_table[b][j / page_size]
+ *   ctx_lens         : device int32 [B], clamped to [0, max_pages * page_size]
+ *   window           : 0 for none, else a sliding window as in fa_decode_sliding_window
+ *   workspace        : fa_decode_workspace_bytes(B, H, max_pages * page_size, d) bytes
+ * page_size must be a power of two; sizes below 16 return FA_ERR_UNSUPPORTED (a 16-key
+ * half step of the kernel must lie in one page). Table entries are device data and are not
+ * checked on the host: the kernel clamps each to [0, num_pages - 1], so a bad table gives
+ * wrong numbers but never an access outside the pools. Entries past a request's context are
+ * not read. q, o, lse, scale and errors as for fa_decode.
+ */
+fa_status fa_decode_paged(const void* q, const void* k_pages, const void* v_pages, void* o, float* lse,
+                          int B, int H, int Hkv, int d, float scale, int page_size, int num_pages,
+                          const int32_t* block_table, int max_pages, const int32_t* ctx_lens, int window,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * fa_bwd_workspace_bytes — bytes of device workspace fa_bwd needs: two fp32 per query row
  * (the row's LSE in base 2 and D = rowsum(dO * O)), i.e. B * H * Lq * 8. Returns 0 for
  * invalid sizes.

@@ -22,6 +22,7 @@ def test_library_exports_every_declared_symbol():
     L = fa.lib()
     names = _declared_functions()
     assert set(names) == {"fa_fwd", "fa_fwd_sliding_window", "fa_fwd_f32", "fa_decode", "fa_decode_sliding_window",
+                          "fa_decode_paged",
                           "fa_decode_workspace_bytes", "fa_bwd", "fa_bwd_sliding_window", "fa_bwd_workspace_bytes",
                           "fa_status_string"}
     assert set(names) == set(fa.binding.SYMBOLS)
@@ -158,3 +159,27 @@ def test_sliding_window_validation():
                                        None) == INV
     assert L.fa_bwd_sliding_window(A, A, A, A, A, A, A2, A2, A2, 2, 4, 2, 100, 100, 128, 0.1, 5, None, A2,
                                    bneed - 1, None) == INV
+
+
+def test_decode_paged_validation():
+    L = fa.lib()
+    INV, UNS, OK = fa.binding.FA_ERR_INVALID, fa.binding.FA_ERR_UNSUPPORTED, fa.binding.FA_OK
+    need = L.fa_decode_workspace_bytes(2, 4, 8 * 16, 128)
+
+    def call(q=A, kp=A, vp=A, o=A2, lse=A2, B=2, H=4, Hkv=2, d=128, scale=0.1, P=16, npg=20, table=A, mp=8,
+             ctx=A, window=0, ws=A2, wsb=need):
+        return L.fa_decode_paged(q, kp, vp, o, lse, B, H, Hkv, d, scale, P, npg, table, mp, ctx, window, ws, wsb, None)
+    assert call(P=24) == INV               # not a power of two
+    assert call(P=0) == INV
+    assert call(P=8) == UNS                # power of two below 16
+    assert call(window=-1) == INV
+    assert call(table=None) == INV
+    assert call(table=A + 2) == INV        # misaligned table
+    assert call(npg=0) == INV              # no pages for B > 0
+    assert call(kp=None) == INV
+    assert call(ctx=None) == INV
+    assert call(wsb=need - 1) == INV
+    assert call(H=5) == INV
+    assert call(d=96) == UNS
+    assert call(mp=1 << 27, P=32) == INV   # capacity past 2^31 positions
+    assert call(B=0, table=None, npg=0) == OK  # empty call
