@@ -147,6 +147,26 @@ def paged_decode_inputs(B, H, Hkv, Lmax, d, page_size, *, seed, device="cpu", le
             "ctx_lens": ctx.to(device), "ctx_lens_cpu": ctx, "page_size": page_size, "num_pages": num_pages}
 
 
+def fp8_prefill_inputs(B, H, Hkv, Lq, Lk, d, *, seed, device="cpu", len_range=None):
+    """FP8 prefill inputs: q, k, v as OCP E4M3 codes (uint8) of seeded normal values, each
+    (batch, head) scaled into the format's range by its own descale (amax / 240), and the
+    descales (fp32 [B, H] for q, [B, Hkv] for k and v). Dequantised: x = decode(code) * descale."""
+    seqlens = None
+    if len_range is not None:
+        seqlens = draw_lengths(B, len_range[0], len_range[1], seed)
+    gen = torch.Generator(device=device).manual_seed(seed + 1)
+    out = {}
+    for name, heads, L in (("q", H, Lq), ("k", Hkv, Lk), ("v", Hkv, Lk)):
+        x = _normal((B, heads, L, d), gen, device)
+        amax = x.abs().amax(dim=(2, 3)).clamp(min=1e-6)
+        ds = (amax / 240.0).to(torch.float32)
+        codes = (x / ds[:, :, None, None]).to(torch.float8_e4m3fn).view(torch.uint8)
+        out[name], out[name + "_descale"] = codes.contiguous(), ds.contiguous()
+    out["seqlens"] = None if seqlens is None else seqlens.to(device)
+    out["seqlens_cpu"] = seqlens
+    return out
+
+
 def workload_inputs(w: Workload, device="cpu"):
     """Inputs for a named workload at its full size."""
     if w.kind == "prefill":
