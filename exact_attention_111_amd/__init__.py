@@ -6,7 +6,7 @@ hand-written HIP kernels behind the C ABI of ``libfa.so`` (``include/fa.h``); th
 package only marshals arguments to it.
 """
 from .binding import (FaError, bwd, bwd_workspace_bytes, decode, decode_paged, decode_workspace_bytes,  # noqa: F401
-                      fwd, lib, status_string)
+                      fwd, fwd_fp8, lib, status_string)
 
-__all__ = ["fwd", "bwd", "bwd_workspace_bytes", "decode", "decode_paged", "decode_workspace_bytes", "FaError", "lib",
+__all__ = ["fwd", "fwd_fp8", "bwd", "bwd_workspace_bytes", "decode", "decode_paged", "decode_workspace_bytes", "FaError", "lib",
            "status_string"]

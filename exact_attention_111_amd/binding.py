@@ -15,7 +15,7 @@ import torch
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
 FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
-SYMBOLS = ("fa_fwd", "fa_fwd_sliding_window", "fa_fwd_f32", "fa_decode", "fa_decode_sliding_window", "fa_decode_paged",
+SYMBOLS = ("fa_fwd", "fa_fwd_sliding_window", "fa_fwd_fp8", "fa_fwd_f32", "fa_decode", "fa_decode_sliding_window", "fa_decode_paged",
            "fa_decode_workspace_bytes", "fa_bwd", "fa_bwd_sliding_window", "fa_bwd_workspace_bytes",
            "fa_status_string")
 
@@ -48,6 +48,8 @@ def lib() -> ctypes.CDLL:
     L.fa_fwd_f32.restype = i32
     L.fa_fwd_sliding_window.argtypes = fwd_args  # the int after scale is the window
     L.fa_fwd_sliding_window.restype = i32
+    L.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, i32, vp, vp]
+    L.fa_fwd_fp8.restype = i32
     L.fa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
     L.fa_decode_workspace_bytes.restype = ctypes.c_size_t
     L.fa_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, vp, vp, ctypes.c_size_t, vp]
@@ -122,6 +124,34 @@ def fwd(q, k, v, *, causal: bool = False, scale: float | None = None, seqlens=No
     st = getattr(lib(), name)(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Hkv, Lq, Lk, d, float(scale),
                               flag, _ptr(seqlens), _stream(q.device))
     _check(st, name)
+    return out, lse
+
+
+def fwd_fp8(q, k, v, q_descale, k_descale, v_descale, *, causal: bool = False, scale: float | None = None,
+            seqlens=None, window: int | None = None, out=None, lse=None):
+    """FP8 prefill through ``fa_fwd_fp8``: q [B, H, Lq, 128], k, v [B, Hkv, Lk, 128] as E4M3
+    codes (uint8 or float8_e4m3fn), descales fp32 [B, H] / [B, Hkv]. Returns (o bf16, lse fp32)."""
+    B, H, Lq, d = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, Lq, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device)
+    for t in (q, k, v, q_descale, k_descale, v_descale, out, lse):
+        if not t.is_contiguous():
+            raise ValueError("libfa needs contiguous tensors")
+    if not all(t.dtype in (torch.uint8, torch.float8_e4m3fn) for t in (q, k, v)):
+        raise ValueError("fwd_fp8 needs E4M3 codes (uint8 or float8_e4m3fn) for q, k, v")
+    if not all(t.dtype == torch.float32 for t in (q_descale, k_descale, v_descale)) or out.dtype != torch.bfloat16:
+        raise ValueError("descales must be float32 and out bfloat16")
+    if seqlens is not None and seqlens.dtype != torch.int32:
+        raise ValueError("seqlens must be int32")
+    st = lib().fa_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(q_descale), _ptr(k_descale), _ptr(v_descale), _ptr(out),
+                          _ptr(lse), B, H, Hkv, Lq, Lk, d, float(scale), int(bool(causal)),
+                          0 if window is None else int(window), _ptr(seqlens), _stream(q.device))
+    _check(st, "fa_fwd_fp8")
     return out, lse
 
 

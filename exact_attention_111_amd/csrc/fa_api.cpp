@@ -23,6 +23,8 @@ bool tensor_ok(const void* p, long long numel) {
 
 bool supported_d(int d) { return d == 64 || d == 128; }
 
+bool aligned4(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
 fa_status validate_fwd(const void* q, const void* k, const void* v, const void* o, const void* lse, int B, int H,
                        int Hkv, int Lq, int Lk, int d, float scale, int causal, const int32_t* seqlens) {
   if (B < 0 || H < 0 || Hkv < 1 || Lq < 0 || Lk < 0 || d < 1) return FA_ERR_INVALID;
@@ -118,6 +120,24 @@ fa_status fa_fwd_sliding_window(const void* q, const void* k, const void* v, voi
                                 void* stream) {
   if (window < 1) return FA_ERR_INVALID;
   return fwd_bf16(q, k, v, o, lse, B, H, Hkv, Lq, Lk, d, scale, 1, window, seqlens, stream);
+}
+
+fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, const float* q_descale, const float* k_descale,
+                     const float* v_descale, void* o, float* lse, int B, int H, int Hkv, int Lq, int Lk, int d,
+                     float scale, int causal, int window, const int32_t* seqlens, void* stream) {
+  if (window < 0 || (window > 0 && causal != 1)) return FA_ERR_INVALID;
+  // Element counts of the fp8 tensors in bf16 units for the shared check: a row of d bytes is
+  // d / 2 bf16 elements, so q, k, v are checked as non-null and 16-byte aligned when not empty.
+  fa_status s = validate_fwd(q, k, v, o, lse, B, H, Hkv, Lq, Lk, d, scale, causal, seqlens);
+  if (s == FA_ERR_INVALID) return s;
+  const bool any = (long long)B * H > 0;
+  if (any && (!aligned4(q_descale) || !aligned4(k_descale) || !aligned4(v_descale))) return FA_ERR_INVALID;
+  if (s != FA_OK) return s;
+  if (d != 128) return FA_ERR_UNSUPPORTED;
+  if (B == 0 || H == 0 || Lq == 0) return FA_OK;
+  fa::Fp8FwdParams p{q, k, v, q_descale, k_descale, v_descale, o, lse, B, H, Hkv, Lq, Lk, scale, causal, window,
+                     seqlens};
+  return fa::launch_fwd_fp8(p, static_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 fa_status fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int Hkv,

@@ -113,34 +113,8 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
   const int col = lane & 31;   // this lane's query row within a 32-row block
   const int half = lane >> 5;  // which 8-element half of a 16-wide k-step
 
-  // XCD-aware renumbering: hardware id i runs on XCD i % 8 as that XCD's slot i / 8.
-  // When the (batch, head) count is a multiple of 8, head bh belongs to XCD bh % 8, so
-  // every XCD gets the same mix of sequences (equal work even when lengths vary) and its
-  // L2 serves the K/V of its own heads only. An XCD goes through its heads in groups of
-  // just enough heads to fill its 32 CUs with query tiles, heaviest tile first across the
-  // group: one head at a time when a head has 32 or more tiles (its CUs then share that
-  // head's K/V in L2; walking all of an XCD's heads at once multiplied HBM re-reads 2.3x
-  // at B=1, H=32, L=16384), several when heads are short (one head at a time would start
-  // the heaviest tiles of later heads too late). Otherwise each XCD takes a contiguous
-  // range of logical ids, heaviest tile first within a head.
-  const int hw = blockIdx.x;
-  const int xcd = hw & 7, slot = hw >> 3;
-  const int nheads = a.nwg / a.ntq;
   int bh, qt;
-  if ((nheads & 7) == 0) {
-    const int per_xcd = nheads >> 3;
-    const int group = min(max(1, (32 + a.ntq - 1) / a.ntq), per_xcd);
-    const int g = slot / (group * a.ntq);
-    const int in_group = min(group, per_xcd - g * group);  // the last group may be smaller
-    const int idx = slot - g * group * a.ntq;
-    qt = a.ntq - 1 - idx / in_group;
-    bh = xcd + 8 * (g * group + idx % in_group);
-  } else {
-    const int per = a.nwg >> 3, extra = a.nwg & 7;
-    const int logical = xcd * per + min(xcd, extra) + slot;
-    bh = logical / a.ntq;
-    qt = a.ntq - 1 - (logical - bh * a.ntq);
-  }
+  xcd_tile_order(blockIdx.x, a.nwg, a.ntq, bh, qt);
   const int b = bh / a.H;
   const int h = bh - b * a.H;
   const int kvh = h / a.group;

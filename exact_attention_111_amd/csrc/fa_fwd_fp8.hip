@@ -1,0 +1,312 @@
+// fa_fwd_fp8.hip — prefill attention on FP8 (E4M3) Q, K, V for gfx950 (MI355X), d = 128.
+//
+// The low-precision step of FlashAttention-3 ("FlashAttention 与长上下文：先分清三张账", section
+// on FlashAttention-2/3; the pages give no scaling scheme). The scheme used:
+//   * q, k, v are OCP E4M3 codes with one fp32 descale per (batch, head); scores are
+//     t = s * (scale * log2(e) * descale_q * descale_k) with s = q8 . k8 from the FP8 matrix
+//     cores (fp32 accumulation of exact products);
+//   * each row keeps an integer base-2 reference m (raised to ceil(tile max) when a tile's
+//     scores pass it), so every rescale of the running output is an exact power of two;
+//   * x = 2^(t - m + 8) <= 256 enters the P V product as E4M3 (v_cvt_pk_fp8_f32, round to
+//     nearest even) while the row sum l adds the unrounded x;
+//   * O = descale_v * o / l (bf16) and LSE = ln(2) (m - 8 + log2 l).
+// E4M3 rounding commutes with power-of-two scaling, so the result does not depend on the
+// tiling: it is the whole-row definition with the final reference.
+//
+// gfx950 mapping (v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales for both products):
+//   * Workgroup: 256 query rows of one (batch, head), 8 waves of 32 rows, two per SIMD. Each
+//     wave keeps its Q rows as B operands: lane (half, col) holds dims 64 ks + 32 half ..
+//     + 31 of query row col (the operands' byte t of half h pair up in the product).
+//   * 64-key K and V tiles (8 KB each) stream through a 4-stage LDS ring filled by direct
+//     buffer-to-LDS loads three tiles ahead, one barrier per tile.
+//   * S^T = K Q^T: K rows read 32 bytes at a time (two 128-bit reads); accumulator element
+//     r of key block kb is key 32 kb + 8 (r / 4) + 4 half + r % 4 of query col.
+//   * P^T as the B operand of O^T += V^T P^T: byte 16 kb + r of a lane is that element's
+//     E4M3 value. V^T comes from ds_read_b64_tr_b8: output lane 16 g + j gets byte j % 8 of
+//     the 8-byte addresses of lanes 16 g + j / 8 + 2 t (t = 0..7), so lane 16 g + p points
+//     at the key of byte 8 u + p / 2 and the 8 dims starting 32 nb + 16 (g % 2) + 8 (p % 2).
+//   * LDS layout: K chunk ^ ((row >> 1) & 7) (128-bit row reads: 16 rows of 128 bytes per
+//     read); V chunk ^ 2 ((row >> 1 & 1) | (row >> 3 & 1) << 1) (transposed reads: 8 rows x
+//     32 bytes per 32 lanes); both conflict-free.
+#include "fa_device.h"
+#include "fa_launch.h"
+#include "fa_tiles.h"
+
+namespace fa {
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+
+constexpr int kF8D = 128;              // head dim
+constexpr int kF8NW = 8;               // waves per workgroup (two per SIMD)
+constexpr int kF8NT = 64 * kF8NW;
+constexpr int kF8BM = 32 * kF8NW;      // query rows per workgroup
+constexpr int kF8BN = 64;              // keys per tile
+constexpr int kF8Tile = kF8BN * kF8D;  // bytes of a K or V tile
+constexpr int kF8Stage = 2 * kF8Tile;  // K | V
+constexpr int kF8NS = 4;               // stages in the ring
+constexpr int kF8KS = kF8D / 64;       // 32x32x64 k-steps over d
+constexpr int kF8NB = kF8D / 32;       // 32-wide blocks of O^T
+static_assert(kF8Tile == 1024 * kF8NW, "one 1 KB direct load per wave and tile");
+
+__device__ __forceinline__ int f8_kxor(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int f8_vxor(int r) { return 2 * (((r >> 1) & 1) | (((r >> 3) & 1) << 1)); }
+
+// Key of P^T byte T (0..31) in lane half h: accumulator element r = T % 16 of key block T / 16.
+__device__ __forceinline__ int f8_key(int h, int T) { return 32 * (T >> 4) + 8 * ((T & 15) >> 2) + 4 * h + (T & 3); }
+
+__device__ __forceinline__ f32x16 mfma_f8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+struct Fp8Args {
+  const unsigned char* q;
+  const unsigned char* k;
+  const unsigned char* v;
+  const float* q_descale;  // [B, H]
+  const float* k_descale;  // [B, Hkv]
+  const float* v_descale;  // [B, Hkv]
+  __bf16* o;
+  float* lse;
+  int B, H, Hkv, Lq, Lk;
+  int group, ntq, nwg;
+  float scale_log2;
+  int causal, window;
+  const int32_t* seqlens;
+};
+
+__global__ __launch_bounds__(kF8NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_fp8_kernel(const Fp8Args a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __shared__ __attribute__((aligned(1024))) char smem[kF8NS * kF8Stage];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31, half = lane >> 5;
+
+  int bh, qt;
+  xcd_tile_order(blockIdx.x, a.nwg, a.ntq, bh, qt);
+  const int b = bh / a.H, h = bh - b * a.H, kvh = h / a.group;
+  int n_kv = a.Lk, n_q = a.Lq;
+  if (a.seqlens != nullptr) {
+    const int n = min(max(a.seqlens[b], 0), a.Lk);
+    n_kv = n;
+    n_q = n;
+  }
+  const int delta = a.Lk - a.Lq;
+  const int q0 = qt * kF8BM;
+  const int qw0 = q0 + 32 * w;
+  const int my_q = qw0 + col;
+
+  int kv_end = 0;
+  if (q0 < n_q) {
+    kv_end = n_kv;
+    if (a.causal) kv_end = min(kv_end, min(q0 + kF8BM, n_q) + delta);
+    kv_end = max(kv_end, 0);
+  }
+  kv_end = __builtin_amdgcn_readfirstlane(kv_end);
+  const int kbase = __builtin_amdgcn_readfirstlane(
+      a.window > 0 ? (max(q0 + delta - a.window + 1, 0) / kF8BN) * kF8BN : 0);
+  const int ntk = max((kv_end - kbase + kF8BN - 1) / kF8BN, 0);
+
+  // Combined score factor (base 2) and the output descale.
+  const float c = a.scale_log2 * a.q_descale[b * a.H + h] * a.k_descale[b * a.Hkv + kvh];
+  const float dv = a.v_descale[b * a.Hkv + kvh];
+
+  // Q rows as B operands.
+  i32x8 qf[kF8KS];
+  const unsigned char* qrow = a.q + ((size_t)(b * a.H + h) * a.Lq + my_q) * kF8D;
+#pragma unroll
+  for (int ks = 0; ks < kF8KS; ++ks) {
+    u32x4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
+    if (my_q < n_q && ntk > 0) {
+      lo = *reinterpret_cast<const u32x4*>(qrow + 64 * ks + 32 * half);
+      hi = *reinterpret_cast<const u32x4*>(qrow + 64 * ks + 32 * half + 16);
+    }
+    qf[ks] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  }
+
+  f32x16 oacc[kF8NB];
+#pragma unroll
+  for (int nb = 0; nb < kF8NB; ++nb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[nb][r] = 0.f;
+  float m = kNegInf, l = 0.f;
+
+  // LDS addresses. K: lane (half, col) reads row 32 kb + col, logical chunks 4 ks + 2 half
+  // (+1); kv rows of the two key blocks share the swizzle, so kb is an immediate offset.
+  int kaddr[kF8KS][2];
+#pragma unroll
+  for (int ks = 0; ks < kF8KS; ++ks)
+#pragma unroll
+    for (int p = 0; p < 2; ++p) kaddr[ks][p] = col * kF8D + (((4 * ks + 2 * half + p) ^ f8_kxor(col)) << 4);
+  // V^T: lane 16 g + p, read u (keys of bytes 8 u .. 8 u + 7), block nb; reads u + 2 are
+  // 32 rows further on with the same swizzle.
+  int vaddr[2][kF8NB];
+  {
+    const int g = lane >> 4, p = lane & 15;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int key = f8_key(half, 8 * u + (p >> 1));
+#pragma unroll
+      for (int nb = 0; nb < kF8NB; ++nb)
+        vaddr[u][nb] = key * kF8D + (((2 * nb + (g & 1)) ^ f8_vxor(key)) << 4) + 8 * (p & 1);
+    }
+  }
+  // Direct-load source offsets of this wave's 1 KB of each tile.
+  const int lrow = w * 8 + (lane >> 3), pch = lane & 7;
+  const unsigned koff = (unsigned)(lrow * kF8D + ((pch ^ f8_kxor(lrow)) << 4));
+  const unsigned voff = (unsigned)(lrow * kF8D + ((pch ^ f8_vxor(lrow)) << 4));
+  const size_t kv_row0 = (size_t)(b * a.Hkv + kvh) * a.Lk;
+  const char* const ksrc = reinterpret_cast<const char*>(a.k) + kv_row0 * kF8D;
+  const char* const vsrc = reinterpret_cast<const char*>(a.v) + kv_row0 * kF8D;
+  auto issue = [&](int t) {
+    const int k0 = kbase + t * kF8BN;
+    const unsigned nrows = (unsigned)max(kv_end - k0, 0);
+    char* st = smem + (t % kF8NS) * kF8Stage;
+    lds_dma16_buf(raw_buffer_rsrc(ksrc + (size_t)k0 * kF8D, nrows * kF8D), koff, lds_addr(st + w * 1024));
+    lds_dma16_buf(raw_buffer_rsrc(vsrc + (size_t)k0 * kF8D, nrows * kF8D), voff, lds_addr(st + kF8Tile + w * 1024));
+  };
+
+  if (ntk > 0) {
+    for (int i = tid; i < (int)sizeof(smem) / 16; i += kF8NT) reinterpret_cast<u32x4*>(smem)[i] = u32x4{0u, 0u, 0u, 0u};
+    __syncthreads();  // the zero fill is done before any direct load lands
+  }
+#pragma unroll
+  for (int t = 0; t < kF8NS - 1; ++t)
+    if (t < ntk) issue(t);
+
+  for (int t = 0; t < ntk; ++t) {
+    if (t + kF8NS - 1 <= ntk) wait_vmcnt<(kF8NS - 2) * 2>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+    if (t + kF8NS - 1 < ntk) issue(t + kF8NS - 1);
+    const char* kt = smem + (t % kF8NS) * kF8Stage;
+    const char* vt = kt + kF8Tile;
+    const int k0 = kbase + t * kF8BN;
+
+    // S^T for the two 32-key blocks.
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < kF8KS; ++ks) {
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(kt + kaddr[ks][0] + 32 * kb * kF8D);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(kt + kaddr[ks][1] + 32 * kb * kF8D);
+        const i32x8 ka = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        s[kb] = mfma_f8(ka, qf[ks], s[kb]);
+      }
+    }
+    // Mask boundary tiles (selects).
+    const bool need_mask = (k0 + kF8BN > n_kv) || (a.causal && k0 + kF8BN - 1 > qw0 + delta) ||
+                           (a.window > 0 && k0 < qw0 + 32 + delta - a.window);
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = k0 + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
+          const bool vis = j < n_kv && (!a.causal || j <= my_q + delta) && (a.window <= 0 || j > my_q + delta - a.window);
+          s[kb][r] = vis ? s[kb][r] : kNegInf;
+        }
+    }
+    // Integer reference: raised to ceil(tile max) when the tile passes it.
+    float mx = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = max_of_halves(mx) * c;
+    const float m_new = mx > m ? ceilf(mx) : m;
+    // 0 when there was no reference, 1 when unchanged, else an exact power of two
+    const float alpha = m == kNegInf ? 0.f : __builtin_amdgcn_ldexpf(1.f, (int)(m - m_new));
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
+      l *= alpha;
+#pragma unroll
+      for (int nb = 0; nb < kF8NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[nb][r] *= alpha;
+    }
+    m = m_new;
+    // x = 2^(t - m + 8) <= 256; a row with no reference yet has only masked scores here.
+    const float off = m == kNegInf ? 0.f : 8.f - m;
+    int pk[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      // bytes 4 i .. 4 i + 3 = elements (kb, r) with 16 kb + r = 4 i .. 4 i + 3
+      float x[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int T = 4 * i + e;
+        x[e] = exp2_hw(fmaf(s[T >> 4][T & 15], c, off));
+        l += x[e];
+      }
+      int word = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+      word = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], word, true);
+      pk[i] = word;
+    }
+    const i32x8 pb = {pk[0], pk[1], pk[2], pk[3], pk[4], pk[5], pk[6], pk[7]};
+    // O^T += V^T P^T.
+#pragma unroll
+    for (int nb = 0; nb < kF8NB; ++nb) {
+      const i32x2 r0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vt + vaddr[0][nb]));
+      const i32x2 r1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vt + vaddr[1][nb]));
+      const i32x2 r2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vt + vaddr[0][nb] + 32 * kF8D));
+      const i32x2 r3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vt + vaddr[1][nb] + 32 * kF8D));
+      const i32x8 va = {r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
+      oacc[nb] = mfma_f8(va, pb, oacc[nb]);
+    }
+  }
+  if (ntk > 0) wait_vmcnt<0>();
+
+  // Epilogue: O = descale_v * o / l, LSE = ln(2) (m - 8 + log2 l); rows that saw nothing
+  // (and padding rows) get O = 0 and LSE = -inf.
+  unsigned lo_bits, hi_bits;
+  wave_halves(__builtin_bit_cast(unsigned, l), lo_bits, hi_bits);
+  const float lt = __builtin_bit_cast(float, lo_bits) + __builtin_bit_cast(float, hi_bits);
+  const bool row_ok = my_q < n_q && lt > 0.f;
+  const float inv = row_ok ? dv / lt : 0.f;
+  if (my_q < a.Lq) {
+    __bf16* op = a.o + ((size_t)(b * a.H + h) * a.Lq + my_q) * kF8D;
+#pragma unroll
+    for (int nb = 0; nb < kF8NB; ++nb)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int d0 = 32 * nb + 8 * jj + 4 * half;
+        Store4<__bf16>::store(op + d0, oacc[nb][4 * jj] * inv, oacc[nb][4 * jj + 1] * inv,
+                              oacc[nb][4 * jj + 2] * inv, oacc[nb][4 * jj + 3] * inv);
+      }
+    if (half == 0) a.lse[(size_t)(b * a.H + h) * a.Lq + my_q] = row_ok ? (m - 8.f + __log2f(lt)) * kLn2 : kNegInf;
+  }
+#endif
+}
+
+}  // namespace
+
+hipError_t launch_fwd_fp8(const Fp8FwdParams& p, hipStream_t stream) {
+  Fp8Args a;
+  a.q = static_cast<const unsigned char*>(p.q);
+  a.k = static_cast<const unsigned char*>(p.k);
+  a.v = static_cast<const unsigned char*>(p.v);
+  a.q_descale = p.q_descale;
+  a.k_descale = p.k_descale;
+  a.v_descale = p.v_descale;
+  a.o = static_cast<__bf16*>(p.o);
+  a.lse = p.lse;
+  a.B = p.B; a.H = p.H; a.Hkv = p.Hkv; a.Lq = p.Lq; a.Lk = p.Lk;
+  a.group = p.H / p.Hkv;
+  a.ntq = (p.Lq + kF8BM - 1) / kF8BM;
+  a.scale_log2 = p.scale * kLog2e;
+  a.causal = p.causal;
+  a.window = p.window;
+  a.seqlens = p.seqlens;
+  const long long nwg = (long long)a.ntq * p.B * p.H;
+  if (nwg > 0x7fffffffLL || (long long)p.Lk * kF8D > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  a.nwg = (int)nwg;
+  void* args[] = {&a};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_fp8_kernel), dim3((unsigned)nwg), dim3(kF8NT), args, 0,
+                         stream);
+}
+
+}  // namespace fa

@@ -21,6 +21,24 @@ struct FwdParams {
   const int32_t* seqlens;
 };
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream);
+
+// FP8 prefill (d = 128): E4M3 q, k, v with per-(batch, head) fp32 descales, bf16 o.
+struct Fp8FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* q_descale;  // [B, H]
+  const float* k_descale;  // [B, Hkv]
+  const float* v_descale;  // [B, Hkv]
+  void* o;
+  float* lse;
+  int B, H, Hkv, Lq, Lk;
+  float scale;
+  int causal;
+  int window;
+  const int32_t* seqlens;
+};
+hipError_t launch_fwd_fp8(const Fp8FwdParams& p, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream);
 
 // Decode: split kernel over key chunks, then the combine kernel.

@@ -32,4 +32,34 @@ __device__ __forceinline__ int kv_xor(int r) {
   return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 
+// Query tile and (batch, head) of prefill workgroup `hw` (ntq query tiles per head, nwg
+// workgroups), heaviest tile first. Hardware id i runs on XCD i % 8 as that XCD's slot i / 8.
+// When the (batch, head) count is a multiple of 8, head bh belongs to XCD bh % 8, so every
+// XCD gets the same mix of sequences (equal work even when lengths vary) and its L2 serves
+// the K/V of its own heads only. An XCD goes through its heads in groups of just enough
+// heads to fill its 32 CUs with query tiles, heaviest tile first across the group: one head
+// at a time when a head has 32 or more tiles (its CUs then share that head's K/V in L2;
+// walking all of an XCD's heads at once multiplied HBM re-reads 2.3x at B=1, H=32,
+// L=16384), several when heads are short (one head at a time would start the heaviest tiles
+// of later heads too late). Otherwise each XCD takes a contiguous range of logical ids,
+// heaviest tile first within a head.
+__device__ __forceinline__ void xcd_tile_order(int hw, int nwg, int ntq, int& bh, int& qt) {
+  const int xcd = hw & 7, slot = hw >> 3;
+  const int nheads = nwg / ntq;
+  if ((nheads & 7) == 0) {
+    const int per_xcd = nheads >> 3;
+    const int group = min(max(1, (32 + ntq - 1) / ntq), per_xcd);
+    const int g = slot / (group * ntq);
+    const int in_group = min(group, per_xcd - g * group);  // the last group may be smaller
+    const int idx = slot - g * group * ntq;
+    qt = ntq - 1 - idx / in_group;
+    bh = xcd + 8 * (g * group + idx % in_group);
+  } else {
+    const int per = nwg >> 3, extra = nwg & 7;
+    const int logical = xcd * per + min(xcd, extra) + slot;
+    bh = logical / ntq;
+    qt = ntq - 1 - (logical - bh * ntq);
+  }
+}
+
 }  // namespace fa

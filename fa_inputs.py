@@ -158,7 +158,7 @@ def fp8_prefill_inputs(B, H, Hkv, Lq, Lk, d, *, seed, device="cpu", len_range=No
     out = {}
     for name, heads, L in (("q", H, Lq), ("k", Hkv, Lk), ("v", Hkv, Lk)):
         x = _normal((B, heads, L, d), gen, device)
-        amax = x.abs().amax(dim=(2, 3)).clamp(min=1e-6)
+        amax = x.abs().amax(dim=(2, 3)).clamp(min=1e-6) if x.numel() else torch.ones(x.shape[:2], device=device)
         ds = (amax / 240.0).to(torch.float32)
         codes = (x / ds[:, :, None, None]).to(torch.float8_e4m3fn).view(torch.uint8)
         out[name], out[name + "_descale"] = codes.contiguous(), ds.contiguous()

@@ -85,6 +85,25 @@ fa_status fa_fwd_sliding_window(const void* q, const void* k, const void* v, voi
                                 const int32_t* seqlens, void* stream);
 
 /*
+ * fa_fwd_fp8 — prefill forward on FP8 operands (d = 128 only; other d: FA_ERR_UNSUPPORTED).
+ * The low-precision step of FlashAttention-3 ("FlashAttention 与长上下文：先分清三张账",
+ * section on FlashAttention-2/3), whose scaling the pages leave open. The scheme read here:
+ *   q : E4M3 codes [B, H, Lq, 128]    k, v : E4M3 codes [B, Hkv, Lk, 128]  (OCP E4M3FN bytes)
+ *   q_descale : device fp32 [B, H]; k_descale, v_descale : device fp32 [B, Hkv];
+ *               the attended values are decode(code) * descale of their (batch, head).
+ *   o : bf16 [B, H, Lq, 128]          lse : fp32 [B, H, Lq] (natural log)
+ * Scores come from the FP8 matrix cores (exact products, fp32 sums). Each row keeps an
+ * integer base-2 reference m >= every score seen; probabilities relative to it, times 2^8,
+ * enter the P V product rounded to E4M3 (nearest even) while the row sum l adds them
+ * unrounded; O = descale_v * (sum_j E4M3(2^8 p_j) v_j) / (2^8 l). The result does not depend
+ * on the tiling. causal, seqlens as for fa_fwd; window = 0 for none, or a sliding window
+ * W >= 1 (needs causal = 1) as in fa_fwd_sliding_window. The call needs no workspace.
+ */
+fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, const float* q_descale, const float* k_descale,
+                     const float* v_descale, void* o, float* lse, int B, int H, int Hkv, int Lq, int Lk, int d,
+                     float scale, int causal, int window, const int32_t* seqlens, void* stream);
+
+/*
  * fa_fwd_f32 — the same contract with fp32 q, k, v and fp32 o. The kernel rounds
  * q, k, v to bf16 (round-to-nearest-even) as it loads them and multiplies them on the
  * bf16 matrix cores with fp32 accumulation; O and LSE are produced in fp32.

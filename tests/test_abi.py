@@ -21,7 +21,7 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     L = fa.lib()
     names = _declared_functions()
-    assert set(names) == {"fa_fwd", "fa_fwd_sliding_window", "fa_fwd_f32", "fa_decode", "fa_decode_sliding_window",
+    assert set(names) == {"fa_fwd", "fa_fwd_sliding_window", "fa_fwd_fp8", "fa_fwd_f32", "fa_decode", "fa_decode_sliding_window",
                           "fa_decode_paged",
                           "fa_decode_workspace_bytes", "fa_bwd", "fa_bwd_sliding_window", "fa_bwd_workspace_bytes",
                           "fa_status_string"}
@@ -183,3 +183,21 @@ def test_decode_paged_validation():
     assert call(d=96) == UNS
     assert call(mp=1 << 27, P=32) == INV   # capacity past 2^31 positions
     assert call(B=0, table=None, npg=0) == OK  # empty call
+
+
+def test_fwd_fp8_validation():
+    L = fa.lib()
+    INV, UNS, OK = fa.binding.FA_ERR_INVALID, fa.binding.FA_ERR_UNSUPPORTED, fa.binding.FA_OK
+
+    def call(q=A, k=A, v=A, qs=A2, ks=A2, vs=A2, o=A2, lse=A2, B=1, H=2, Hkv=1, Lq=4, Lk=4, d=128, scale=0.1,
+             causal=1, window=0, seqlens=None):
+        return L.fa_fwd_fp8(q, k, v, qs, ks, vs, o, lse, B, H, Hkv, Lq, Lk, d, scale, causal, window, seqlens, None)
+    assert call(d=64) == UNS
+    assert call(window=-1) == INV
+    assert call(window=3, causal=0) == INV
+    assert call(qs=None) == INV
+    assert call(vs=A2 + 2) == INV   # misaligned descale
+    assert call(q=MIS) == INV
+    assert call(H=3, Hkv=2) == INV
+    assert call(scale=0.0) == INV
+    assert call(B=0) == OK

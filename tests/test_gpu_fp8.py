@@ -1,0 +1,108 @@
+"""GPU parity of fa_fwd_fp8 (FP8 prefill) against the fp64 FP8 oracle (oracle/fp8.py), through
+the C ABI, at the tolerance of the bf16 prefill. The oracle writes out the same P rounding, so
+only fp32 sums differ, plus probabilities that lie within fp32 error of an E4M3 rounding
+midpoint and may round the other way; each such element adds its one-spacing effect on O to
+that row's allowance (parity.fp8_flip_slack)."""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import fa_inputs
+import oracle
+from parity import compare, fp8_flip_slack
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _fa():
+    import exact_attention_111_amd as fa
+    return fa
+
+
+def announce(**case):
+    print("\n[case] " + " ".join(f"{k}={v}" for k, v in case.items()), flush=True)
+    sys.stdout.flush()
+
+
+def run_fp8(B, H, Hkv, Lq, Lk, *, causal, seed, window=None, len_range=None):
+    d = 128
+    announce(entry="fa_fwd_fp8", B=B, H=H, Hkv=Hkv, Lq=Lq, Lk=Lk, causal=causal, window=window, seed=seed,
+             len_range=len_range)
+    x = fa_inputs.fp8_prefill_inputs(B, H, Hkv, Lq, Lk, d, seed=seed, device=DEV, len_range=len_range)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = _fa().fwd_fp8(x["q"], x["k"], x["v"], x["q_descale"], x["k_descale"], x["v_descale"], causal=causal,
+                           scale=scale, seqlens=x["seqlens"], window=window)
+    torch.cuda.synchronize()
+    sl = None if x["seqlens_cpu"] is None else x["seqlens_cpu"].numpy()
+    arrs = [x[n].cpu().numpy() for n in ("q", "k", "v", "q_descale", "k_descale", "v_descale")]
+    O, LSE = oracle.attention_fp8(*arrs, scale=scale, causal=causal, seqlens=sl, window=window)
+    slack = np.zeros(LSE.shape)
+    for b in range(B):
+        for h in range(H):
+            kvh = h // (H // Hkv)
+            Q = oracle.e4m3_decode(arrs[0][b, h]) * float(arrs[3][b, h])
+            K = oracle.e4m3_decode(arrs[1][b, kvh]) * float(arrs[4][b, kvh])
+            V = oracle.e4m3_decode(arrs[2][b, kvh]) * float(arrs[5][b, kvh])
+            slack[b, h] = fp8_flip_slack(Q, K, V, scale=scale, causal=causal,
+                                         n_valid=None if sl is None else int(sl[b]), window=window)
+    st = compare(o, lse, O, LSE, bf16_out=True, what=f"fp8 B{B} H{H}/{Hkv} L{Lq}x{Lk} c{int(causal)} W{window}",
+                 o_slack=slack)
+    print(f"  rows with flip allowance: {int((slack > 0).sum())} of {slack.size}; {st}", flush=True)
+    return x, o, lse
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_ragged_gqa(causal):
+    run_fp8(2, 4, 2, 300, 300, causal=causal, seed=600 + int(causal))
+
+
+@pytest.mark.parametrize("Lq,Lk", [(100, 333), (333, 100), (1, 700)])
+def test_fp8_unequal_lengths(Lq, Lk):
+    run_fp8(1, 2, 1, Lq, Lk, causal=True, seed=610 + Lq)
+
+
+def test_fp8_varlen():
+    run_fp8(3, 4, 2, 700, 700, causal=True, seed=620, len_range=(1, 700))
+
+
+@pytest.mark.parametrize("W", [1, 100])
+def test_fp8_window(W):
+    run_fp8(2, 2, 1, 400, 400, causal=True, seed=630 + W, window=W)
+
+
+def test_fp8_empty_and_no_keys():
+    announce(entry="fa_fwd_fp8", case="empty / no keys")
+    fa = _fa()
+    q = torch.zeros(1, 2, 0, 128, dtype=torch.uint8, device=DEV)
+    ds = torch.ones(1, 2, device=DEV)
+    o, lse = fa.fwd_fp8(q, q, q, ds, ds, ds)
+    assert o.shape == (1, 2, 0, 128)
+    x = fa_inputs.fp8_prefill_inputs(1, 2, 2, 50, 0, 128, seed=640, device=DEV)
+    o, lse = fa.fwd_fp8(x["q"], x["k"], x["v"], x["q_descale"], x["k_descale"], x["v_descale"])
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_fp8_full_size_16k_sampled():
+    """The 16,384-token causal workload with FP8 inputs in bench.py's launch configuration:
+    sampled rows of two heads against the oracle."""
+    w = fa_inputs.WORKLOADS["causal_prefill_B1_H32_L16384_d128"]
+    announce(entry="fa_fwd_fp8", workload=w.name, case="sampled rows")
+    x = fa_inputs.fp8_prefill_inputs(w.B, w.H, w.Hkv, w.L, w.L, w.d, seed=w.seed, device=DEV)
+    o, lse = _fa().fwd_fp8(x["q"], x["k"], x["v"], x["q_descale"], x["k_descale"], x["v_descale"], causal=True,
+                           scale=w.scale)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(650)
+    rows = np.sort(np.concatenate([[0, 1, 255, 256, w.L - 1], rng.choice(w.L, 27, replace=False)]))
+    for h in (0, 19):
+        Q = oracle.e4m3_decode(x["q"][0, h].cpu().numpy()) * float(x["q_descale"][0, h])
+        K = oracle.e4m3_decode(x["k"][0, h].cpu().numpy()) * float(x["k_descale"][0, h])
+        V = oracle.e4m3_decode(x["v"][0, h].cpu().numpy()) * float(x["v_descale"][0, h])
+        O, LSE = oracle.attention_fp8_head(Q, K, V, scale=w.scale, causal=True, rows=rows)
+        slack = fp8_flip_slack(Q, K, V, scale=w.scale, causal=True, rows=rows)
+        compare(o[0, h, rows], lse[0, h, rows], O, LSE, bf16_out=True, what=f"fp8 16k head {h}", o_slack=slack)

@@ -168,3 +168,19 @@ def test_batched_wrapper_dequantises_per_head():
                                         F.e4m3_decode(v8[b, kvh]) * vs[b, kvh], scale=0.25, causal=True)
             np.testing.assert_array_equal(O[b, h], o)
             np.testing.assert_array_equal(L_[b, h], l)
+
+
+def test_flip_allowance_marks_only_near_midpoint_probabilities():
+    """parity.fp8_flip_slack: zero when every probability is far from an E4M3 midpoint, and one
+    spacing's worth when a probability sits on one."""
+    from parity import fp8_flip_slack
+    scale = 0.5
+    # t = (0, -1): x = 256 and 128, both E4M3 values, far from midpoints
+    q = np.array([[1.0, 0.0]])
+    k = np.array([[0.0, 0.0], [-1.0 / (scale * np.log2(np.e)), 0.0]])
+    v = np.array([[1.0, 0.0], [3.0, 0.0]])
+    assert fp8_flip_slack(q, k, v, scale=scale)[0] == 0.0
+    # x2 = 256 * 2^t2 = 136, the midpoint between 128 and 144 (spacing 16)
+    k2 = np.array([[0.0, 0.0], [np.log2(136 / 256) / (scale * np.log2(np.e)), 0.0]])
+    got = fp8_flip_slack(q, k2, v, scale=scale)[0]
+    assert abs(got - 16.0 * 3.0 / (256 + 136)) < 1e-9
