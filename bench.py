@@ -56,6 +56,8 @@ def parse():
     ap.add_argument("--window", type=int, default=None,
                     help="with --only: a sliding window of this many keys (prefill, backward and decode workloads); "
                          "work is counted over the keys inside the window")
+    ap.add_argument("--fp8", action="store_true",
+                    help="with --only and a prefill workload (d = 128): FP8 E4M3 inputs through fa_fwd_fp8")
     ap.add_argument("--page", type=int, default=None,
                     help="with --only and a decode workload: the KV cache in pages of this many positions, "
                          "scattered through a pool by a random block table (fa_decode_paged)")
@@ -144,7 +146,7 @@ def _window_pairs(lens, W):
     return float(tot)
 
 
-def run_only(part, steps, warmup, window=None, page=None):
+def run_only(part, steps, warmup, window=None, page=None, fp8=False):
     """Time one part alone (for profiling): the prefill or decode part of the step, a plain
     1 GiB device copy, or any named workload. Prints the kernel time and, for workloads,
     the algorithmic rate (prefill: TFLOP/s over visible pairs as in the metric; decode: K/V
@@ -206,6 +208,20 @@ def run_only(part, steps, warmup, window=None, page=None):
             if window is not None:
                 ctx = ctx.clamp(max=window)
             work, unit = float(2 * w.Hkv * w.d * 2 * int(ctx.sum())), "GB/s"
+        elif fp8:
+            x = fa_inputs.fp8_prefill_inputs(w.B, w.H, w.Hkv, w.L, w.L, w.d, seed=w.seed, device=dev,
+                                             len_range=w.len_range)
+            o = torch.empty((w.B, w.H, w.L, w.d), dtype=torch.bfloat16, device=dev)
+            lse = torch.empty((w.B, w.H, w.L), dtype=torch.float32, device=dev)
+            sl = x.get("seqlens")
+            fn = lambda: fa.fwd_fp8(x["q"], x["k"], x["v"], x["q_descale"], x["k_descale"],  # noqa: E731
+                                    x["v_descale"], causal=w.causal, scale=w.scale, seqlens=sl, window=window,
+                                    out=o, lse=lse)
+            lens = x["seqlens_cpu"].to(torch.float64) if sl is not None else torch.full((w.B,), float(w.L))
+            pairs = float((lens * lens).sum()) * (0.5 if w.causal else 1.0)
+            if window is not None:
+                pairs = _window_pairs(lens.tolist(), window)
+            work, unit = 4.0 * w.H * w.d * pairs, "TFLOP/s"
         else:
             o = torch.empty_like(x["q"])
             lse = torch.empty((w.B, w.H, w.L), dtype=torch.float32, device=dev)
@@ -228,7 +244,7 @@ def run_only(part, steps, warmup, window=None, page=None):
         a.record(); fn(); b.record()
     torch.cuda.synchronize()
     ms = sorted(a.elapsed_time(b) for a, b in ev)
-    line = {"only": name, "window": window, "page": page, "steps": steps, "ms_avg": sum(ms) / len(ms), "ms_min": ms[0], "ms_median": ms[len(ms) // 2]}
+    line = {"only": name, "window": window, "page": page, "fp8": fp8, "steps": steps, "ms_avg": sum(ms) / len(ms), "ms_min": ms[0], "ms_median": ms[len(ms) // 2]}
     if rate is not None:
         work, unit = rate
         scale = 1e12 if unit == "TFLOP/s" else 1e9
@@ -242,7 +258,7 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only; run with --gpus 1"}))
         sys.exit(2)
     if args.only:
-        run_only(args.only, args.steps, args.warmup, args.window, args.page)
+        run_only(args.only, args.steps, args.warmup, args.window, args.page, args.fp8)
         return
     import torch
 
