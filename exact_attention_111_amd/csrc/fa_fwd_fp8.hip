@@ -18,7 +18,8 @@
 //     wave keeps its Q rows as B operands: lane (half, col) holds dims 64 ks + 32 half ..
 //     + 31 of query row col (the operands' byte t of half h pair up in the product).
 //   * 64-key K and V tiles (8 KB each) stream through a 4-stage LDS ring filled by direct
-//     buffer-to-LDS loads three tiles ahead, one barrier per tile.
+//     buffer-to-LDS loads three tiles ahead, one barrier per tile. The S products of the next
+//     tile are issued before the softmax of the current one (software pipeline).
 //   * S^T = K Q^T: K rows read 32 bytes at a time (two 128-bit reads); accumulator element
 //     r of key block kb is key 32 kb + 8 (r / 4) + 4 half + r % 4 of query col.
 //   * P^T as the B operand of O^T += V^T P^T: byte 16 kb + r of a lane is that element's
@@ -46,7 +47,10 @@ constexpr int kF8BM = 32 * kF8NW;      // query rows per workgroup
 constexpr int kF8BN = 64;              // keys per tile
 constexpr int kF8Tile = kF8BN * kF8D;  // bytes of a K or V tile
 constexpr int kF8Stage = 2 * kF8Tile;  // K | V
-constexpr int kF8NS = 4;               // stages in the ring
+#ifndef FA_FP8_NS
+#define FA_FP8_NS 4
+#endif
+constexpr int kF8NS = FA_FP8_NS;       // stages in the ring
 constexpr int kF8KS = kF8D / 64;       // 32x32x64 k-steps over d
 constexpr int kF8NB = kF8D / 32;       // 32-wide blocks of O^T
 static_assert(kF8Tile == 1024 * kF8NW, "one 1 KB direct load per wave and tile");
@@ -176,17 +180,9 @@ __global__ __launch_bounds__(kF8NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   for (int t = 0; t < kF8NS - 1; ++t)
     if (t < ntk) issue(t);
 
-  for (int t = 0; t < ntk; ++t) {
-    if (t + kF8NS - 1 <= ntk) wait_vmcnt<(kF8NS - 2) * 2>();
-    else wait_vmcnt<0>();
-    lds_barrier();
-    if (t + kF8NS - 1 < ntk) issue(t + kF8NS - 1);
+  // S^T of tile t (K from its slot) and its mask on boundary tiles (selects).
+  auto scores = [&](int t, f32x16 (&s)[2]) {
     const char* kt = smem + (t % kF8NS) * kF8Stage;
-    const char* vt = kt + kF8Tile;
-    const int k0 = kbase + t * kF8BN;
-
-    // S^T for the two 32-key blocks.
-    f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = f32x16{};
@@ -198,25 +194,54 @@ __global__ __launch_bounds__(kF8NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
         s[kb] = mfma_f8(ka, qf[ks], s[kb]);
       }
     }
-    // Mask boundary tiles (selects).
+  };
+  auto mask = [&](int t, f32x16 (&s)[2]) {
+    const int k0 = kbase + t * kF8BN;
     const bool need_mask = (k0 + kF8BN > n_kv) || (a.causal && k0 + kF8BN - 1 > qw0 + delta) ||
                            (a.window > 0 && k0 < qw0 + 32 + delta - a.window);
-    if (need_mask) {
+    if (!need_mask) return;
+    // visible: lo <= (key - base) < lim, with base the lane's first key of the tile
+    const int base = k0 + 4 * half;
+    const int lim = min(n_kv - base, a.causal ? my_q + delta + 1 - base : n_kv - base);
+    const int lo = a.window > 0 ? my_q + delta - a.window + 1 - base : -kF8BN;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = k0 + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
-          const bool vis = j < n_kv && (!a.causal || j <= my_q + delta) && (a.window <= 0 || j > my_q + delta - a.window);
-          s[kb][r] = vis ? s[kb][r] : kNegInf;
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
+        s[kb][r] = (off >= lim || off < lo) ? kNegInf : s[kb][r];
+      }
+  };
+
+  // Software pipeline: iteration t issues the S products of tile t + 1 before the softmax of
+  // tile t, so a wave's own matrix-core work runs under its VALU work; then P V of tile t.
+  // Tile t + 1's K|V stage must have landed at iteration t, and the slot refilled there (of
+  // tile t + 3) was last read at iteration t - 1.
+  f32x16 sc[2], sn[2];
+  if (ntk > 0) {
+    if (kF8NS - 1 <= ntk) wait_vmcnt<(kF8NS - 2) * 2>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+    scores(0, sc);
+    mask(0, sc);
+  }
+  for (int t = 0; t < ntk; ++t) {
+    const bool more = t + 1 < ntk;
+    if (more) {
+      if (t + 2 < ntk) wait_vmcnt<2>();  // stage t + 2 may stay in flight
+      else wait_vmcnt<0>();
+      lds_barrier();
+      if (t + kF8NS - 1 < ntk) issue(t + kF8NS - 1);
+      scores(t + 1, sn);
     }
+    const char* vt = smem + (t % kF8NS) * kF8Stage + kF8Tile;
+
     // Integer reference: raised to ceil(tile max) when the tile passes it.
     float mx = kNegInf;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
     mx = max_of_halves(mx) * c;
     const float m_new = mx > m ? ceilf(mx) : m;
     // 0 when there was no reference, 1 when unchanged, else an exact power of two
@@ -239,7 +264,7 @@ __global__ __launch_bounds__(kF8NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int T = 4 * i + e;
-        x[e] = exp2_hw(fmaf(s[T >> 4][T & 15], c, off));
+        x[e] = exp2_hw(fmaf(sc[T >> 4][T & 15], c, off));
         l += x[e];
       }
       int word = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
@@ -256,6 +281,11 @@ __global__ __launch_bounds__(kF8NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
       const i32x2 r3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vt + vaddr[1][nb] + 32 * kF8D));
       const i32x8 va = {r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
       oacc[nb] = mfma_f8(va, pb, oacc[nb]);
+    }
+    if (more) {
+      mask(t + 1, sn);
+      sc[0] = sn[0];
+      sc[1] = sn[1];
     }
   }
   if (ntk > 0) wait_vmcnt<0>();
