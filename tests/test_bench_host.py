@@ -21,7 +21,8 @@ def test_traffic_record_matches_sources_or_is_withheld(monkeypatch):
         rec, src = bench.traffic_record(part)
         if rec is not None:  # a committed profile of exactly these sources
             assert rec["source_sha256_16"] == bench.source_digest(part)
-            assert rec["bytes_per_launch"] == rec["read_bytes_per_launch"] + rec["write_bytes_per_launch"]
+            # each of the three is rounded to whole bytes on its own
+            assert abs(rec["bytes_per_launch"] - rec["read_bytes_per_launch"] - rec["write_bytes_per_launch"]) <= 1
             assert src.startswith("profiles" + os.sep)
     # once a kernel source differs from the profiled one, no traffic figure is reported
     monkeypatch.setattr(bench, "source_digest", lambda part: "0" * 16)
