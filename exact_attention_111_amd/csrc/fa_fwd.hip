@@ -98,7 +98,9 @@ struct FwdArgs {
   const int32_t* seqlens;
 };
 
-template <int D, typename IT, typename OT>
+// WIN: a sliding window is in force (a.window > 0). Only then can a row meet its first
+// visible key after the first tile; the window-free kernel leaves that test out.
+template <int D, typename IT, typename OT, bool WIN>
 __global__ __launch_bounds__(FwdCfg<D>::NT)
 __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_PER_SIMD))) void fwd_kernel(const FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
@@ -143,7 +145,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
   }
   kv_end = __builtin_amdgcn_readfirstlane(kv_end);  // uniform: keeps load setup in SGPRs
   const int kbase = __builtin_amdgcn_readfirstlane(
-      a.window > 0 ? (max(q0 + delta - a.window + 1, 0) / C::BN) * C::BN : 0);
+      WIN ? (max(q0 + delta - a.window + 1, 0) / C::BN) * C::BN : 0);
   const int ntk = max((kv_end - kbase + C::BN - 1) / C::BN, 0);
 
   const IT* __restrict__ qp = static_cast<const IT*>(a.q) + (size_t)(b * a.H + h) * a.Lq * D;
@@ -195,11 +197,15 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
     for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[qb][nb][r] = 0.f;
-  float m[QB], l[QB];  // reference (scaled, base 2) and this lane's part of the row sum
+  // Per row: the reference m (scaled, base 2), the shift nm applied before each exp (-m, or
+  // 0 while the row has no reference), and this lane's part of the row sum l as two
+  // interleaved chains of adds (elements of even and of odd index).
+  float m[QB], nm[QB], lc[QB][2];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     m[qb] = kNegInf;
-    l[qb] = 0.f;
+    nm[qb] = 0.f;
+    lc[qb][0] = lc[qb][1] = 0.f;
   }
   f32x16 sa[QB][2], sb[QB][2];  // S^T (then scaled, shifted scores) of two consecutive tiles
   bf16x8 pb[QB][4];              // P^T of the tile whose P V runs next
@@ -274,14 +280,14 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
   auto mask_tile = [&](int t, f32x16 (&sx)[QB][2]) {
     const int k0 = kbase + t * C::BN;
     if (!((k0 + C::BN > n_kv) || (a.causal && k0 + C::BN - 1 > qw0 + delta) ||
-          (a.window > 0 && k0 < qw0 + 32 * QB + delta - a.window)))
+          (WIN && k0 < qw0 + 32 * QB + delta - a.window)))
       return;  // uniform
     const int base = k0 + 4 * half;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       // visible: lo <= (offset from base) < lim
       const int lim = min(n_kv - base, a.causal ? my_q[qb] + delta + 1 - base : n_kv - base);
-      const int lo = a.window > 0 ? my_q[qb] + delta - a.window + 1 - base : -C::BN;
+      const int lo = WIN ? my_q[qb] + delta - a.window + 1 - base : -C::BN;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -305,11 +311,11 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
       float mx = fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
       // lanes l and l ^ 32 hold the same row
       m[qb] = max_of_halves(mx) * a.scale_log2;
-      const float neg_m = (m[qb] == kNegInf) ? 0.f : -m[qb];
+      nm[qb] = (m[qb] == kNegInf) ? 0.f : -m[qb];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sx[qb][kb][r] = fmaf(sx[qb][kb][r], a.scale_log2, neg_m);
+        for (int r = 0; r < 16; ++r) sx[qb][kb][r] = fmaf(sx[qb][kb][r], a.scale_log2, nm[qb]);
     }
   };
   // The two halves of a body, written out step by step. A region is one step per MFMA
@@ -329,35 +335,52 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
   auto elem = [](const f32x16 (&x)[QB][2], int e) { return x[e / 32][(e % 32) / 16][e % 16]; };
   // Keep running sums where they are computed: without this, chains of adds are linearised
   // after the region's last MFMA, where nothing else overlaps them.
-  auto pin_partials = [](float (&x)[QB][4]) {
+  auto pin_sums = [&] {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(x[qb][i]));
+      for (int i = 0; i < 2; ++i) asm volatile("" : "+v"(lc[qb][i]));
   };
-  // Row-sum partial and bf16 P^T operand of element e, whose p is in pv[e].
-  auto sum_elem = [&](const float (&pv)[kElems], int e, float (&rs)[QB][4]) {
+  // Row-sum add and bf16 P^T operand of element e, whose p is in pv[e].
+  auto sum_elem = [&](const float (&pv)[kElems], int e) {
     const int qb = e / 32, h = (e % 32) / 16, r = e % 16;
-    rs[qb][e & 3] += pv[e];
+    lc[qb][e & 1] += pv[e];
     pb[qb][2 * h + (r >> 3)][r & 7] = (__bf16)pv[e];
+  };
+  // The rows' sums as they stood before a part was added (kept for the rare rescale).
+  auto snapshot = [&](float (&lo)[QB][2]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) lo[qb][0] = lc[qb][0], lo[qb][1] = lc[qb][1];
   };
 
   // Softmax without a per-tile maximum. Scores are shifted by the row's current reference m
-  // before anyone looks at the tile, p = 2^(s*scale*log2(e) - m) is formed, and only then is
-  // the part checked: it stands unless some p went past kMaxP (or is not a number), or the
-  // row had no reference yet. Otherwise (rare after a row's first tile; a wave-uniform
-  // branch) the row's reference is raised to the part's maximum, l and o are rescaled at
-  // once, and the part's p are recomputed. Parts whose p stayed at or below 2^32 keep fp32
-  // far from overflow (l <= keys * 2^32). Elements [E0, E1) of `cu` have been exponentiated
-  // (sums in rs); [E1, E2) are still to be, and are shifted along with them.
-  constexpr float kMaxP = 4294967296.f;
-  auto fix_part = [&](f32x16 (&cu)[QB][2], auto e0c, auto e1c, auto e2c, float (&rs)[QB][4]) {
-    constexpr int E0 = decltype(e0c)::value, E1 = decltype(e1c)::value, E2 = decltype(e2c)::value;
+  // before anyone looks at the tile, p = 2^(s*scale*log2(e) - m) is formed and added to the
+  // row sum, and only then is the part checked: it stands unless a chain of the row sum went
+  // past kMaxL (or is not a number: some p overflowed), or, with a sliding window, the row
+  // has no reference yet and the tile holds keys it can see. Otherwise (rare after a row's
+  // first tile; a wave-uniform branch) the row's reference is raised to the part's maximum,
+  // l and o are rescaled at once, and the part's p are recomputed. A chain at or below 2^40
+  // bounds every p and l far from fp32 overflow, and its test costs two compares per part.
+  // Elements [E0, E1) of `cu` have been exponentiated (added to lc, which held `lo` before);
+  // [E1, E2) are still to be, and are shifted along with them. Elements [EP, E0) belong to
+  // an earlier part whose P^T operands are still waiting for their P V k-steps: a rescale
+  // re-derives them against the new reference (o already holds the k-steps that ran, and
+  // is rescaled). k0: the tile's first key.
+  constexpr float kMaxL = 1099511627776.f;  // 2^40
+  auto fix_part = [&](f32x16 (&cu)[QB][2], auto epc, auto e0c, auto e1c, auto e2c, const float (&lo)[QB][2],
+                      int k0) {
+    constexpr int EP = decltype(epc)::value, E0 = decltype(e0c)::value, E1 = decltype(e1c)::value,
+                  E2 = decltype(e2c)::value;
     bool need[QB], any = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      const float sum = (rs[qb][0] + rs[qb][1]) + (rs[qb][2] + rs[qb][3]);
-      need[qb] = !(sum <= kMaxP) || (m[qb] == kNegInf && sum > 0.f);
+      need[qb] = !(lc[qb][0] <= kMaxL) || !(lc[qb][1] <= kMaxL);
+      if constexpr (WIN) {
+        // A row's first visible keys may all give p = 0 against the provisional shift of 0
+        // (scores far below zero), so the test is on the keys, not on the sum.
+        const int last = my_q[qb] + delta;  // the row's newest visible key
+        need[qb] = need[qb] || (m[qb] == kNegInf && last - a.window + 1 < k0 + C::BN && last >= k0 && k0 < n_kv);
+      }
       any |= need[qb];
     }
     if (__builtin_amdgcn_ballot_w64(any) == 0) return;  // the fast path holds for every row
@@ -372,19 +395,29 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
       const bool row_need = any_of_halves(need[qb]) && mx != kNegInf;
       float d = 0.f, al = 1.f;
       if (row_need) {
-        const float base = (m[qb] == kNegInf) ? 0.f : m[qb];  // the scores were shifted by -base
-        const float m_new = base + mx;
-        al = exp2_hw(m[qb] - m_new);  // 0 for a row without a reference (l, o are 0 then)
-        m[qb] = m_new;
-        d = mx;
+        if (m[qb] == kNegInf) {  // first reference: the scores were shifted by 0; l, o are 0
+          m[qb] = mx;
+          d = mx;
+          al = 0.f;
+        } else if (mx > 0.f) {   // raise only: the scores were shifted by -m
+          m[qb] += mx;
+          d = mx;
+          al = exp2_hw(-mx);
+        }
+        nm[qb] = -m[qb];
       }
-      l[qb] *= al;
+      lc[qb][0] = lo[qb][0] * al;
+      lc[qb][1] = lo[qb][1] * al;
 #pragma unroll
       for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[qb][nb][r] *= al;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) rs[qb][i] = 0.f;
+      for (int e = EP; e < E0; ++e) {
+        if (e / 32 != qb) continue;
+        const int h = (e % 32) / 16, r = e % 16;
+        pb[qb][2 * h + (r >> 3)][r & 7] = (__bf16)exp2_hw(cu[qb][h][r] - d);
+      }
 #pragma unroll
       for (int e = E0; e < E2; ++e) {
         if (e / 32 != qb) continue;
@@ -392,7 +425,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
         cu[qb][h][r] -= d;
         if (e < E1) {
           const float pe = exp2_hw(cu[qb][h][r]);
-          rs[qb][e & 3] += pe;
+          lc[qb][e & 1] += pe;
           pb[qb][2 * h + (r >> 3)][r & 7] = (__bf16)pe;
         }
       }
@@ -402,15 +435,12 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
   // Region X: S^T of the next tile into `nx`, beside p = 2^t, the row sums and the bf16 P^T
   // operands of most of the current tile `cu` (whose scores were shifted in region Y), and
   // the check of that part.
-  auto region_x = [&](int ksl, f32x16 (&nx)[QB][2], f32x16 (&cu)[QB][2], auto&& mid) {
+  auto region_x = [&](int ksl, f32x16 (&nx)[QB][2], f32x16 (&cu)[QB][2], int k0, auto&& mid) {
     constexpr int NF = C::NKF;
     const f32x16 zero = {};
     float pv[kElems];  // p of element e, between its exp and its sum / conversion
-    float rs[QB][4];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) rs[qb][i] = 0.f;
+    float lo[QB][2];
+    snapshot(lo);
     bf16x8 buf[kPF];
 #pragma unroll
     for (int f = 0; f < kPF; ++f) buf[f] = read_k(ksl, f);
@@ -425,21 +455,20 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
       // This step's exps; the sums and conversions of the previous step's (their results
       // are ready by now, so the wave does not stall on them).
 #pragma unroll
-      for (int e = (f - 1) * kExpX / NF; f > 0 && e < f * kExpX / NF; ++e) sum_elem(pv, e, rs);
+      for (int e = (f - 1) * kExpX / NF; f > 0 && e < f * kExpX / NF; ++e) sum_elem(pv, e);
 #pragma unroll
       for (int e = f * kExpX / NF; e < (f + 1) * kExpX / NF; ++e) pv[e] = exp2_hw(elem(cu, e));
-      pin_partials(rs);
+      pin_sums();
       if (f == kDmaStep) mid();
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int e = (NF - 1) * kExpX / NF; e < kExpX; ++e) sum_elem(pv, e, rs);
-    fix_part(cu, std::integral_constant<int, 0>{}, std::integral_constant<int, kExpX>{},
-             std::integral_constant<int, kElems>{}, rs);
+    for (int e = (NF - 1) * kExpX / NF; e < kExpX; ++e) sum_elem(pv, e);
+    fix_part(cu, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{},
+             std::integral_constant<int, kExpX>{}, std::integral_constant<int, kElems>{}, lo, k0);
+    pin_sums();
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      l[qb] += (rs[qb][0] + rs[qb][1]) + (rs[qb][2] + rs[qb][3]);
-      asm volatile("" : "+v"(l[qb]));
 #pragma unroll
       for (int i = 0; i < 4; ++i)  // operands completed here (the rest are written in region Y)
         if (32 * qb + 8 * i + 8 <= kExpX) asm volatile("" : "+v"(pb[qb][i]));
@@ -450,19 +479,18 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
   // Region Y: O^T += V^T P^T of the current tile `cu` (V tile at byte `vs` of the V slots),
   // beside the rest of `cu`'s exp work and its check (first half of the steps), then
   // t = s * scale*log2(e) - m in place for the next tile `nx` (second half).
-  auto region_y = [&](int vs, f32x16 (&nx)[QB][2], f32x16 (&cu)[QB][2], auto&& mid) {
+  auto region_y = [&](int vs, f32x16 (&nx)[QB][2], f32x16 (&cu)[QB][2], int k0, auto&& mid) {
     constexpr int NF = C::NVF;
     constexpr int NM = NF / 2;                       // steps of the leftover exps; the check
     constexpr int NS = NF - NM - 1;                  // steps of the shift
     constexpr int EPF = (32 * QB + NS - 1) / NS;     // elements per shift step
     constexpr int NE = kElems - kExpX;               // exp elements left over from region X
-    float pv[kElems], rs[QB][4], neg_m[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      neg_m[qb] = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) rs[qb][i] = 0.f;
-    }
+    // P^T operands not yet consumed when the leftover part is checked (operand i holds
+    // elements 8 i .. 8 i + 7 and feeds k-step i, which starts at step i * NB)
+    constexpr int kPend = 8 * (NM / C::NB);
+    static_assert(QB == 1 && NM % C::NB == 0 && kPend <= kExpX, "pending operands of region X");
+    float pv[kElems], lo[QB][2];
+    snapshot(lo);
     bf16x8 buf[kPF];
 #pragma unroll
     for (int f = 0; f < kPF; ++f) buf[f] = read_v(vs, f);
@@ -472,14 +500,10 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
       if (f == NM) {
         // The leftover part is complete: check it before the P V k-steps that read it.
 #pragma unroll
-        for (int e = kExpX + (NM - 1) * NE / NM; e < kElems; ++e) sum_elem(pv, e, rs);
-        fix_part(cu, std::integral_constant<int, kExpX>{}, std::integral_constant<int, kElems>{},
-                 std::integral_constant<int, kElems>{}, rs);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          l[qb] += (rs[qb][0] + rs[qb][1]) + (rs[qb][2] + rs[qb][3]);
-          neg_m[qb] = (m[qb] == kNegInf) ? 0.f : -m[qb];  // a row without a reference shifts by 0
-        }
+        for (int e = kExpX + (NM - 1) * NE / NM; e < kElems; ++e) sum_elem(pv, e);
+        fix_part(cu, std::integral_constant<int, kPend>{}, std::integral_constant<int, kExpX>{},
+                 std::integral_constant<int, kElems>{}, std::integral_constant<int, kElems>{}, lo, k0);
+        pin_sums();
         __builtin_amdgcn_sched_barrier(0);
       }
       const bf16x8 x = buf[f % kPF];
@@ -489,16 +513,16 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
       for (int qb = 0; qb < QB; ++qb) oacc[qb][nb] = mfma_32x32x16(x, pb[qb][ks], oacc[qb][nb]);
       if (f < NM) {
 #pragma unroll
-        for (int e = kExpX + (f - 1) * NE / NM; f > 0 && e < kExpX + f * NE / NM; ++e) sum_elem(pv, e, rs);
+        for (int e = kExpX + (f - 1) * NE / NM; f > 0 && e < kExpX + f * NE / NM; ++e) sum_elem(pv, e);
 #pragma unroll
         for (int e = kExpX + f * NE / NM; e < kExpX + (f + 1) * NE / NM; ++e) pv[e] = exp2_hw(elem(cu, e));
-        pin_partials(rs);
+        pin_sums();
       } else if (f > NM) {
         const int s0 = (f - NM - 1) * EPF;
 #pragma unroll
         for (int e = s0; e < s0 + EPF && e < kElems; ++e) {
           const int qb = e / 32, h = (e % 32) / 16, r = e % 16;
-          nx[qb][h][r] = fmaf(nx[qb][h][r], a.scale_log2, neg_m[qb]);
+          nx[qb][h][r] = fmaf(nx[qb][h][r], a.scale_log2, nm[qb]);
         }
       }
       if (f == kDmaStep) mid();
@@ -506,7 +530,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      asm volatile("" : "+v"(l[qb]), "+v"(m[qb]));
+      asm volatile("" : "+v"(lc[qb][0]), "+v"(lc[qb][1]), "+v"(m[qb]), "+v"(nm[qb]));
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) asm volatile("" : "+v"(nx[qb][kb]));
     }
@@ -538,11 +562,12 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
     auto load_k = [&] { if (ld_k) stage(j + 3, 0, (u % 3) * C::TILE_BYTES); };        // slot of tile j + 3
     auto load_v = [&] { if (ld_v) stage(j + 2, 1, (3 + (u + 2) % 3) * C::TILE_BYTES); };  // slot of tile j + 2
     __builtin_amdgcn_sched_barrier(0);
-    region_x(ksl_next, nxt, cur, load_k);
+    const int k0 = kbase + j * C::BN;  // tile j's first key
+    region_x(ksl_next, nxt, cur, k0, load_k);
     if (j + 1 < ntk) mask_tile(j + 1, nxt);
     __builtin_amdgcn_sched_barrier(0);
     if (w >= C::NW / 2) __builtin_amdgcn_s_setprio(1);  // the wave that finished region X later goes first
-    region_y(vsl_cur, nxt, cur, load_v);
+    region_y(vsl_cur, nxt, cur, k0, load_v);
     __builtin_amdgcn_s_setprio(0);
     // Wait for this wave's loads issued one iteration ago (K tile j + 2, V tile j + 1; the
     // ones just issued may stay in flight), then the barrier makes everyone's visible and
@@ -592,7 +617,8 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
   // no key get O = 0 and LSE = -inf.
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const float lt = l[qb] + __shfl_xor(l[qb], 32);
+    const float lh = lc[qb][0] + lc[qb][1];
+    const float lt = lh + __shfl_xor(lh, 32);
     const bool row_ok = (my_q[qb] < n_q) && (lt > 0.f);
     const float inv = row_ok ? 1.f / lt : 0.f;
     if (my_q[qb] < a.Lq) {
@@ -614,7 +640,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
 #endif
 }
 
-template <int D, typename IT, typename OT>
+template <int D, typename IT, typename OT, bool WIN>
 hipError_t launch(const FwdParams& p, hipStream_t stream) {
   using C = FwdCfg<D>;
   FwdArgs a;
@@ -630,20 +656,25 @@ hipError_t launch(const FwdParams& p, hipStream_t stream) {
   if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   a.nwg = (int)nwg;
   void* args[] = {&a};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_kernel<D, IT, OT>), dim3((unsigned)nwg), dim3(C::NT),
+  return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_kernel<D, IT, OT, WIN>), dim3((unsigned)nwg), dim3(C::NT),
                          args, 0, stream);
 }
 
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {
-  if (p.d == 64) return launch<64, __bf16, __bf16>(p, stream);
-  return launch<128, __bf16, __bf16>(p, stream);
+  if (p.window > 0) {
+    if (p.d == 64) return launch<64, __bf16, __bf16, true>(p, stream);
+    return launch<128, __bf16, __bf16, true>(p, stream);
+  }
+  if (p.d == 64) return launch<64, __bf16, __bf16, false>(p, stream);
+  return launch<128, __bf16, __bf16, false>(p, stream);
 }
 
 hipError_t launch_fwd_f32(const FwdParams& p, hipStream_t stream) {
-  if (p.d == 64) return launch<64, float, float>(p, stream);
-  return launch<128, float, float>(p, stream);
+  if (p.window > 0) return hipErrorInvalidValue;  // the fp32 entry point has no window
+  if (p.d == 64) return launch<64, float, float, false>(p, stream);
+  return launch<128, float, float, false>(p, stream);
 }
 
 }  // namespace fa

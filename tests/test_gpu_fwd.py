@@ -206,6 +206,32 @@ def test_scores_growing_across_tiles(d, causal):
     compare(o, lse, O, LSE, bf16_out=True, what=f"growing scores d{d} c{int(causal)}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_scores_jumping_in_last_keys_of_tiles(d, causal):
+    """Only keys 48..63 of each 64-key tile (after the first) score about 60 higher in base 2
+    than the rest, so within a tile the first keys' probabilities stay small and the row's
+    reference has to rise when the last keys arrive, after part of the tile's P V product
+    has run. Probabilities of the tile's earlier keys still waiting for their product must be
+    taken against the raised reference."""
+    fa = _fa()
+    B, H, L = 1, 2, 600
+    announce(entry="fa_fwd", case="scores jumping in last keys of tiles", B=B, H=H, L=L, d=d, causal=causal)
+    g = torch.Generator().manual_seed(183)
+    q = torch.randn(B, H, L, d, generator=g) * 0.5
+    k = torch.randn(B, H, L, d, generator=g) * 0.5
+    v = torch.randn(B, H, L, d, generator=g)
+    scale = 1.0 / math.sqrt(d)
+    q[..., 0] = 4.0 / scale
+    j = torch.arange(L)
+    k[..., 0] = torch.where((j >= 64) & (j % 64 >= 48), torch.full((L,), 10.5), torch.zeros(L))
+    q, k, v = (t.to(torch.bfloat16).to(DEV) for t in (q, k, v))
+    o, lse = fa.fwd(q, k, v, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    O, LSE = oracle.attention(*(fa_inputs.as_oracle_f64(t) for t in (q, k, v)), scale=scale, causal=causal)
+    compare(o, lse, O, LSE, bf16_out=True, what=f"jumping last keys d{d} c{int(causal)}")
+
+
 def test_uniform_attention_closed_form():
     """Q = 0: every visible key has weight 1/#visible, so O_i is a prefix mean of V and
     LSE_i = ln(i + 1) under the causal mask."""

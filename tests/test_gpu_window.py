@@ -158,3 +158,28 @@ def test_window_backward_varlen_unequal():
         compare_grad(dq, dQ, f"dQ {Lq}x{Lk}")
         compare_grad(dk, dK, f"dK {Lq}x{Lk}")
         compare_grad(dv, dV, f"dV {Lq}x{Lk}")
+
+
+@pytest.mark.parametrize("W", [0, 16, 100])
+def test_scores_far_below_zero(W):
+    """Every score is about -100 (natural log units), so 2^(s * scale * log2 e) underflows to
+    zero when taken against a shift of 0. With a narrow window most rows of a query tile meet
+    their first visible key after the tile's first key tile; they must still take a reference
+    from those keys rather than keep an all-zero sum (LSE would read -inf)."""
+    fa = _fa()
+    B, H, L, d = 1, 2, 400, 128
+    announce(entry="fa_fwd_sliding_window" if W else "fa_fwd", case="scores far below zero", B=B, H=H, L=L, d=d, W=W)
+    g = torch.Generator().manual_seed(470 + W)
+    q = torch.randn(B, H, L, d, generator=g) * 0.5
+    k = torch.randn(B, H, L, d, generator=g) * 0.5
+    v = torch.randn(B, H, L, d, generator=g)
+    scale = 1.0 / math.sqrt(d)
+    q[..., 0] = 10.0 / scale
+    k[..., 0] = -10.0
+    q, k, v = (t.to(torch.bfloat16).to(DEV) for t in (q, k, v))
+    o, lse = fa.fwd(q, k, v, causal=True, scale=scale, window=W or None)
+    torch.cuda.synchronize()
+    O, LSE = oracle.attention(*(fa_inputs.as_oracle_f64(t) for t in (q, k, v)), scale=scale, causal=True,
+                              window=W or None)
+    assert np.isfinite(LSE).all() and LSE.max() < -80
+    compare(o, lse, O, LSE, bf16_out=True, what=f"scores far below zero W{W}")
