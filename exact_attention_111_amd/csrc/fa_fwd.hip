@@ -56,6 +56,10 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
+#ifndef FA_FWD_WAVES
+#define FA_FWD_WAVES 8
+#endif
+static_assert(FA_FWD_WAVES == 8 || FA_FWD_WAVES == 4, "8 waves: one workgroup per CU; 4: two per CU");
 template <int D>
 struct FwdCfg {
   // 32 rows per wave and 8 waves, two per SIMD: a wave fits in 256 registers, which also
@@ -63,9 +67,10 @@ struct FwdCfg {
   // AGPR form and copies every score tile into VGPRs for the softmax). A workgroup covers
   // 256 query rows, which sets how often each K/V tile is streamed from L2 into LDS.
   static constexpr int QB = 1;                    // 32-row query blocks per wave
-  static constexpr int NW = 8;                    // waves per workgroup
-  static constexpr int BM = 32 * QB * NW;         // query rows per workgroup (256)
-  static constexpr int WAVES_PER_SIMD = NW / 4;
+  static constexpr int NW = FA_FWD_WAVES;         // waves per workgroup
+  static constexpr int BM = 32 * QB * NW;         // query rows per workgroup
+  static constexpr int WAVES_PER_SIMD = 2;
+  static constexpr int NS = NW == 8 ? 3 : 2;      // LDS slots for K tiles (and as many for V)
   static constexpr int BN = 64;                   // keys per tile
   static constexpr int NT = NW * 64;              // threads
   static constexpr int ROWB = D * 2;              // bytes per K/V row
@@ -107,7 +112,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
   using C = FwdCfg<D>;
   constexpr int QB = C::QB;
   // [K slots 0-2 | V slots 0-2]
-  __shared__ __attribute__((aligned(1024))) char smem[6 * C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * C::NS * C::TILE_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -129,7 +134,11 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
   }
   const int delta = a.Lk - a.Lq;  // bottom-right causal alignment
   const int q0 = qt * C::BM;
-  const int qw0 = q0 + 32 * QB * w;  // first query row of this wave
+  // Row block of this wave. Waves w and w + NW/2 share a SIMD; giving them blocks s and
+  // NW - 1 - s pairs a top block of the tile with a bottom one, so that on causal diagonal
+  // tiles every SIMD has the same amount of work left after its waves' last visible keys.
+  const int rblk = w < C::NW / 2 ? w : 3 * C::NW / 2 - 1 - w;
+  const int qw0 = q0 + 32 * QB * rblk;  // first query row of this wave
   int my_q[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) my_q[qb] = qw0 + 32 * qb + col;
@@ -147,6 +156,8 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
   const int kbase = __builtin_amdgcn_readfirstlane(
       WIN ? (max(q0 + delta - a.window + 1, 0) / C::BN) * C::BN : 0);
   const int ntk = max((kv_end - kbase + C::BN - 1) / C::BN, 0);
+  // Newest key any row of this wave can see (every key of the tile range without a causal mask)
+  const int wave_last_key = __builtin_amdgcn_readfirstlane(a.causal ? qw0 + 32 * QB - 1 + delta : kv_end);
 
   const IT* __restrict__ qp = static_cast<const IT*>(a.q) + (size_t)(b * a.H + h) * a.Lq * D;
   const IT* __restrict__ kp = uniform_ptr(static_cast<const IT*>(a.k) + (size_t)(b * a.Hkv + kvh) * a.Lk * D);
@@ -175,7 +186,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
 #pragma unroll
   for (int nb = 0; nb < C::NB; ++nb) {
     const int dim = 32 * nb + 16 * (g & 1) + 4 * (sl & 3);
-    vaddr[nb] = 3 * C::TILE_BYTES + vrow * C::ROWB + (((dim >> 3) ^ v_xor<D>(vrow)) << 4) + ((dim & 4) << 1);
+    vaddr[nb] = C::NS * C::TILE_BYTES + vrow * C::ROWB + (((dim >> 3) ^ v_xor<D>(vrow)) << 4) + ((dim & 4) << 1);
   }
   // Direct-load source offsets within a tile (bytes from the tile's first row): segment i
   // of this wave puts 16 bytes at LDS byte seg * 1024 + 16 * lane, holding row r's logical
@@ -212,8 +223,8 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
 
   // K and V tile t live in slot t % 3 (K slots first, then V slots), so loads can run two
   // tiles ahead of their use.
-  auto k_slot = [&](int t) { return (t % 3) * C::TILE_BYTES; };
-  auto v_slot = [&](int t) { return (3 + t % 3) * C::TILE_BYTES; };
+  auto k_slot = [&](int t) { return (t % C::NS) * C::TILE_BYTES; };
+  auto v_slot = [&](int t) { return (C::NS + t % C::NS) * C::TILE_BYTES; };
 
   // Stage K tile t (which = 0) or V tile t (which = 1) into the slot at byte `slot` of the
   // LDS buffer. bf16 input: branch-free direct loads through a buffer resource that ends at
@@ -538,44 +549,61 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
   };
 
   // Tile j: region X = S of tile j + 1 beside the exp half of tile j's softmax; region Y =
-  // P V of tile j beside the max half of tile j + 1's softmax. Loads of K tile j + 2 and V
-  // tile j + 1 stream in meanwhile. `uc` is j mod 6 as a compile-time constant (the loop is
-  // unrolled six times, the period of the 3 slots and the 2 score buffers), which makes
-  // every slot offset an immediate.
+  // P V of tile j beside the max half of tile j + 1's softmax. Later tiles' loads stream in
+  // meanwhile. `uc` is j mod 6 as a compile-time constant (the loop is unrolled six times, a
+  // period of both the NS slots and the 2 score buffers), which makes every slot offset an
+  // immediate.
+  // End of iteration j: wait for this wave's loads of K tile j + 2 and V tile j + 1 (with
+  // three slots they were issued one iteration ago, and the ones just issued may stay in
+  // flight), then the barrier makes everyone's visible and frees the slots read in it.
+  auto close_tile = [&](bool ld_k, bool ld_v) {
+    if constexpr (C::NS >= 3) {
+      if (ld_k && ld_v) wait_vmcnt<2 * C::SEGS_PER_WAVE>();
+      else if (ld_k || ld_v) wait_vmcnt<C::SEGS_PER_WAVE>();
+      else wait_vmcnt<0>();
+    } else {
+      wait_vmcnt<0>();  // two slots: the loads just issued are read by the next iteration
+    }
+    lds_barrier();
+  };
   auto body = [&](auto uc, int j, f32x16 (&cur)[QB][2], f32x16 (&nxt)[QB][2]) {
     constexpr int u = decltype(uc)::value;
-    constexpr int ksl_next = ((u + 1) % 3) * C::TILE_BYTES;  // K slot of tile j + 1
-    constexpr int vsl_cur = (u % 3) * C::TILE_BYTES;         // V slot of tile j
+    constexpr int NS = C::NS;
+    constexpr int ksl_next = ((u + 1) % NS) * C::TILE_BYTES;  // K slot of tile j + 1
+    constexpr int vsl_cur = (u % NS) * C::TILE_BYTES;         // V slot of tile j
     // Keep the per-lane operand bases opaque to loop-invariant code motion: otherwise every
     // (base + immediate offset) pair is hoisted out of the loop into its own VGPR.
 #pragma unroll
     for (int ks = 0; ks < C::QKS; ++ks) asm volatile("" : "+v"(kaddr[ks]));
 #pragma unroll
     for (int nb = 0; nb < C::NB; ++nb) asm volatile("" : "+v"(vaddr[nb]));
-    // Loads two tiles ahead: K tile j + 3 (read by the S products of iteration j + 2) and
-    // V tile j + 2 (read by the P V products of iteration j + 2), issued inside the regions
+    // Loads NS - 1 tiles ahead: K tile j + NS (read by the S products of iteration j + NS - 1)
+    // and V tile j + NS - 1 (read by the P V products of that iteration), issued inside the regions
     // so that the workgroup's waves do not all queue on the load path at once. bf16 loads
     // are issued even past the last tile (they read nothing), which keeps the regions free
     // of branches; fp32 staging keeps its bounds.
     constexpr bool kAll = sizeof(IT) == 2;
-    const bool ld_k = kAll || j + 3 < ntk, ld_v = kAll || j + 2 < ntk;
-    auto load_k = [&] { if (ld_k) stage(j + 3, 0, (u % 3) * C::TILE_BYTES); };        // slot of tile j + 3
-    auto load_v = [&] { if (ld_v) stage(j + 2, 1, (3 + (u + 2) % 3) * C::TILE_BYTES); };  // slot of tile j + 2
+    const bool ld_k = kAll || j + NS < ntk, ld_v = kAll || j + NS - 1 < ntk;
+    auto load_k = [&] { if (ld_k) stage(j + NS, 0, (u % NS) * C::TILE_BYTES); };                 // tile j + NS
+    auto load_v = [&] { if (ld_v) stage(j + NS - 1, 1, (NS + (u + NS - 1) % NS) * C::TILE_BYTES); };  // j + NS - 1
     __builtin_amdgcn_sched_barrier(0);
     const int k0 = kbase + j * C::BN;  // tile j's first key
     region_x(ksl_next, nxt, cur, k0, load_k);
     if (j + 1 < ntk) mask_tile(j + 1, nxt);
     __builtin_amdgcn_sched_barrier(0);
-    if (w >= C::NW / 2) __builtin_amdgcn_s_setprio(1);  // the wave that finished region X later goes first
+    if (C::NW == 8 && w >= C::NW / 2) __builtin_amdgcn_s_setprio(1);  // the wave that finished region X later goes first
     region_y(vsl_cur, nxt, cur, k0, load_v);
     __builtin_amdgcn_s_setprio(0);
-    // Wait for this wave's loads issued one iteration ago (K tile j + 2, V tile j + 1; the
-    // ones just issued may stay in flight), then the barrier makes everyone's visible and
-    // frees the slots read in this iteration.
-    if (ld_k && ld_v) wait_vmcnt<2 * C::SEGS_PER_WAVE>();
-    else if (ld_k || ld_v) wait_vmcnt<C::SEGS_PER_WAVE>();
-    else wait_vmcnt<0>();
-    lds_barrier();
+    close_tile(ld_k, ld_v);
+  };
+  // A wave whose remaining tiles lie wholly past its rows (causal diagonal) computes nothing
+  // more; it still moves its share of those tiles into LDS and meets every barrier.
+  auto tail_body = [&](int j) {
+    constexpr bool kAll = sizeof(IT) == 2;
+    const bool ld_k = kAll || j + C::NS < ntk, ld_v = kAll || j + C::NS - 1 < ntk;
+    if (ld_k) stage(j + C::NS, 0, k_slot(j + C::NS));
+    if (ld_v) stage(j + C::NS - 1, 1, v_slot(j + C::NS - 1));
+    close_tile(ld_k, ld_v);
   };
 
   if (ntk > 0) {
@@ -589,27 +617,33 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     // Tiles the first iteration does not read yet, kept in flight: K tile 2 and V tile 1.
-    if (2 < ntk) stage(2, 0, k_slot(2));
-    if (1 < ntk) stage(1, 1, v_slot(1));
+    if (C::NS >= 3 && 2 < ntk) stage(2, 0, k_slot(2));
+    if (C::NS >= 3 && 1 < ntk) stage(1, 1, v_slot(1));
     s_mfmas(0, sa);
     mask_tile(0, sa);
     first_shift(sa);
-    // Six bodies per trip, leaving after the body of the last tile.
+    // The first body loads into K slot 0, which every wave has just read.
+    lds_barrier();
+    // Six bodies per trip, leaving after the body of the last tile this wave has keys in.
     using std::integral_constant;
-    for (int j = 0;; j += 6) {
+    const int ntw = __builtin_amdgcn_readfirstlane(
+        min(ntk, max((wave_last_key - kbase) / C::BN + 1, 1)));  // tiles with keys for this wave
+    int j = 0;
+    for (;; j += 6) {
       body(integral_constant<int, 0>{}, j, sa, sb);
-      if (j + 1 >= ntk) break;
+      if (j + 1 >= ntw) { j += 1; break; }
       body(integral_constant<int, 1>{}, j + 1, sb, sa);
-      if (j + 2 >= ntk) break;
+      if (j + 2 >= ntw) { j += 2; break; }
       body(integral_constant<int, 2>{}, j + 2, sa, sb);
-      if (j + 3 >= ntk) break;
+      if (j + 3 >= ntw) { j += 3; break; }
       body(integral_constant<int, 3>{}, j + 3, sb, sa);
-      if (j + 4 >= ntk) break;
+      if (j + 4 >= ntw) { j += 4; break; }
       body(integral_constant<int, 4>{}, j + 4, sa, sb);
-      if (j + 5 >= ntk) break;
+      if (j + 5 >= ntw) { j += 5; break; }
       body(integral_constant<int, 5>{}, j + 5, sb, sa);
-      if (j + 6 >= ntk) break;
+      if (j + 6 >= ntw) { j += 6; break; }
     }
+    for (; j < ntk; ++j) tail_body(j);
     wait_vmcnt<0>();  // loads issued by the last bodies must land before the workgroup ends
   }
 
