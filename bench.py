@@ -369,7 +369,7 @@ def main():
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": tr_p["bytes_per_launch"] if tr_p else None, "traffic_unit": "bytes/launch",
                      "traffic_algorithmic": alg_p, "traffic_source": src_p,
-                     "kernel": "fwd_kernel<128, bf16, bf16>"},
+                     "kernel": "fwd_kernel<128, bf16, bf16, false>"},
         "roofline_decode": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                             "frac": round(gbps / PEAK_HBM_GBPS, 4),
                             "traffic": tr_d["bytes_per_launch"] if tr_d else None, "traffic_unit": "bytes/launch",
