@@ -99,7 +99,10 @@ __global__ __launch_bounds__(kF8NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   }
   const int delta = a.Lk - a.Lq;
   const int q0 = qt * kF8BM;
-  const int qw0 = q0 + 32 * w;
+  // Waves w and w + 4 share a SIMD; they take row blocks s and 7 - s, a top block of the tile
+  // with a bottom one, so that every SIMD is left the same work on causal diagonal tiles.
+  const int rblk = w < kF8NW / 2 ? w : 3 * kF8NW / 2 - 1 - w;
+  const int qw0 = q0 + 32 * rblk;
   const int my_q = qw0 + col;
 
   int kv_end = 0;
@@ -112,6 +115,10 @@ __global__ __launch_bounds__(kF8NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   const int kbase = __builtin_amdgcn_readfirstlane(
       a.window > 0 ? (max(q0 + delta - a.window + 1, 0) / kF8BN) * kF8BN : 0);
   const int ntk = max((kv_end - kbase + kF8BN - 1) / kF8BN, 0);
+  // Tiles this wave has keys in (causal: up to its last row's newest key); past them it only
+  // moves its share of the tiles into LDS and meets the barriers.
+  const int ntw = __builtin_amdgcn_readfirstlane(
+      a.causal ? min(ntk, max((qw0 + 31 + delta - kbase) / kF8BN + 1, 1)) : ntk);
 
   // Combined score factor (base 2) and the output descale.
   const float c = a.scale_log2 * a.q_descale[b * a.H + h] * a.k_descale[b * a.Hkv + kvh];
@@ -225,14 +232,16 @@ __global__ __launch_bounds__(kF8NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     scores(0, sc);
     mask(0, sc);
   }
-  for (int t = 0; t < ntk; ++t) {
-    const bool more = t + 1 < ntk;
+  int t = 0;
+  for (; t < ntw; ++t) {
+    const bool more = t + 1 < ntk;   // another tile for the workgroup
+    const bool mine = t + 1 < ntw;   // and this wave has keys in it
     if (more) {
       if (t + 2 < ntk) wait_vmcnt<2>();  // stage t + 2 may stay in flight
       else wait_vmcnt<0>();
       lds_barrier();
       if (t + kF8NS - 1 < ntk) issue(t + kF8NS - 1);
-      scores(t + 1, sn);
+      if (mine) scores(t + 1, sn);
     }
     const char* vt = smem + (t % kF8NS) * kF8Stage + kF8Tile;
 
@@ -282,10 +291,18 @@ __global__ __launch_bounds__(kF8NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
       const i32x8 va = {r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
       oacc[nb] = mfma_f8(va, pb, oacc[nb]);
     }
-    if (more) {
+    if (mine) {
       mask(t + 1, sn);
       sc[0] = sn[0];
       sc[1] = sn[1];
+    }
+  }
+  for (; t < ntk; ++t) {  // tiles past this wave's rows: loads and barriers only
+    if (t + 1 < ntk) {
+      if (t + 2 < ntk) wait_vmcnt<2>();
+      else wait_vmcnt<0>();
+      lds_barrier();
+      if (t + kF8NS - 1 < ntk) issue(t + kF8NS - 1);
     }
   }
   if (ntk > 0) wait_vmcnt<0>();
