@@ -56,10 +56,6 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
-#ifndef FA_FWD_WAVES
-#define FA_FWD_WAVES 8
-#endif
-static_assert(FA_FWD_WAVES == 8 || FA_FWD_WAVES == 4, "8 waves: one workgroup per CU; 4: two per CU");
 template <int D>
 struct FwdCfg {
   // 32 rows per wave and 8 waves, two per SIMD: a wave fits in 256 registers, which also
@@ -67,10 +63,10 @@ struct FwdCfg {
   // AGPR form and copies every score tile into VGPRs for the softmax). A workgroup covers
   // 256 query rows, which sets how often each K/V tile is streamed from L2 into LDS.
   static constexpr int QB = 1;                    // 32-row query blocks per wave
-  static constexpr int NW = FA_FWD_WAVES;         // waves per workgroup
-  static constexpr int BM = 32 * QB * NW;         // query rows per workgroup
-  static constexpr int WAVES_PER_SIMD = 2;
-  static constexpr int NS = NW == 8 ? 3 : 2;      // LDS slots for K tiles (and as many for V)
+  static constexpr int NW = 8;                    // waves per workgroup (waves w, w + 4 share a SIMD)
+  static constexpr int BM = 32 * QB * NW;         // query rows per workgroup (256)
+  static constexpr int WAVES_PER_SIMD = NW / 4;
+  static constexpr int NS = 3;                    // LDS slots for K tiles (and as many for V)
   static constexpr int BN = 64;                   // keys per tile
   static constexpr int NT = NW * 64;              // threads
   static constexpr int ROWB = D * 2;              // bytes per K/V row
@@ -549,21 +545,17 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
   };
 
   // Tile j: region X = S of tile j + 1 beside the exp half of tile j's softmax; region Y =
-  // P V of tile j beside the max half of tile j + 1's softmax. Later tiles' loads stream in
-  // meanwhile. `uc` is j mod 6 as a compile-time constant (the loop is unrolled six times, a
-  // period of both the NS slots and the 2 score buffers), which makes every slot offset an
-  // immediate.
-  // End of iteration j: wait for this wave's loads of K tile j + 2 and V tile j + 1 (with
-  // three slots they were issued one iteration ago, and the ones just issued may stay in
-  // flight), then the barrier makes everyone's visible and frees the slots read in it.
+  // P V of tile j beside the rest of tile j's exps and the shift of tile j + 1. Loads of K tile
+  // j + 3 and V tile j + 2 stream in meanwhile. `uc` is j mod 6 as a compile-time constant (the
+  // loop is unrolled six times, the period of the 3 slots and the 2 score buffers), which
+  // makes every slot offset an immediate.
+  // End of iteration j: wait for this wave's loads of K tile j + 2 and V tile j + 1 (issued
+  // one iteration ago; the ones just issued may stay in flight), then the barrier makes
+  // everyone's visible and frees the slots read in it.
   auto close_tile = [&](bool ld_k, bool ld_v) {
-    if constexpr (C::NS >= 3) {
-      if (ld_k && ld_v) wait_vmcnt<2 * C::SEGS_PER_WAVE>();
-      else if (ld_k || ld_v) wait_vmcnt<C::SEGS_PER_WAVE>();
-      else wait_vmcnt<0>();
-    } else {
-      wait_vmcnt<0>();  // two slots: the loads just issued are read by the next iteration
-    }
+    if (ld_k && ld_v) wait_vmcnt<2 * C::SEGS_PER_WAVE>();
+    else if (ld_k || ld_v) wait_vmcnt<C::SEGS_PER_WAVE>();
+    else wait_vmcnt<0>();
     lds_barrier();
   };
   auto body = [&](auto uc, int j, f32x16 (&cur)[QB][2], f32x16 (&nxt)[QB][2]) {
@@ -577,8 +569,8 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
     for (int ks = 0; ks < C::QKS; ++ks) asm volatile("" : "+v"(kaddr[ks]));
 #pragma unroll
     for (int nb = 0; nb < C::NB; ++nb) asm volatile("" : "+v"(vaddr[nb]));
-    // Loads NS - 1 tiles ahead: K tile j + NS (read by the S products of iteration j + NS - 1)
-    // and V tile j + NS - 1 (read by the P V products of that iteration), issued inside the regions
+    // Loads two tiles ahead: K tile j + 3 (read by the S products of iteration j + 2) and V
+    // tile j + 2 (read by the P V products of iteration j + 2), issued inside the regions
     // so that the workgroup's waves do not all queue on the load path at once. bf16 loads
     // are issued even past the last tile (they read nothing), which keeps the regions free
     // of branches; fp32 staging keeps its bounds.
@@ -591,7 +583,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
     region_x(ksl_next, nxt, cur, k0, load_k);
     if (j + 1 < ntk) mask_tile(j + 1, nxt);
     __builtin_amdgcn_sched_barrier(0);
-    if (C::NW == 8 && w >= C::NW / 2) __builtin_amdgcn_s_setprio(1);  // the wave that finished region X later goes first
+    if (w >= C::NW / 2) __builtin_amdgcn_s_setprio(1);  // the wave that finished region X later goes first
     region_y(vsl_cur, nxt, cur, k0, load_v);
     __builtin_amdgcn_s_setprio(0);
     close_tile(ld_k, ld_v);
@@ -617,8 +609,8 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     // Tiles the first iteration does not read yet, kept in flight: K tile 2 and V tile 1.
-    if (C::NS >= 3 && 2 < ntk) stage(2, 0, k_slot(2));
-    if (C::NS >= 3 && 1 < ntk) stage(1, 1, v_slot(1));
+    if (2 < ntk) stage(2, 0, k_slot(2));
+    if (1 < ntk) stage(1, 1, v_slot(1));
     s_mfmas(0, sa);
     mask_tile(0, sa);
     first_shift(sa);
