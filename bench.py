@@ -135,6 +135,31 @@ def cpu_baseline(w, x, seconds):
             "seconds": round(dt, 2)}
 
 
+def library_gemm_tflops(dev, n=16384, reps=10):
+    """Context for the matrix-core roofline: a plain bf16 GEMM (n x n x n) through the vendor
+    BLAS behind torch.matmul, on the same GPU in the same run; median of `reps` launches.
+    It shows what a dense bf16 product reaches at the clock this GPU holds under load."""
+    import torch
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b, out=c)
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.matmul(a, b, out=c)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ts.sort()
+    ms = ts[len(ts) // 2]
+    del a, b, c
+    return {"tflops": round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1), "ms": round(ms, 4),
+            "what": f"torch.matmul bf16 {n}x{n}x{n}, median of {reps}"}
+
+
 def _window_pairs(lens, W):
     """Visible (query, key) pairs of causal self-attention with a window of W keys per query,
     summed over sequences of the given lengths: sum over i < n of min(W, i + 1)."""
@@ -333,6 +358,8 @@ def main():
     bwd_flop = BWD_FLOP_PER_FWD * 4.0 * wp.B * wp.H * wp.L * wp.L * wp.d / 2.0
     bwd_tflops = bwd_flop / (bwd_avg * 1e-3) / 1e12
 
+    gemm = library_gemm_tflops(dev)
+
     tr_p, src_p = traffic_record("prefill")
     tr_d, src_d = traffic_record("decode")
     tr_b, src_b = traffic_record("backward")
@@ -369,7 +396,8 @@ def main():
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": tr_p["bytes_per_launch"] if tr_p else None, "traffic_unit": "bytes/launch",
                      "traffic_algorithmic": alg_p, "traffic_source": src_p,
-                     "kernel": "fwd_kernel<128, bf16, bf16, false>"},
+                     "kernel": "fwd_kernel<128, bf16, bf16, false>",
+                     "library_gemm": gemm, "frac_of_library_gemm": round(tflops / gemm["tflops"], 4)},
         "roofline_decode": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                             "frac": round(gbps / PEAK_HBM_GBPS, 4),
                             "traffic": tr_d["bytes_per_launch"] if tr_d else None, "traffic_unit": "bytes/launch",
