@@ -36,6 +36,10 @@ namespace {
 
 constexpr int kHeadsPerPass = 4;
 constexpr int kKeysPerStep = 32;
+constexpr int kDecodeChunkShift = 11;        // kDecodeChunk keys: the workspace's slot unit
+constexpr int kDecodeMinChunkShift = 9;      // shortest chunk a sliding window may use
+constexpr long long kDecodeTargetWG = 4096;  // split workgroups that fill the GPU
+static_assert((1 << kDecodeChunkShift) == kDecodeChunk, "workspace slots are kDecodeChunk keys");
 
 struct DecArgs {
   const __bf16* q;
@@ -46,7 +50,8 @@ struct DecArgs {
   int B, H, Hkv, Lmax;
   int group;   // H / Hkv
   int nsg;     // head slots of 4 per KV head
-  int nchunk;  // chunks per request at capacity
+  int nchunk;  // workspace slots per (request, head): chunks of kDecodeChunk keys at capacity
+  int cshift;  // log2 of the keys per chunk of this launch (kDecodeChunk, or less for short windows)
   float scale_log2;
   int window;  // sliding window W (0: none): the last W keys of the context
   const int32_t* ctx;
@@ -76,8 +81,10 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecArgs a) {
 
   const int n = min(max(a.ctx[b], 0), a.Lmax);
   const int w0 = a.window > 0 ? max(n - a.window, 0) : 0;  // first visible key
-  const int c0 = chunk * kDecodeChunk;
-  const int c1 = min(n, c0 + kDecodeChunk);
+  // Chunks of 2^cshift keys, counted from the one holding the first visible key (chunk 0
+  // of the cache without a window); `chunk` is also the workspace slot.
+  const int c0 = ((w0 >> a.cshift) + chunk) << a.cshift;
+  const int c1 = min(n, c0 + (1 << a.cshift));
   if (c0 >= n || c1 <= w0) return;  // chunk outside the visible keys: nothing to write
   // First step: the 32-key step that holds the first visible key of the chunk, so every
   // step holds at least one visible key; keys of that step before the window are neither
@@ -92,7 +99,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecArgs a) {
   int pg_lo = 0, pg_hi = 0, first = 0;
   if constexpr (PAGED) {
     first = c0 >> a.page_shift;
-    const int npc = max(kDecodeChunk >> a.page_shift, 1);  // pages per chunk, <= 128
+    const int npc = max((1 << a.cshift) >> a.page_shift, 1);  // pages per chunk, <= 128
     const int32_t* row = a.table + (size_t)b * a.max_pages;
     if (lane < npc && first + lane < a.max_pages) pg_lo = min(max(row[first + lane], 0), a.num_pages - 1);
     if (64 + lane < npc && first + 64 + lane < a.max_pages) pg_hi = min(max(row[first + 64 + lane], 0), a.num_pages - 1);
@@ -255,21 +262,21 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const DecArgs a) {
   const int bh = blockIdx.x;
   const int b = bh / a.H;
   const int n = min(max(a.ctx[b], 0), a.Lmax);
-  const int nc = (n + kDecodeChunk - 1) / kDecodeChunk;
-  // Chunks before the window's first key were not written.
-  const int cf = a.window > 0 ? max(n - a.window, 0) / kDecodeChunk : 0;
+  // Slots 0 .. nc - 1 hold the chunks from the one with the first visible key to the last.
+  const int w0 = a.window > 0 ? max(n - a.window, 0) : 0;
+  const int nc = ((n + (1 << a.cshift) - 1) >> a.cshift) - (w0 >> a.cshift);
   const float* ml = a.ws_ml + (size_t)bh * a.nchunk * 2;
   const float* wo = a.ws_o + (size_t)bh * a.nchunk * D;
 
   float M = kNegInf;
-  for (int c = cf + lane; c < nc; c += 64) M = fmaxf(M, ml[2 * c]);
+  for (int c = lane; c < nc; c += 64) M = fmaxf(M, ml[2 * c]);
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
 
   float L = 0.f, acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-  for (int c = cf; c < nc; ++c) {
+  for (int c = 0; c < nc; ++c) {
     const float wgt = exp2_hw(ml[2 * c] - M);
     L += wgt * ml[2 * c + 1];
 #pragma unroll
@@ -295,6 +302,23 @@ hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
   a.group = p.H / p.Hkv;
   a.nsg = (a.group + kHeadsPerPass - 1) / kHeadsPerPass;
   a.nchunk = decode_num_chunks(p.Lmax);
+  // Chunk size: kDecodeChunk keys, or less when a sliding window leaves so few chunks per
+  // request that the grid would not fill the GPU (at least kDecodeTargetWG workgroups, as long
+  // as the window's chunks still fit the workspace's slots).
+  const long long nx = (long long)p.B * p.Hkv * a.nsg;
+  int ny = a.nchunk;
+  a.cshift = kDecodeChunkShift;
+  if (p.window > 0) {
+    for (int s = kDecodeChunkShift; s >= kDecodeMinChunkShift; --s) {
+      const long long cs = 1LL << s;
+      const long long span = (p.window + cs - 1) / cs + 1, cap = (p.Lmax + cs - 1) / cs;
+      const long long nys = span < cap ? span : cap;
+      if (nys > a.nchunk) break;
+      a.cshift = s;
+      ny = (int)nys;
+      if (nx * nys >= kDecodeTargetWG) break;
+    }
+  }
   a.scale_log2 = p.scale * kLog2e;
   a.ctx = p.ctx_lens;
   a.window = p.window;
@@ -307,10 +331,9 @@ hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
   a.ws_ml = p.ws_ml;
   void* args[] = {&a};
   hipError_t e = hipSuccess;
-  if (a.nchunk > 0) {
-    const long long nx = (long long)p.B * p.Hkv * a.nsg;
-    if (nx > 0x7fffffffLL || a.nchunk > 65535) return hipErrorInvalidConfiguration;
-    e = hipLaunchKernel(reinterpret_cast<const void*>(&decode_split_kernel<D, PAGED>), dim3((unsigned)nx, a.nchunk),
+  if (ny > 0) {
+    if (nx > 0x7fffffffLL || ny > 65535) return hipErrorInvalidConfiguration;
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&decode_split_kernel<D, PAGED>), dim3((unsigned)nx, ny),
                         dim3(64), args, 0, stream);
     if (e != hipSuccess) return e;
   }
