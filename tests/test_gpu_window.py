@@ -93,7 +93,9 @@ def test_window_full_size_16k_sampled():
 @pytest.mark.parametrize("W", [1, 100, 2048, 3000, 10000])
 def test_window_decode_chunks(W):
     """Contexts across the 2048-key chunk boundaries, windows inside one chunk, exactly one
-    chunk, across two chunks, and wider than every context."""
+    chunk, across two chunks, and wider than every context. At this shape (10 split
+    workgroups per chunk, 3 workspace slots per head) the launch picks 512-key chunks for
+    W = 1 and 100, 1024-key chunks for W = 2048 and 2048-key chunks for W = 3000 and 10000."""
     B, H, Hkv, Lmax, d = 5, 8, 2, 5000, 128
     announce(entry="fa_decode_sliding_window", B=B, H=H, Hkv=Hkv, Lmax=Lmax, W=W)
     x = fa_inputs.decode_inputs(B, H, Hkv, Lmax, d, seed=440 + W, device=DEV)
