@@ -171,3 +171,36 @@ def test_bwd_full_size_causal_L16384_d128_sampled():
             dK, dV = _keys_oracle(q64, k64, v64, do64, keys, scale=w.scale, causal=True)
             _close(dk[0, h, keys], dK, "dK keys head 0")
             _close(dv[0, h, keys], dV, "dV keys head 0")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_empty_and_single_token_sequences(d):
+    """Per-sequence lengths 0, 300 and 1 in one call. The empty sequence has no visible key:
+    O = 0, LSE = -inf and zero gradients, with no NaN anywhere; the others match the oracle."""
+    fa = _fa()
+    B, H, Hkv, L = 3, 4, 2, 300
+    announce(entry="fa_fwd + fa_bwd", case="lengths 0, 300, 1", B=B, H=H, Hkv=Hkv, L=L, d=d)
+    x = fa_inputs.prefill_inputs(B, H, Hkv, L, L, d, seed=240 + d, device=DEV)
+    sl_cpu = torch.tensor([0, 300, 1], dtype=torch.int32)
+    sl = sl_cpu.to(DEV)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = fa.fwd(x["q"], x["k"], x["v"], causal=True, scale=scale, seqlens=sl)
+    do = _dout(o.shape, 241 + d)
+    dq, dk, dv = fa.bwd(x["q"], x["k"], x["v"], o, do, lse, causal=True, scale=scale, seqlens=sl)
+    ow, lsew = fa.fwd(x["q"], x["k"], x["v"], causal=True, scale=scale, seqlens=sl, window=37)
+    torch.cuda.synchronize()
+    for t in (o, dq, dk, dv, ow):
+        assert torch.isfinite(t.float()).all()
+    assert torch.all(o[0] == 0) and torch.all(torch.isneginf(lse[0]))
+    assert torch.all(ow[0] == 0) and torch.all(torch.isneginf(lsew[0]))
+    assert torch.all(dq[0] == 0) and torch.all(dk[0] == 0) and torch.all(dv[0] == 0)
+    q64, k64, v64, do64 = (fa_inputs.as_oracle_f64(t) for t in (x["q"], x["k"], x["v"], do))
+    O, LSE = oracle.attention(q64, k64, v64, scale=scale, causal=True, seqlens=sl_cpu.numpy())
+    from parity import compare
+    compare(o[1:], lse[1:], O[1:], LSE[1:], bf16_out=True, what=f"lengths 0/300/1 d{d}")
+    OW, LSEW = oracle.attention(q64, k64, v64, scale=scale, causal=True, seqlens=sl_cpu.numpy(), window=37)
+    compare(ow[1:], lsew[1:], OW[1:], LSEW[1:], bf16_out=True, what=f"lengths 0/300/1 window 37 d{d}")
+    dQ, dK, dV = oracle.attention_backward(q64, k64, v64, do64, scale=scale, causal=True, seqlens=sl_cpu.numpy())
+    _close(dq, dQ, f"dQ lengths 0/300/1 d{d}")
+    _close(dk, dK, f"dK lengths 0/300/1 d{d}")
+    _close(dv, dV, f"dV lengths 0/300/1 d{d}")
