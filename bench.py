@@ -135,6 +135,14 @@ def cpu_baseline(w, x, seconds):
             "seconds": round(dt, 2)}
 
 
+def spread(ms):
+    """Median and 10th / 90th percentiles of per-launch times (ms)."""
+    import statistics
+    t = sorted(ms)
+    pick = lambda f: t[min(len(t) - 1, int(f * (len(t) - 1) + 0.5))]  # noqa: E731  (nearest rank)
+    return {"ms_median": round(statistics.median(t), 4), "ms_p10": round(pick(0.1), 4), "ms_p90": round(pick(0.9), 4)}
+
+
 def library_gemm_tflops(dev, n=16384, reps=10):
     """Context for the matrix-core roofline: a plain bf16 GEMM (n x n x n) through the vendor
     BLAS behind torch.matmul, on the same GPU in the same run; median of `reps` launches.
@@ -382,11 +390,13 @@ def main():
                    "decode": {"B": wd.B, "H": wd.H, "Hkv": wd.Hkv, "Lmax": wd.L, "d": wd.d,
                               "ctx_range": list(wd.len_range), "seed": wd.seed,
                               "ctx_sum": int(ctx.sum())}},
-        "prefill": {"ms": round(fwd_avg, 4), "ms_min": round(min(fwd_ms), 4), "tflops": round(tflops, 2),
+        "prefill": {"ms": round(fwd_avg, 4), "ms_min": round(min(fwd_ms), 4), **spread(fwd_ms), "tflops": round(tflops, 2),
                     "pct_mfma_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2), "flop_per_launch": flop},
         "decode": {"value": round(gbps, 1), "unit": "GB/s", "ms": round(dec_avg, 4), "ms_min": round(min(dec_ms), 4),
+                   **spread(dec_ms),
                    "pct_hbm_peak": round(100 * gbps / PEAK_HBM_GBPS, 2), "kv_bytes_per_launch": kv_bytes},
-        "backward": {"ms": round(bwd_avg, 4), "ms_min": round(min(bwd_ms), 4), "tflops": round(bwd_tflops, 2),
+        "backward": {"ms": round(bwd_avg, 4), "ms_min": round(min(bwd_ms), 4), **spread(bwd_ms),
+                     "tflops": round(bwd_tflops, 2),
                      "pct_mfma_peak": round(100 * bwd_tflops / PEAK_BF16_TFLOPS, 2), "flop_per_launch": bwd_flop,
                      "flop_counting": "5 products of the forward's size (2.5x forward FLOP)",
                      "kernels": "bwd_dot_kernel<128> + bwd_dkdv_kernel<128> + bwd_dq_kernel<128>",
