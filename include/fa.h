@@ -141,9 +141,11 @@ fa_status fa_decode(const void* q, const void* k_cache, const void* v_cache, voi
 /*
  * fa_decode_sliding_window — fa_decode with a sliding window (reading as for
  * fa_fwd_sliding_window): request b attends to cache positions
- * max(0, ctx_lens[b] - window) .. ctx_lens[b] - 1 only. Chunks wholly before that range
- * are neither read nor merged. window >= 1, else FA_ERR_INVALID; the workspace is the
- * same as fa_decode's.
+ * max(0, ctx_lens[b] - window) .. ctx_lens[b] - 1 only. Keys before that range are
+ * neither read nor merged. Chunks are counted from the one holding the window's first key,
+ * and are shortened (down to 512 keys) when a short window would leave too few of them to
+ * fill the GPU; the result changes only by the rounding of the merge. window >= 1, else
+ * FA_ERR_INVALID; the workspace is the same as fa_decode's.
  */
 fa_status fa_decode_sliding_window(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
                                    int B, int H, int Hkv, int Lmax, int d, float scale, const int32_t* ctx_lens,
