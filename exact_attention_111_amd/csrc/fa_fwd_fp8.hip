@@ -232,8 +232,9 @@ __global__ __launch_bounds__(kF8NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     scores(0, sc);
     mask(0, sc);
   }
-  int t = 0;
-  for (; t < ntw; ++t) {
+  // One tile: its softmax and P V from `cur`, the next tile's scores into `nxt`. The loop
+  // runs two tiles per trip with the buffers swapped, so no scores are copied.
+  auto tile = [&](int t, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
     const bool more = t + 1 < ntk;   // another tile for the workgroup
     const bool mine = t + 1 < ntw;   // and this wave has keys in it
     if (more) {
@@ -241,7 +242,7 @@ __global__ __launch_bounds__(kF8NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
       else wait_vmcnt<0>();
       lds_barrier();
       if (t + kF8NS - 1 < ntk) issue(t + kF8NS - 1);
-      if (mine) scores(t + 1, sn);
+      if (mine) scores(t + 1, nxt);
     }
     const char* vt = smem + (t % kF8NS) * kF8Stage + kF8Tile;
 
@@ -250,7 +251,7 @@ __global__ __launch_bounds__(kF8NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, cur[kb][r]);
     mx = max_of_halves(mx) * c;
     const float m_new = mx > m ? ceilf(mx) : m;
     // 0 when there was no reference, 1 when unchanged, else an exact power of two
@@ -273,7 +274,7 @@ __global__ __launch_bounds__(kF8NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int T = 4 * i + e;
-        x[e] = exp2_hw(fmaf(sc[T >> 4][T & 15], c, off));
+        x[e] = exp2_hw(fmaf(cur[T >> 4][T & 15], c, off));
         l += x[e];
       }
       int word = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
@@ -291,11 +292,14 @@ __global__ __launch_bounds__(kF8NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
       const i32x8 va = {r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
       oacc[nb] = mfma_f8(va, pb, oacc[nb]);
     }
-    if (mine) {
-      mask(t + 1, sn);
-      sc[0] = sn[0];
-      sc[1] = sn[1];
-    }
+    if (mine) mask(t + 1, nxt);
+  };
+  int t = 0;
+  while (t < ntw) {
+    tile(t, sc, sn);
+    if (++t >= ntw) break;
+    tile(t, sn, sc);
+    ++t;
   }
   for (; t < ntk; ++t) {  // tiles past this wave's rows: loads and barriers only
     if (t + 1 < ntk) {
