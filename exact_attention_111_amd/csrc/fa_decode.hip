@@ -23,6 +23,8 @@
 //     keeping it in the caches only evicts lines that are still wanted (measured: +4-7%).
 //   * Chunks are 2048 keys: long enough that the exposed latency of a workgroup's first
 //     load is amortised, short enough that a 32k context still spreads over 16 workgroups.
+//     With a sliding window, chunks are counted from the one holding the window's first key
+//     and shortened (down to 512 keys) when the window leaves too few to fill the GPU.
 //   * Paged cache (PagedAttention's layout, which the same page names): position j of a
 //     request is row j % P of page table[j / P] of a pool [pages, Hkv, P, d]. With P a power
 //     of two >= 16, each 16-key half of a step lies in one page. A workgroup loads its

@@ -8,9 +8,8 @@
 // o are multiplied by exp(m_old - m_new). At the end O = o / l and the row's log-sum-exp
 // is written. Score and probability tiles never leave the compute unit.
 //
-// gfx950 mapping. One workgroup = one 256-row query tile of one head. At d = 128 it is 8
-// wave64s of 32 query rows (two waves per SIMD, so a wave fits in 256 VGPRs); at d = 64 it
-// is 4 wave64s of 64 rows (two 32-row blocks each, one wave per SIMD).
+// gfx950 mapping. One workgroup = one 256-row query tile of one head: 8 wave64s of 32 query
+// rows, two waves per SIMD, so a wave fits in 256 VGPRs (d = 64 and 128).
 //   * One body per 64-key tile j, one workgroup barrier each, in two regions: (X) the MFMAs
 //     of S for tile j + 1 beside exp / row sum / bf16 conversion of most of tile j, then
 //     (Y) the MFMAs of P V for tile j beside the rest of tile j's exps and the scale-and-
@@ -34,12 +33,15 @@
 //     bank conflicts on gfx950's LDS (128-bit reads are served 16 lanes at a time); every
 //     operand address is computed once per lane and reused with immediate offsets.
 //   * exp is 2^x on v_exp_f32 with scale*log2(e) folded into one FMA. Tiles are shifted by
-//     the row's current reference m without computing their maximum; only a part whose p
-//     went past 2^32 (or a row's first visible keys) raises m and rescales l and o. o / l
-//     does not depend on the reference, so this only skips work.
+//     the row's current reference m without computing their maximum; only a part after
+//     which a row-sum chain passes 2^40 (or, with a window, a row's first visible keys)
+//     raises m and rescales l and o. o / l does not depend on the reference, so this only
+//     skips work.
 //   * Causal and padding masks are applied element-wise only on tiles that straddle the
 //     diagonal or the sequence end, and key tiles past the query tile's last visible key are
-//     never loaded.
+//     never loaded. On the causal diagonal a wave stops computing after the last tile its
+//     own rows can see; the two waves of a SIMD hold a top and a bottom row block, so every
+//     SIMD is left the same work there.
 //   * Heads are dealt round-robin to the 8 XCDs (dispatch is round-robin over them), and
 //     each XCD works through its heads one at a time, heaviest query tile first, so that its
 //     CUs share that head's K/V in the XCD's L2.

@@ -16,7 +16,9 @@
 // gfx950 mapping (v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales for both products):
 //   * Workgroup: 256 query rows of one (batch, head), 8 waves of 32 rows, two per SIMD. Each
 //     wave keeps its Q rows as B operands: lane (half, col) holds dims 64 ks + 32 half ..
-//     + 31 of query row col (the operands' byte t of half h pair up in the product).
+//     + 31 of query row col (the operands' byte t of half h pair up in the product). On the
+//     causal diagonal a wave stops computing after the last tile its rows can see; the two
+//     waves of a SIMD hold a top and a bottom row block.
 //   * 64-key K and V tiles (8 KB each) stream through a 4-stage LDS ring filled by direct
 //     buffer-to-LDS loads three tiles ahead, one barrier per tile. The S products of the next
 //     tile are issued before the softmax of the current one (software pipeline).
