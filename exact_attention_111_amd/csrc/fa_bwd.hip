@@ -410,7 +410,8 @@ void bwd_dkdv_kernel(const BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------
-template <int D>
+// XCD_ORDER: workgroups grouped by KV head on the XCDs (used with GQA, see below).
+template <int D, bool XCD_ORDER>
 __global__ __launch_bounds__(BwdCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(FA_BWD_WPE, FA_BWD_WPE)))
 void bwd_dq_kernel(const BwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -421,12 +422,26 @@ void bwd_dq_kernel(const BwdArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
   // Query blocks in order of decreasing work under a causal mask (the last rows see the
-  // most keys), all (batch, head) pairs of one block together.
-  const int nbh = a.B * a.H;
+  // most keys). Without GQA: all (batch, head) pairs of one block together. With GQA
+  // (XCD_ORDER) the query heads of a group read the same K and V rows, so the order of the
+  // prefill (xcd_tile_order) is applied to (batch, KV head) pairs, each with `group` x ntq
+  // blocks: a pair's blocks run on one XCD, and the group's heads take the same query block
+  // next to each other, so their K/V tiles are shared in that XCD's L2.
   const int ntq = (a.Lq + C::QROWS - 1) / C::QROWS;
-  const int qt = ntq - 1 - (int)(blockIdx.x / nbh);
-  const int bh = blockIdx.x % nbh;
-  const int b = bh / a.H, h = bh - b * a.H;
+  int qt, b, h;
+  if constexpr (XCD_ORDER) {
+    int pair, u;
+    xcd_tile_order(blockIdx.x, gridDim.x, a.group * ntq, pair, u);
+    qt = u / a.group;
+    b = pair / a.Hkv;
+    h = (pair - b * a.Hkv) * a.group + (u - qt * a.group);
+  } else {
+    const int nbh = a.B * a.H;
+    qt = ntq - 1 - (int)(blockIdx.x / nbh);
+    const int bh = blockIdx.x % nbh;
+    b = bh / a.H;
+    h = bh - b * a.H;
+  }
   const int kvh = h / a.group;
   int n_q, n_kv;
   seq_extent(a, b, n_q, n_kv);
@@ -634,8 +649,9 @@ hipError_t launch_b(const BwdParams& p, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   if (nq > 0)
-    e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dq_kernel<D>), dim3((unsigned)nq), dim3(C::NT), args, 0,
-                        stream);
+    e = hipLaunchKernel(p.H > p.Hkv ? reinterpret_cast<const void*>(&bwd_dq_kernel<D, true>)
+                                    : reinterpret_cast<const void*>(&bwd_dq_kernel<D, false>),
+                        dim3((unsigned)nq), dim3(C::NT), args, 0, stream);
   return e;
 }
 
