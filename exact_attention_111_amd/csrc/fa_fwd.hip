@@ -118,11 +118,16 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
   const int col = lane & 31;   // this lane's query row within a 32-row block
   const int half = lane >> 5;  // which 8-element half of a 16-wide k-step
 
-  int bh, qt;
-  xcd_tile_order(blockIdx.x, a.nwg, a.ntq, bh, qt);
-  const int b = bh / a.H;
-  const int h = bh - b * a.H;
-  const int kvh = h / a.group;
+  // Workgroup order: xcd_tile_order over (batch, KV head) pairs with group x ntq tiles
+  // each, so the query heads that share a KV head run on one XCD and take the same query
+  // tile side by side (their K/V tiles are then shared in that XCD's L2). Without GQA the
+  // pairs are the heads themselves.
+  int pair, u;
+  xcd_tile_order(blockIdx.x, a.nwg, a.group * a.ntq, pair, u);
+  const int qt = u / a.group;
+  const int b = pair / a.Hkv;
+  const int kvh = pair - b * a.Hkv;
+  const int h = kvh * a.group + (u - qt * a.group);
 
   int n_kv = a.Lk, n_q = a.Lq;
   if (a.seqlens != nullptr) {
