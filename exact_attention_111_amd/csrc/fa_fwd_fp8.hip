@@ -90,9 +90,13 @@ __global__ __launch_bounds__(kF8NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
 
-  int bh, qt;
-  xcd_tile_order(blockIdx.x, a.nwg, a.ntq, bh, qt);
-  const int b = bh / a.H, h = bh - b * a.H, kvh = h / a.group;
+  // Workgroup order as in the bf16 prefill: (batch, KV head) pairs with group x ntq tiles
+  // each, so the query heads that share a KV head run side by side on one XCD.
+  int pair, u;
+  xcd_tile_order(blockIdx.x, a.nwg, a.group * a.ntq, pair, u);
+  const int qt = u / a.group;
+  const int b = pair / a.Hkv, kvh = pair - b * a.Hkv;
+  const int h = kvh * a.group + (u - qt * a.group);
   int n_kv = a.Lk, n_q = a.Lq;
   if (a.seqlens != nullptr) {
     const int n = min(max(a.seqlens[b], 0), a.Lk);
