@@ -204,3 +204,19 @@ def test_empty_and_single_token_sequences(d):
     _close(dq, dQ, f"dQ lengths 0/300/1 d{d}")
     _close(dk, dK, f"dK lengths 0/300/1 d{d}")
     _close(dv, dV, f"dV lengths 0/300/1 d{d}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_gqa_grouped_order_varlen(d):
+    """8 (batch, KV head) pairs, so the GQA workgroup orders (prefill, dQ and dK/dV) deal whole
+    pairs to the XCDs; variable lengths, causal; forward and gradients against the oracle."""
+    from parity import compare
+    for causal, seed, lr in ((True, 250 + d, (1, 300)), (False, 260 + d, None)):
+        x, _, _, _ = run_bwd(2, 16, 4, 300, 300, d, causal=causal, seed=seed, len_range=lr)
+        scale = 1.0 / math.sqrt(d)
+        o, lse = _fa().fwd(x["q"], x["k"], x["v"], causal=causal, scale=scale, seqlens=x["seqlens"])
+        torch.cuda.synchronize()
+        sl = None if x["seqlens_cpu"] is None else x["seqlens_cpu"].numpy()
+        O, LSE = oracle.attention(*(fa_inputs.as_oracle_f64(x[n]) for n in ("q", "k", "v")), scale=scale,
+                                  causal=causal, seqlens=sl)
+        compare(o, lse, O, LSE, bf16_out=True, what=f"GQA 8 pairs fwd d{d} c{int(causal)}")
