@@ -1,0 +1,124 @@
+"""Every entry point recorded into a HIP graph and replayed.
+
+The library allocates nothing and never synchronises; each call only enqueues kernels on the
+caller's stream, so a serving loop can capture a step once and replay it. A replay reads the
+current contents of its input buffers (device-side lengths and block tables included). No
+kernel uses atomics, so each launch is deterministic: every replay must equal, bit for bit,
+the same calls made eagerly on the same inputs. Between replays the inputs are refilled and
+other eager work runs on the stream, and every replay is checked, not only the first.
+"""
+import math
+import sys
+
+import pytest
+import torch
+
+import fa_inputs
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _fa():
+    import exact_attention_111_amd as fa
+    return fa
+
+
+def announce(**case):
+    print("\n[case] " + " ".join(f"{k}={v}" for k, v in case.items()), flush=True)
+    sys.stdout.flush()
+
+
+def _inputs(seed):
+    """One set of inputs for all six calls (prefill, windowed prefill, FP8 prefill, decode,
+    paged decode, backward), seeded."""
+    x = fa_inputs.prefill_inputs(2, 4, 2, 640, 640, 128, seed=seed, device=DEV, len_range=(1, 640))
+    x8 = fa_inputs.fp8_prefill_inputs(2, 4, 2, 640, 640, 128, seed=seed + 1, device=DEV, len_range=(1, 640))
+    xd = fa_inputs.decode_inputs(3, 8, 2, 5000, 128, seed=seed + 2, device=DEV)
+    xp = fa_inputs.paged_decode_inputs(3, 8, 2, 3000, 128, 64, seed=seed + 3, device=DEV)
+    g = torch.Generator(device=DEV).manual_seed(seed + 4)
+    dout = torch.randn(x["q"].shape, generator=g, device=DEV).to(torch.bfloat16)
+    return {"pre": x, "fp8": x8, "dec": xd, "pag": xp, "dout": dout}
+
+
+def _buffers(inp):
+    """Output and workspace buffers for one set of calls, allocated up front."""
+    fa = _fa()
+    x, x8, xd, xp = inp["pre"], inp["fp8"], inp["dec"], inp["pag"]
+    B, H, L, d = x["q"].shape
+    f32 = dict(dtype=torch.float32, device=DEV)
+    Bd, Hd, dd = xd["q"].shape
+    Bp, Hp, dp = xp["q"].shape
+    return {
+        "o1": torch.empty_like(x["q"]), "l1": torch.empty((B, H, L), **f32),
+        "o2": torch.empty_like(x["q"]), "l2": torch.empty((B, H, L), **f32),
+        "o3": torch.empty((B, H, L, d), dtype=torch.bfloat16, device=DEV), "l3": torch.empty((B, H, L), **f32),
+        "o4": torch.empty_like(xd["q"]), "l4": torch.empty((Bd, Hd), **f32),
+        "o5": torch.empty_like(xp["q"]), "l5": torch.empty((Bp, Hp), **f32),
+        "ws4": torch.empty(fa.decode_workspace_bytes(Bd, Hd, xd["k_cache"].shape[2], dd), dtype=torch.uint8,
+                           device=DEV),
+        "ws5": torch.empty(fa.decode_workspace_bytes(Bp, Hp, xp["block_table"].shape[1] * xp["page_size"], dp),
+                           dtype=torch.uint8, device=DEV),
+        "wsb": torch.empty(max(fa.bwd_workspace_bytes(B, H, L), 16), dtype=torch.uint8, device=DEV),
+        "dq": torch.empty_like(x["q"]), "dk": torch.empty_like(x["k"]), "dv": torch.empty_like(x["v"]),
+    }
+
+
+OUTPUTS = ("o1", "l1", "o2", "l2", "o3", "l3", "o4", "l4", "o5", "l5", "dq", "dk", "dv")
+
+
+def _calls(inp, buf):
+    fa = _fa()
+    x, x8, xd, xp = inp["pre"], inp["fp8"], inp["dec"], inp["pag"]
+    sc = 1.0 / math.sqrt(128)
+    fa.fwd(x["q"], x["k"], x["v"], causal=True, scale=sc, seqlens=x["seqlens"], out=buf["o1"], lse=buf["l1"])
+    fa.fwd(x["q"], x["k"], x["v"], causal=True, scale=sc, window=100, out=buf["o2"], lse=buf["l2"])
+    fa.fwd_fp8(x8["q"], x8["k"], x8["v"], x8["q_descale"], x8["k_descale"], x8["v_descale"], causal=True,
+               scale=sc, seqlens=x8["seqlens"], out=buf["o3"], lse=buf["l3"])
+    fa.decode(xd["q"], xd["k_cache"], xd["v_cache"], xd["ctx_lens"], scale=sc, workspace=buf["ws4"],
+              out=buf["o4"], lse=buf["l4"])
+    fa.decode_paged(xp["q"], xp["k_pages"], xp["v_pages"], xp["block_table"], xp["ctx_lens"], scale=sc,
+                    workspace=buf["ws5"], out=buf["o5"], lse=buf["l5"])
+    fa.bwd(x["q"], x["k"], x["v"], buf["o1"], inp["dout"], buf["l1"], causal=True, scale=sc,
+           seqlens=x["seqlens"], workspace=buf["wsb"], dq=buf["dq"], dk=buf["dk"], dv=buf["dv"])
+
+
+def _refill(dst, src):
+    """Copy every tensor of input set `src` into the matching buffer of `dst` (same shapes)."""
+    for key, val in src.items():
+        if isinstance(val, dict):
+            _refill(dst[key], val)
+        elif isinstance(val, torch.Tensor) and val.is_cuda:
+            dst[key].copy_(val)
+
+
+def test_all_entry_points_replay_in_a_graph():
+    announce(entry="all (graph capture)", seed=900)
+    static = _inputs(900)
+    gbuf, ebuf = _buffers(static), _buffers(static)
+    # warm-up on a side stream, as capture expects
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        _calls(static, gbuf)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        _calls(static, gbuf)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        announce(replay=rep, seed=901 + rep)
+        _refill(static, _inputs(901 + rep))  # new values, lengths and block tables in the same buffers
+        for name in OUTPUTS:  # rows a call does not write then read the same in both sets
+            gbuf[name].zero_()
+            ebuf[name].zero_()
+        _calls(static, ebuf)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name in OUTPUTS:
+            assert torch.equal(gbuf[name], ebuf[name]), f"replay {rep}: {name} differs from the eager call"
+        assert torch.isfinite(gbuf["o1"].float()).all() and torch.isfinite(gbuf["dq"].float()).all()
+    graph.reset()
