@@ -412,7 +412,7 @@ def main():
                             "frac": round(gbps / PEAK_HBM_GBPS, 4),
                             "traffic": tr_d["bytes_per_launch"] if tr_d else None, "traffic_unit": "bytes/launch",
                             "traffic_algorithmic": kv_bytes, "traffic_source": src_d,
-                            "kernels": "decode_split_kernel<128> + decode_combine_kernel<128>"},
+                            "kernels": "decode_split_kernel<128, false, true> + decode_combine_kernel<128, true>"},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

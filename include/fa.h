@@ -129,9 +129,12 @@ size_t fa_decode_workspace_bytes(int B, int H, int Lmax, int d);
  *              (all of them: the new token is the newest position).
  *   workspace: device memory of at least fa_decode_workspace_bytes(B, H, Lmax, d) bytes,
  *              16-byte aligned, owned by the caller; its contents are scratch.
- * The keys are split into fixed-size chunks; one kernel computes each chunk's partial
- * (max, sum, unnormalised output) and a second merges the partials of a row with the
- * two-state merge rule of "2.1 FlashAttention-2 的核心思想" §2.1.3 into O and LSE.
+ * The keys are split into ranges; one kernel computes each range's partial (max, sum,
+ * unnormalised output) and a second merges the partials of a row with the two-state merge
+ * rule of "2.1 FlashAttention-2 的核心思想" §2.1.3 into O and LSE. With Lmax > 2048 the
+ * ranges balance the whole call's keys over the GPU (equal runs of 32-key steps per
+ * workgroup, from the device-side lengths), otherwise they are 2048-key chunks; the split
+ * changes the result only by the rounding of the merge.
  * Requirements: B, H >= 0 (0 = empty call), Hkv >= 1, H % Hkv == 0, Lmax >= 0.
  */
 fa_status fa_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,

@@ -61,6 +61,20 @@ def test_decode_group_sizes(H, Hkv):
     run_decode(2, H, Hkv, 700, 128, seed=110 + H, ctx=[700, 300])
 
 
+@pytest.mark.parametrize("H,Hkv,d", [(16, 2, 128), (12, 2, 64), (3, 1, 128)])
+def test_decode_balanced_partition(H, Hkv, d):
+    """A contiguous cache longer than one 2048-key chunk, without a window, is split into equal
+    step ranges per workgroup, cut where a (request, KV head, head slot) unit ends. Mixed
+    lengths (empty, 1, 31, 32, 33 keys, full) make workgroups span several units and requests;
+    group 8 takes two head passes, group 6 a partial one."""
+    ctx = [0, 1, 31, 32, 33, 5000, 2049, 0, 4096, 777, 5000, 2]
+    st, x, o, lse = run_decode(len(ctx), H, Hkv, 5000, d, seed=130 + H + d, ctx=ctx)
+    assert torch.all(o[0] == 0) and torch.all(torch.isneginf(lse[0]))
+    assert torch.all(o[7] == 0) and torch.all(torch.isneginf(lse[7]))
+    st, x, o, lse = run_decode(2, H, Hkv, 3000, d, seed=140 + H + d, ctx=[0, 0])  # no keys at all
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+
+
 def test_decode_empty_context_and_empty_call():
     fa = _fa()
     announce(entry="fa_decode", case="ctx = 0 and B = 0")
