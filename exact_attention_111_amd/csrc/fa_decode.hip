@@ -21,18 +21,21 @@
 //   * The chunk's K/V for the next 32 keys are loaded before the current 32 are used.
 //   * K/V are read with non-temporal loads: each byte is used by exactly one workgroup, so
 //     keeping it in the caches only evicts lines that are still wanted (measured: +4-7%).
-//   * Contiguous cache, no window: a balanced partition. The launch has one workgroup per
-//     split slot of the GPU (2048), and each takes an equal run of the 32-key steps of all
-//     (request, KV head) units, cut where a unit ends. With fixed-size chunks, 2.6 chunks
-//     per slot left some slots a whole chunk longer than others (measured: +11% K/V rate).
-//   * Sliding window or paged cache: chunks of 2048 keys, one workgroup each. With a window
-//     they are counted from the one holding the window's first key and shortened (down to
-//     512 keys) when the window leaves too few to fill the GPU.
+//   * Caches longer than 2048 keys, without a window or with one of 2048 keys or more: a
+//     balanced partition. The launch has one workgroup per split slot of the GPU (2048),
+//     and each takes an equal run of the 32-key steps with visible keys of all (request, KV
+//     head) units, cut where a unit ends. With fixed-size chunks, 2.6 chunks per slot left
+//     some slots a whole chunk longer than others (measured: +11% K/V rate, contiguous or
+//     paged, with or without a window).
+//   * Otherwise chunks of 2048 keys, one workgroup each. With a window they are counted
+//     from the one holding the window's first key and shortened (down to 512 keys) when
+//     the window leaves too few to fill the GPU.
 //   * Paged cache (PagedAttention's layout, which the same page names): position j of a
 //     request is row j % P of page table[j / P] of a pool [pages, Hkv, P, d]. With P a power
-//     of two >= 16, each 16-key half of a step lies in one page. A workgroup loads its
-//     chunk's page numbers once (two per lane, at most 128 pages) and takes each step's page
-//     with a uniform readlane, so the K/V loads stay 16-byte row loads.
+//     of two >= 16, each 16-key half of a step lies in one page. A workgroup holds the page
+//     numbers of up to 128 pages (two per lane; a balanced run reloads them when it moves
+//     past them) and takes each step's page with a uniform readlane, so the K/V loads stay
+//     16-byte row loads.
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -71,14 +74,23 @@ struct DecArgs {
   int qmin;  // balanced partition: fewest 32-key steps per workgroup (keeps slots < nchunk)
 };
 
+// Visible keys of request b: [first, n), first > 0 only with a sliding window.
+__device__ __forceinline__ int decode_ctx(const DecArgs& a, int b) { return min(max(a.ctx[b], 0), a.Lmax); }
+__device__ __forceinline__ int decode_first_key(const DecArgs& a, int n) {
+  return a.window > 0 ? max(n - a.window, 0) : 0;
+}
+// 32-key steps of request b that hold visible keys: from the one holding its first visible
+// key to the one holding its last (0 for an empty context or b >= B).
 __device__ __forceinline__ int decode_steps(const DecArgs& a, int b) {
-  return b < a.B ? (min(max(a.ctx[b], 0), a.Lmax) + kKeysPerStep - 1) / kKeysPerStep : 0;
+  if (b >= a.B) return 0;
+  const int n = decode_ctx(a, b);
+  return n > 0 ? (n + kKeysPerStep - 1) / kKeysPerStep - decode_first_key(a, n) / kKeysPerStep : 0;
 }
 
-// Balanced partition of a contiguous-cache decode without a window. The 32-key steps of
-// all (request, KV head, head slot) units, taken in that order, form one sequence of T
-// steps; workgroup w takes steps [w Qs, (w + 1) Qs), Qs = max(ceil(T / nwg), qmin), cut
-// at unit boundaries into segments. Every workgroup then reads the same number of K/V
+// Balanced partition of a decode. The 32-key steps with visible keys of all (request, KV
+// head, head slot) units, taken in that order, form one sequence of T steps; workgroup w
+// takes steps [w Qs, (w + 1) Qs), Qs = max(ceil(T / nwg), qmin), cut at unit boundaries
+// into segments. Every workgroup then reads the same number of K/V
 // bytes, where a grid of fixed-size chunks leaves some slots one whole chunk longer than
 // others. A segment of unit u is partial slot w - floor(S_u / Qs) of u, S_u being u's first
 // step; qmin bounds that slot below nchunk. Both kernels derive T and Qs from the same
@@ -174,11 +186,13 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecArgs a) {
       seg = (int)min((long long)(sb - st), end - pos);
       kvh = pr / a.nsg;
       sg = pr - kvh * a.nsg;
-      n = min(max(a.ctx[b], 0), a.Lmax);
-      w0 = 0;
-      c0 = st * kKeysPerStep;
+      n = decode_ctx(a, b);
+      w0 = decode_first_key(a, n);
+      // the unit's steps start at the one holding w0; keys of it before w0 are masked
+      const int s0 = w0 / kKeysPerStep;
+      c0 = (s0 + st) * kKeysPerStep;
       k_start = c0;
-      c1 = min(n, (st + seg) * kKeysPerStep);
+      c1 = min(n, (s0 + st + seg) * kKeysPerStep);
       slot = (int)((long long)blockIdx.x - (R + (long long)pr * sb) / Qs);
     }
     const int h0 = kvh * a.group + sg * kHeadsPerPass;
@@ -187,14 +201,18 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecArgs a) {
     // Rows of the 16 keys from kb0 (a multiple of 16): contiguous cache, or the page that
     // holds them. Paged: this lane holds page numbers first + lane and first + 64 + lane of the
     // chunk (clamped into the pool, so a bad table cannot address outside it).
+    // A balanced segment may span more than 128 pages: its page numbers are then reloaded,
+    // 128 at a time, before the step that first needs the next ones.
     int pg_lo = 0, pg_hi = 0, first = 0;
-    if constexpr (PAGED) {
-      first = c0 >> a.page_shift;
-      const int npc = max((1 << a.cshift) >> a.page_shift, 1);  // pages per chunk, <= 128
+    const int npc = BAL ? 128 : max((1 << a.cshift) >> a.page_shift, 1);  // pages held, <= 128
+    auto load_pages = [&](int f) {
+      first = f;
+      pg_lo = pg_hi = 0;
       const int32_t* row = a.table + (size_t)b * a.max_pages;
-      if (lane < npc && first + lane < a.max_pages) pg_lo = min(max(row[first + lane], 0), a.num_pages - 1);
-      if (64 + lane < npc && first + 64 + lane < a.max_pages) pg_hi = min(max(row[first + 64 + lane], 0), a.num_pages - 1);
-    }
+      if (lane < npc && f + lane < a.max_pages) pg_lo = min(max(row[f + lane], 0), a.num_pages - 1);
+      if (64 + lane < npc && f + 64 + lane < a.max_pages) pg_hi = min(max(row[f + 64 + lane], 0), a.num_pages - 1);
+    };
+    if constexpr (PAGED) load_pages(c0 >> a.page_shift);
     auto rows_at = [&](const __bf16* base, int kb0) -> const __bf16* {
       if constexpr (PAGED) {
         const int cp = (kb0 >> a.page_shift) - first;  // chunk-relative page, uniform
@@ -269,7 +287,14 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecArgs a) {
       u32x4 vcur[VLOADS];
 #pragma unroll
       for (int i = 0; i < VLOADS; ++i) vcur[i] = vr[i];
-      if (k0 + kKeysPerStep < c1) load_step(k0 + kKeysPerStep);  // prefetch the next 32 keys
+      if (k0 + kKeysPerStep < c1) {  // prefetch the next 32 keys
+        if constexpr (PAGED && BAL) {
+          // loads already issued do not depend on the page numbers any more
+          const int nk = k0 + kKeysPerStep;
+          if (((nk + kKeysPerStep - 1) >> a.page_shift) - first >= npc) load_pages(nk >> a.page_shift);
+        }
+        load_step(k0 + kKeysPerStep);
+      }
 
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
@@ -460,18 +485,24 @@ hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
   a.num_pages = p.num_pages;
   a.ws_o = p.ws_o;
   a.ws_ml = p.ws_ml;
-  // Balanced partition (contiguous cache, no window): qmin steps per workgroup keep a
-  // unit's segments, at most ceil((smax - 1) / Qs) + 1 of them, within its nchunk slots.
-  const long long smax = (p.Lmax + kKeysPerStep - 1) / kKeysPerStep;
-  const bool bal = !PAGED && p.window == 0 && a.nchunk >= 2 && nx * smax < 0x7fffffffLL;
+  // Balanced partition: qmin steps per workgroup keep a unit's segments, at most
+  // ceil((smax - 1) / Qs) + 1 of them, within its nchunk slots; smax bounds a unit's steps
+  // (a window of W keys meets at most ceil(W / 32) + 1 of them).
+  long long smax = (p.Lmax + kKeysPerStep - 1) / kKeysPerStep;
+  const long long wsteps = ((long long)p.window + kKeysPerStep - 1) / kKeysPerStep + 1;
+  if (p.window > 0 && wsteps < smax) smax = wsteps;
+  // Windows shorter than a chunk keep the chunk grid, whose chunks shorten to fill the GPU:
+  // at a 1024-key window the balanced runs (288 keys) were 6% slower; at 2048 and more
+  // keys they were 10-12% faster.
+  const bool bal = a.nchunk >= 2 && nx * smax < 0x7fffffffLL && (p.window == 0 || p.window >= kDecodeChunk);
   a.nwg = kBalancedWG;
-  a.qmin = bal ? (int)((smax - 1 + a.nchunk - 2) / (a.nchunk - 1)) : 1;
+  a.qmin = bal ? (int)((smax - 1 + a.nchunk - 2) / (a.nchunk - 1)) : 1;  // bal: nchunk >= 2
   void* args[] = {&a};
   hipError_t e = hipSuccess;
   const long long nbh = (long long)p.B * p.H;
   if (nbh > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (bal) {
-    e = hipLaunchKernel(reinterpret_cast<const void*>(&decode_split_kernel<D, false, true>), dim3(kBalancedWG),
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&decode_split_kernel<D, PAGED, true>), dim3(kBalancedWG),
                         dim3(64), args, 0, stream);
     if (e != hipSuccess) return e;
     return hipLaunchKernel(reinterpret_cast<const void*>(&decode_combine_kernel<D, true>), dim3((unsigned)nbh),

@@ -133,8 +133,9 @@ size_t fa_decode_workspace_bytes(int B, int H, int Lmax, int d);
  * unnormalised output) and a second merges the partials of a row with the two-state merge
  * rule of "2.1 FlashAttention-2 的核心思想" §2.1.3 into O and LSE. With Lmax > 2048 the
  * ranges balance the whole call's keys over the GPU (equal runs of 32-key steps per
- * workgroup, from the device-side lengths), otherwise they are 2048-key chunks; the split
- * changes the result only by the rounding of the merge.
+ * workgroup, from the device-side lengths; the split depends on Lmax as well as on the
+ * lengths), otherwise they are 2048-key chunks; the split changes the result only by the
+ * rounding of the merge.
  * Requirements: B, H >= 0 (0 = empty call), Hkv >= 1, H % Hkv == 0, Lmax >= 0.
  */
 fa_status fa_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
@@ -145,10 +146,12 @@ fa_status fa_decode(const void* q, const void* k_cache, const void* v_cache, voi
  * fa_decode_sliding_window — fa_decode with a sliding window (reading as for
  * fa_fwd_sliding_window): request b attends to cache positions
  * max(0, ctx_lens[b] - window) .. ctx_lens[b] - 1 only. Keys before that range are
- * neither read nor merged. Chunks are counted from the one holding the window's first key,
- * and are shortened (down to 512 keys) when a short window would leave too few of them to
- * fill the GPU; the result changes only by the rounding of the merge. window >= 1, else
- * FA_ERR_INVALID; the workspace is the same as fa_decode's.
+ * neither read nor merged. A window of 2048 keys or more (with Lmax > 2048) takes the
+ * balanced ranges of fa_decode, counted from each request's first visible key. A shorter
+ * window takes 2048-key chunks counted from the one holding the window's first key,
+ * shortened (down to 512 keys) when they would be too few to fill the GPU. The split
+ * changes the result only by the rounding of the merge. window >= 1, else FA_ERR_INVALID;
+ * the workspace is the same as fa_decode's.
  */
 fa_status fa_decode_sliding_window(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
                                    int B, int H, int Hkv, int Lmax, int d, float scale, const int32_t* ctx_lens,
@@ -169,7 +172,9 @@ fa_status fa_decode_sliding_window(const void* q, const void* k_cache, const voi
  * half step of the kernel must lie in one page). Table entries are device data and are not
  * checked on the host: the kernel clamps each to [0, num_pages - 1], so a bad table gives
  * wrong numbers but never an access outside the pools. Entries past a request's context are
- * not read. q, o, lse, scale and errors as for fa_decode.
+ * not read. The keys are split as for fa_decode (or fa_decode_sliding_window) on a cache of
+ * capacity max_pages * page_size, so paged and contiguous calls of equal capacity give
+ * identical results. q, o, lse, scale and errors as for fa_decode.
  */
 fa_status fa_decode_paged(const void* q, const void* k_pages, const void* v_pages, void* o, float* lse,
                           int B, int H, int Hkv, int d, float scale, int page_size, int num_pages,

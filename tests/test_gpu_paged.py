@@ -45,18 +45,22 @@ def _paginate(cache, P, seed):
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("P", [16, 64, 256, 2048, 4096])
 def test_paged_equals_contiguous_bitwise(d, P):
-    """Same arithmetic, rows from other addresses: the outputs are identical. Without a window a
-    contiguous cache takes the balanced partition (other split points, so other rounding); a
-    window as long as the cache reads every key through the same 2048-key chunks as the paged
-    kernel, so that is the contiguous call compared bit for bit with the paged one."""
+    """Same arithmetic and the same split of the keys (pages up to 4096 positions, so balanced
+    runs cross many 128-page windows at P = 16), rows from other addresses: the outputs are
+    identical."""
     B, H, Hkv, Lmax = 4, 8, 2, 5000
     announce(entry="fa_decode_paged vs fa_decode", d=d, P=P, B=B, H=H, Hkv=Hkv, Lmax=Lmax)
     x = fa_inputs.decode_inputs(B, H, Hkv, Lmax, d, seed=500 + P + d, device=DEV)
     ctx = torch.tensor([1, 2047, 2049, 5000], dtype=torch.int32, device=DEV)
     kp, table = _paginate(x["k_cache"], P, 501)
     vp, _ = _paginate(x["v_cache"], P, 501)
+    # the contiguous cache gets the paged one's capacity (max_pages * P), which sets the split
+    cap = table.shape[1] * P
+    kc = torch.zeros((B, Hkv, cap, d), device=DEV, dtype=torch.bfloat16)
+    vc = torch.zeros_like(kc)
+    kc[:, :, :Lmax], vc[:, :, :Lmax] = x["k_cache"], x["v_cache"]
     for W in (None, 700):
-        o1, l1 = _fa().decode(x["q"], x["k_cache"], x["v_cache"], ctx, window=Lmax if W is None else W)
+        o1, l1 = _fa().decode(x["q"], kc, vc, ctx, window=W)
         o2, l2 = _fa().decode_paged(x["q"], kp, vp, table, ctx, window=W)
         torch.cuda.synchronize()
         assert torch.equal(o1, o2) and torch.equal(l1, l2), (P, W)

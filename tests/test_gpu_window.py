@@ -92,10 +92,11 @@ def test_window_full_size_16k_sampled():
 
 @pytest.mark.parametrize("W", [1, 100, 2048, 3000, 10000])
 def test_window_decode_chunks(W):
-    """Contexts across the 2048-key chunk boundaries, windows inside one chunk, exactly one
-    chunk, across two chunks, and wider than every context. At this shape (10 split
-    workgroups per chunk, 3 workspace slots per head) the launch picks 512-key chunks for
-    W = 1 and 100, 1024-key chunks for W = 2048 and 2048-key chunks for W = 3000 and 10000."""
+    """Contexts across 2048-key boundaries; windows of one key, inside 2048 keys, exactly 2048,
+    across two 2048-key spans, and wider than every context. Windows of 1 and 100 keys take
+    the chunk grid with shortened chunks (512 keys at this shape); windows of 2048 keys and
+    more take the balanced partition, each unit's steps running from the one holding its
+    window's first key and workgroups spanning several units."""
     B, H, Hkv, Lmax, d = 5, 8, 2, 5000, 128
     announce(entry="fa_decode_sliding_window", B=B, H=H, Hkv=Hkv, Lmax=Lmax, W=W)
     x = fa_inputs.decode_inputs(B, H, Hkv, Lmax, d, seed=440 + W, device=DEV)
@@ -106,6 +107,22 @@ def test_window_decode_chunks(W):
     O, LSE = oracle.decode(*(fa_inputs.as_oracle_f64(x[n]) for n in ("q", "k_cache", "v_cache")), ctx.numpy(),
                            scale=scale, window=W)
     compare(o, lse, O, LSE, bf16_out=True, what=f"decode W{W}")
+
+
+@pytest.mark.parametrize("W", [1, 700])
+def test_window_decode_single_chunk(W):
+    """A cache of at most 2048 keys takes the grid of 2048-key chunks (one per request and KV
+    head), with the window's first key inside the chunk."""
+    B, H, Hkv, Lmax, d = 3, 8, 2, 2000, 128
+    announce(entry="fa_decode_sliding_window", B=B, H=H, Hkv=Hkv, Lmax=Lmax, W=W, case="chunk grid")
+    x = fa_inputs.decode_inputs(B, H, Hkv, Lmax, d, seed=460 + W, device=DEV)
+    ctx = torch.tensor([1, 1999, 2000], dtype=torch.int32)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = _fa().decode(x["q"], x["k_cache"], x["v_cache"], ctx.to(DEV), scale=scale, window=W)
+    torch.cuda.synchronize()
+    O, LSE = oracle.decode(*(fa_inputs.as_oracle_f64(x[n]) for n in ("q", "k_cache", "v_cache")), ctx.numpy(),
+                           scale=scale, window=W)
+    compare(o, lse, O, LSE, bf16_out=True, what=f"decode chunk grid W{W}")
 
 
 def test_window_decode_ignores_nan_before_window():
