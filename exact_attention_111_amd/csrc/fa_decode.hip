@@ -87,20 +87,21 @@ __device__ __forceinline__ int decode_steps(const DecArgs& a, int b) {
   return n > 0 ? (n + kKeysPerStep - 1) / kKeysPerStep - decode_first_key(a, n) / kKeysPerStep : 0;
 }
 
-// Balanced partition of a decode. The 32-key steps with visible keys of all (request, KV
-// head, head slot) units, taken in that order, form one sequence of T steps; workgroup w
-// takes steps [w Qs, (w + 1) Qs), Qs = max(ceil(T / nwg), qmin), cut at unit boundaries
-// into segments. Every workgroup then reads the same number of K/V
-// bytes, where a grid of fixed-size chunks leaves some slots one whole chunk longer than
-// others. A segment of unit u is partial slot w - floor(S_u / Qs) of u, S_u being u's first
-// step; qmin bounds that slot below nchunk. Both kernels derive T and Qs from the same
-// context lengths, so they agree on the slots.
 // A value every lane holds alike, moved to scalar registers.
 __device__ __forceinline__ long long wave_uniform(long long v) {
   const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v);
   const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)((unsigned long long)v >> 32));
   return (long long)(((unsigned long long)hi << 32) | lo);
 }
+
+// Balanced partition of a decode. The 32-key steps with visible keys of all (request, KV
+// head, head slot) units, taken in that order, form one sequence of T steps; workgroup w
+// takes steps [w Qs, (w + 1) Qs), Qs = max(ceil(T / nwg), qmin), cut at unit boundaries
+// into segments. Every workgroup then reads the same number of K/V bytes, where a grid of
+// fixed-size chunks leaves some slots one whole chunk longer than others. A segment of
+// unit u is partial slot w - floor(S_u / Qs) of u, S_u being u's first step; qmin bounds
+// that slot below nchunk. Both kernels derive T and Qs from the same context lengths, so
+// they agree on the slots. (T < 2^31: the launch checks units x steps per unit.)
 __device__ __forceinline__ long long decode_total_steps(const DecArgs& a, int lane) {
   long long tot = 0;
   for (int c = 0; c < a.B; c += 64) {
