@@ -90,6 +90,37 @@ def _check(status: int, what: str):
         raise FaError(status, what)
 
 
+def _need(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _shape(t, shape, name: str):
+    _need(tuple(t.shape) == tuple(shape), f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _contiguous(named):
+    for name, t in named:
+        if t is not None:
+            _need(t.is_contiguous(), f"libfa needs contiguous tensors ({name} is not)")
+
+
+def _on_device(dev, named):
+    """Every tensor on q's device, and that device a GPU: the library only sees raw
+    pointers, so a host or foreign-device tensor would be read by the kernels as device
+    memory of this GPU."""
+    _need(dev.type == "cuda", f"libfa runs on a GPU: q is on {dev}")
+    for name, t in named:
+        if t is not None:
+            _need(t.device == dev, f"{name} is on {t.device}, not on q's device {dev}")
+
+
+def _lengths(t, B: int, name: str):
+    if t is not None:
+        _need(t.dtype == torch.int32, f"{name} must be int32")
+        _shape(t, (B,), name)
+
+
 def fwd(q, k, v, *, causal: bool = False, scale: float | None = None, seqlens=None, out=None, lse=None,
         window: int | None = None):
     """Attention forward through ``fa_fwd`` (bf16), ``fa_fwd_f32`` (fp32 I/O) or, with
@@ -99,21 +130,26 @@ def fwd(q, k, v, *, causal: bool = False, scale: float | None = None, seqlens=No
     fp32. seqlens: optional int32 [B] on the same device (requires Lq == Lk).
     Returns (o [B, H, Lq, d] in the input dtype, lse [B, H, Lq] fp32).
     """
+    _need(q.dim() == 4 and k.dim() == 4 and v.dim() == 4, "q, k, v must be 4-D [B, heads, L, d]")
     B, H, Lq, d = q.shape
     Hkv, Lk = k.shape[1], k.shape[2]
+    _shape(k, (B, Hkv, Lk, d), "k")
+    _shape(v, (B, Hkv, Lk, d), "v")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device)
-    for t in (q, k, v, out, lse):
-        if not t.is_contiguous():
-            raise ValueError("libfa needs contiguous tensors")
+    _shape(out, q.shape, "out")
+    _shape(lse, (B, H, Lq), "lse")
     if not (q.dtype == k.dtype == v.dtype == out.dtype) or q.dtype not in (torch.bfloat16, torch.float32):
         raise ValueError("q, k, v, out must all be bfloat16 or all float32")
-    if seqlens is not None and seqlens.dtype != torch.int32:
-        raise ValueError("seqlens must be int32")
+    _need(lse.dtype == torch.float32, "lse must be float32")
+    _lengths(seqlens, B, "seqlens")
+    named = (("q", q), ("k", k), ("v", v), ("out", out), ("lse", lse), ("seqlens", seqlens))
+    _contiguous(named)
+    _on_device(q.device, named)
     if window is not None:
         if q.dtype != torch.bfloat16 or not causal:
             raise ValueError("a sliding window needs bfloat16 inputs and causal=True")
@@ -131,23 +167,32 @@ def fwd_fp8(q, k, v, q_descale, k_descale, v_descale, *, causal: bool = False, s
             seqlens=None, window: int | None = None, out=None, lse=None):
     """FP8 prefill through ``fa_fwd_fp8``: q [B, H, Lq, 128], k, v [B, Hkv, Lk, 128] as E4M3
     codes (uint8 or float8_e4m3fn), descales fp32 [B, H] / [B, Hkv]. Returns (o bf16, lse fp32)."""
+    _need(q.dim() == 4 and k.dim() == 4 and v.dim() == 4, "q, k, v must be 4-D [B, heads, L, d]")
     B, H, Lq, d = q.shape
     Hkv, Lk = k.shape[1], k.shape[2]
+    _shape(k, (B, Hkv, Lk, d), "k")
+    _shape(v, (B, Hkv, Lk, d), "v")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty((B, H, Lq, d), dtype=torch.bfloat16, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device)
-    for t in (q, k, v, q_descale, k_descale, v_descale, out, lse):
-        if not t.is_contiguous():
-            raise ValueError("libfa needs contiguous tensors")
+    _shape(q_descale, (B, H), "q_descale")
+    _shape(k_descale, (B, Hkv), "k_descale")
+    _shape(v_descale, (B, Hkv), "v_descale")
+    _shape(out, (B, H, Lq, d), "out")
+    _shape(lse, (B, H, Lq), "lse")
     if not all(t.dtype in (torch.uint8, torch.float8_e4m3fn) for t in (q, k, v)):
         raise ValueError("fwd_fp8 needs E4M3 codes (uint8 or float8_e4m3fn) for q, k, v")
     if not all(t.dtype == torch.float32 for t in (q_descale, k_descale, v_descale)) or out.dtype != torch.bfloat16:
         raise ValueError("descales must be float32 and out bfloat16")
-    if seqlens is not None and seqlens.dtype != torch.int32:
-        raise ValueError("seqlens must be int32")
+    _need(lse.dtype == torch.float32, "lse must be float32")
+    _lengths(seqlens, B, "seqlens")
+    named = (("q", q), ("k", k), ("v", v), ("q_descale", q_descale), ("k_descale", k_descale),
+             ("v_descale", v_descale), ("out", out), ("lse", lse), ("seqlens", seqlens))
+    _contiguous(named)
+    _on_device(q.device, named)
     st = lib().fa_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(q_descale), _ptr(k_descale), _ptr(v_descale), _ptr(out),
                           _ptr(lse), B, H, Hkv, Lq, Lk, d, float(scale), int(bool(causal)),
                           0 if window is None else int(window), _ptr(seqlens), _stream(q.device))
@@ -167,24 +212,32 @@ def decode(q, k_cache, v_cache, ctx_lens, *, scale: float | None = None, workspa
     ``workspace``: optional uint8 device tensor of at least ``decode_workspace_bytes``.
     Returns (o [B, H, d] bf16, lse [B, H] fp32).
     """
+    _need(q.dim() == 3 and k_cache.dim() == 4 and v_cache.dim() == 4,
+          "q must be [B, H, d] and the caches [B, Hkv, Lmax, d]")
     B, H, d = q.shape
     Hkv, Lmax = k_cache.shape[1], k_cache.shape[2]
+    _shape(k_cache, (B, Hkv, Lmax, d), "k_cache")
+    _shape(v_cache, (B, Hkv, Lmax, d), "v_cache")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    _shape(out, (B, H, d), "out")
+    _shape(lse, (B, H), "lse")
     need = decode_workspace_bytes(B, H, Lmax, d)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    for t in (q, k_cache, v_cache, out, lse, ctx_lens, workspace):
-        if not t.is_contiguous():
-            raise ValueError("libfa needs contiguous tensors")
     if not (q.dtype == k_cache.dtype == v_cache.dtype == out.dtype == torch.bfloat16):
         raise ValueError("decode needs bfloat16 q, caches and out")
-    if ctx_lens.dtype != torch.int32:
-        raise ValueError("ctx_lens must be int32")
+    _need(lse.dtype == torch.float32, "lse must be float32")
+    _need(ctx_lens is not None, "ctx_lens is required")
+    _lengths(ctx_lens, B, "ctx_lens")
+    named = (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("out", out), ("lse", lse),
+             ("ctx_lens", ctx_lens), ("workspace", workspace))
+    _contiguous(named)
+    _on_device(q.device, named)
     wsb = workspace.numel() * workspace.element_size()
     if window is None:
         st = lib().fa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), B, H, Hkv, Lmax, d,
@@ -205,8 +258,13 @@ def decode_paged(q, k_pages, v_pages, block_table, ctx_lens, *, scale: float | N
     q: [B, H, d] bf16; k_pages, v_pages: [num_pages, Hkv, P, d] bf16; block_table: int32
     [B, max_pages]; ctx_lens: int32 [B]. Returns (o [B, H, d] bf16, lse [B, H] fp32).
     """
+    _need(q.dim() == 3 and k_pages.dim() == 4 and v_pages.dim() == 4 and block_table.dim() == 2,
+          "q must be [B, H, d], the pools [num_pages, Hkv, P, d] and the block table [B, max_pages]")
     B, H, d = q.shape
     num_pages, Hkv, P = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
+    _shape(k_pages, (num_pages, Hkv, P, d), "k_pages")
+    _shape(v_pages, (num_pages, Hkv, P, d), "v_pages")
+    _need(block_table.shape[0] == B, f"block_table must have B = {B} rows, got {block_table.shape[0]}")
     max_pages = block_table.shape[1]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -214,16 +272,22 @@ def decode_paged(q, k_pages, v_pages, block_table, ctx_lens, *, scale: float | N
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    _shape(out, (B, H, d), "out")
+    _shape(lse, (B, H), "lse")
     need = decode_workspace_bytes(B, H, max_pages * P, d)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    for t in (q, k_pages, v_pages, block_table, out, lse, ctx_lens, workspace):
-        if not t.is_contiguous():
-            raise ValueError("libfa needs contiguous tensors")
     if not (q.dtype == k_pages.dtype == v_pages.dtype == out.dtype == torch.bfloat16):
         raise ValueError("decode_paged needs bfloat16 q, pages and out")
-    if ctx_lens.dtype != torch.int32 or block_table.dtype != torch.int32:
-        raise ValueError("ctx_lens and block_table must be int32")
+    if block_table.dtype != torch.int32:
+        raise ValueError("block_table must be int32")
+    _need(lse.dtype == torch.float32, "lse must be float32")
+    _need(ctx_lens is not None, "ctx_lens is required")
+    _lengths(ctx_lens, B, "ctx_lens")
+    named = (("q", q), ("k_pages", k_pages), ("v_pages", v_pages), ("block_table", block_table), ("out", out),
+             ("lse", lse), ("ctx_lens", ctx_lens), ("workspace", workspace))
+    _contiguous(named)
+    _on_device(q.device, named)
     st = lib().fa_decode_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(out), _ptr(lse), B, H, Hkv, d,
                                float(scale), P, num_pages, _ptr(block_table), max_pages, _ptr(ctx_lens),
                                0 if window is None else int(window), _ptr(workspace),
@@ -244,25 +308,34 @@ def bwd(q, k, v, o, dout, lse, *, causal: bool = False, scale: float | None = No
     q, o, dout: [B, H, Lq, d]; k, v: [B, Hkv, Lk, d], bf16, contiguous; lse: [B, H, Lq] fp32
     from ``fwd``; causal, scale, seqlens and window as passed to ``fwd``.
     """
+    _need(q.dim() == 4 and k.dim() == 4 and v.dim() == 4, "q, k, v must be 4-D [B, heads, L, d]")
     B, H, Lq, d = q.shape
     Hkv, Lk = k.shape[1], k.shape[2]
+    _shape(k, (B, Hkv, Lk, d), "k")
+    _shape(v, (B, Hkv, Lk, d), "v")
+    _shape(o, q.shape, "o")
+    _shape(dout, q.shape, "dout")
+    _shape(lse, (B, H, Lq), "lse")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
+    _shape(dq, q.shape, "dq")
+    _shape(dk, k.shape, "dk")
+    _shape(dv, k.shape, "dv")
     need = bwd_workspace_bytes(B, H, Lq)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    for t in (q, k, v, o, dout, lse, dq, dk, dv, workspace):
-        if not t.is_contiguous():
-            raise ValueError("libfa needs contiguous tensors")
     if not all(t.dtype == torch.bfloat16 for t in (q, k, v, o, dout, dq, dk, dv)):
         raise ValueError("bwd needs bfloat16 q, k, v, o, dout and gradients")
     if lse.dtype != torch.float32:
         raise ValueError("lse must be float32")
-    if seqlens is not None and seqlens.dtype != torch.int32:
-        raise ValueError("seqlens must be int32")
+    _lengths(seqlens, B, "seqlens")
+    named = (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("lse", lse), ("dq", dq), ("dk", dk),
+             ("dv", dv), ("seqlens", seqlens), ("workspace", workspace))
+    _contiguous(named)
+    _on_device(q.device, named)
     if window is not None:
         if not causal:
             raise ValueError("a sliding window needs causal=True")

@@ -25,3 +25,14 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    try:
+        from parity import SUMMARY
+    except Exception:  # pragma: no cover
+        return
+    if SUMMARY:
+        terminalreporter.section("parity statistics")
+        for line in SUMMARY:
+            terminalreporter.write_line(line)

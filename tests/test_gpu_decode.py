@@ -119,11 +119,3 @@ def test_decode_deterministic():
     o1, l1 = fa.decode(x["q"], x["k_cache"], x["v_cache"], x["ctx_lens"])
     o2, l2 = fa.decode(x["q"], x["k_cache"], x["v_cache"], x["ctx_lens"])
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
-
-
-def test_decode_full_size_workload_sampled():
-    w = fa_inputs.WORKLOADS["decode_B64_H32_Hkv8_ctx32768_d128"]
-    rng = np.random.default_rng(w.seed)
-    heads = sorted({(int(rng.integers(w.B)), int(rng.integers(w.H))) for _ in range(24)} | {(0, 0), (w.B - 1, w.H - 1)})
-    st, *_ = run_decode(w.B, w.H, w.Hkv, w.L, w.d, seed=w.seed, len_range=w.len_range, heads=heads)
-    print(w.name, st, flush=True)

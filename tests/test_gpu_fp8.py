@@ -1,8 +1,12 @@
-"""GPU parity of fa_fwd_fp8 (FP8 prefill) against the fp64 FP8 oracle (oracle/fp8.py), through
-the C ABI, at the tolerance of the bf16 prefill. The oracle writes out the same P rounding, so
-only fp32 sums differ, plus probabilities that lie within fp32 error of an E4M3 rounding
-midpoint and may round the other way; each such element adds its one-spacing effect on O to
-that row's allowance (parity.fp8_flip_slack)."""
+"""GPU parity of fa_fwd_fp8 (FP8 prefill), through the C ABI, against two references:
+
+* the fp64 FP8 oracle (oracle/fp8.py), at the tolerance of the bf16 prefill. The oracle writes
+  out the same P rounding, so only fp32 sums differ, plus probabilities that lie within fp32
+  error of an E4M3 rounding midpoint and may round the other way; each such element adds its
+  one-spacing effect on O to that row's allowance (parity.fp8_flip_slack);
+* exact fp64 attention of the dequantised inputs (oracle.attention_head), at the E4M3 bound
+  the FP8 oracle is pinned to: 2^-4 of sum_j P_ij |V_jc| per element (parity.compare_fp8_exact),
+  which does not depend on the P scheme being the kernel's own."""
 import math
 import sys
 
@@ -12,7 +16,7 @@ import torch
 
 import fa_inputs
 import oracle
-from parity import compare, fp8_flip_slack
+from parity import compare, compare_fp8_exact, fp8_flip_slack, report
 
 pytestmark = pytest.mark.gpu
 
@@ -48,8 +52,10 @@ def run_fp8(B, H, Hkv, Lq, Lk, *, causal, seed, window=None, len_range=None):
             Q = oracle.e4m3_decode(arrs[0][b, h]) * float(arrs[3][b, h])
             K = oracle.e4m3_decode(arrs[1][b, kvh]) * float(arrs[4][b, kvh])
             V = oracle.e4m3_decode(arrs[2][b, kvh]) * float(arrs[5][b, kvh])
-            slack[b, h] = fp8_flip_slack(Q, K, V, scale=scale, causal=causal,
-                                         n_valid=None if sl is None else int(sl[b]), window=window)
+            n_b = None if sl is None else int(sl[b])
+            slack[b, h] = fp8_flip_slack(Q, K, V, scale=scale, causal=causal, n_valid=n_b, window=window)
+            compare_fp8_exact(o[b, h], lse[b, h], Q, K, V, scale=scale, causal=causal, n_valid=n_b, window=window,
+                              what=f"fp8 b{b} h{h}")
     st = compare(o, lse, O, LSE, bf16_out=True, what=f"fp8 B{B} H{H}/{Hkv} L{Lq}x{Lk} c{int(causal)} W{window}",
                  o_slack=slack)
     print(f"  rows with flip allowance: {int((slack > 0).sum())} of {slack.size}; {st}", flush=True)
@@ -105,4 +111,8 @@ def test_fp8_full_size_16k_sampled():
         V = oracle.e4m3_decode(x["v"][0, h].cpu().numpy()) * float(x["v_descale"][0, h])
         O, LSE = oracle.attention_fp8_head(Q, K, V, scale=w.scale, causal=True, rows=rows)
         slack = fp8_flip_slack(Q, K, V, scale=w.scale, causal=True, rows=rows)
-        compare(o[0, h, rows], lse[0, h, rows], O, LSE, bf16_out=True, what=f"fp8 16k head {h}", o_slack=slack)
+        st = compare(o[0, h, rows], lse[0, h, rows], O, LSE, bf16_out=True, what=f"fp8 16k head {h}", o_slack=slack)
+        r = compare_fp8_exact(o[0, h, rows], lse[0, h, rows], Q, K, V, scale=w.scale, causal=True, rows=rows,
+                              what=f"fp8 16k head {h}")
+        report(f"fa_fwd_fp8 {w.name}, head {h}, {len(rows)} rows: vs FP8 oracle O {st['o_max']:.3g} "
+               f"LSE {st['lse_max']:.3g}; vs exact attention max err/allowance {r:.3f}")

@@ -260,23 +260,3 @@ def test_empty_and_degenerate_calls():
     with pytest.raises(fa.FaError) as e:
         fa.fwd(q96, q96, q96)
     assert e.value.status == 2
-
-
-# Full-size workloads, in the launch configuration the benchmark uses, checked on
-# sampled query rows of sampled heads (the oracle computes those rows one by one).
-def _sample_rows(L, rng, n=48):
-    picks = {0, 1, 2, 63, 64, 127, 128, L - 1, L - 2, L // 2}
-    picks |= set(rng.integers(0, L, size=n).tolist())
-    return sorted(p for p in picks if 0 <= p < L)
-
-
-@pytest.mark.parametrize("name", ["causal_prefill_B4_H16_L2048_d64", "causal_prefill_B1_H32_L16384_d128",
-                                  "gqa_varlen_prefill_B8_H32_Hkv8_L8192_d128"])
-def test_full_size_workload_sampled(name):
-    w = fa_inputs.WORKLOADS[name]
-    rng = np.random.default_rng(w.seed)
-    rows = _sample_rows(w.L, rng)
-    heads = sorted({(int(rng.integers(w.B)), int(rng.integers(w.H))) for _ in range(4)} | {(0, 0), (w.B - 1, w.H - 1)})
-    st = run_case(w.B, w.H, w.Hkv, w.L, w.L, w.d, causal=w.causal, seed=w.seed, len_range=w.len_range,
-                  rows=rows, heads=heads)
-    print(name, st, flush=True)
