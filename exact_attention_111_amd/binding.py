@@ -6,6 +6,7 @@ There is no fallback: if libfa.so is missing or a call fails, an exception is ra
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import math
 import os
@@ -13,6 +14,7 @@ import os
 import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+SERIAL_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa_serial.so")
 
 FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 SYMBOLS = ("fa_fwd", "fa_fwd_sliding_window", "fa_fwd_fp8", "fa_fwd_f32", "fa_decode", "fa_decode_sliding_window", "fa_decode_paged",
@@ -39,7 +41,27 @@ def lib() -> ctypes.CDLL:
     if not os.path.exists(_LIB_PATH):
         raise ImportError(f"libfa.so not found at {_LIB_PATH}; build it with "
                           "`python -m exact_attention_111_amd.build` (needs hipcc)")
-    L = ctypes.CDLL(_LIB_PATH)
+    _lib = _declare(ctypes.CDLL(_LIB_PATH))
+    return _lib
+
+
+@contextlib.contextmanager
+def library_variant(path: str):
+    """Route this module's calls through another build of the same C ABI while the context is
+    open (the race-check build libfa_serial.so, for its test)."""
+    global _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} not found; build it with `python -m exact_attention_111_amd.build`")
+    saved = lib()
+    _lib = _declare(ctypes.CDLL(path))
+    try:
+        yield _lib
+    finally:
+        _lib = saved
+
+
+def _declare(L: ctypes.CDLL) -> ctypes.CDLL:
+    """Argument and result types of every entry point (include/fa.h)."""
     vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     fwd_args = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp, vp]
     L.fa_fwd.argtypes = fwd_args
@@ -69,7 +91,6 @@ def lib() -> ctypes.CDLL:
     L.fa_bwd_sliding_window.restype = i32
     L.fa_status_string.argtypes = [i32]
     L.fa_status_string.restype = ctypes.c_char_p
-    _lib = L
     return L
 
 

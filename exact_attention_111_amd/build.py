@@ -5,6 +5,11 @@
 Every source is compiled by hipcc for gfx950 only, with the packed-fp32 VALU forms
 disabled (the compiler would otherwise pair independent fp32 operations itself).
 ``--asm DIR`` additionally writes the gfx950 assembly of each source to DIR.
+
+A second library, libfa_serial.so, is built from the same sources with FA_SERIAL_PIPELINE
+defined: every direct-to-LDS load stage then waits for all loads and for the whole
+workgroup on both sides. It is the race check of the load pipelines (its results must be
+bit for bit those of libfa.so) and is only loaded by that test.
 """
 from __future__ import annotations
 
@@ -20,6 +25,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfa.so")
+SERIAL_LIB = os.path.join(PKG, "libfa_serial.so")
 SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_fwd_fp8.hip", "fa_decode.hip", "fa_bwd.hip"]
 ARCH = "gfx950"
 
@@ -38,16 +44,20 @@ def common_flags():
 
 
 def build(verbose: bool = False, asm_dir: str | None = None) -> str:
-    """Compile every source and link libfa.so next to this file; returns its path."""
+    """Compile every source and link libfa.so (and the race-check libfa_serial.so) next to
+    this file; returns the path of libfa.so."""
     cc = hipcc()
+    variants = [(LIB, []), (SERIAL_LIB, ["-DFA_SERIAL_PIPELINE"])]
     with tempfile.TemporaryDirectory(prefix="fa_build_") as tmp:
-        objs = []
         procs = []
-        for src in SOURCES:
-            obj = os.path.join(tmp, src + ".o")
-            cmd = [cc, *common_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
-            procs.append((src, cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
-            objs.append(obj)
+        objs = {lib: [] for lib, _ in variants}
+        for lib, defs in variants:
+            for src in SOURCES:
+                obj = os.path.join(tmp, os.path.basename(lib) + "." + src + ".o")
+                cmd = [cc, *common_flags(), *defs, "-c", os.path.join(CSRC, src), "-o", obj]
+                procs.append((src, cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                                                         text=True)))
+                objs[lib].append(obj)
         failed = False
         for src, cmd, p in procs:
             out, _ = p.communicate()
@@ -59,12 +69,14 @@ def build(verbose: bool = False, asm_dir: str | None = None) -> str:
                 sys.stderr.write(f"[fa build] {src}:\n{out}\n")
         if failed:
             raise RuntimeError("libfa build failed")
-        tmp_lib = LIB + ".tmp"
-        link = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib]
-        r = subprocess.run(link, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-        if r.returncode != 0:
-            raise RuntimeError(f"libfa link failed:\n{' '.join(link)}\n{r.stdout}")
-        os.replace(tmp_lib, LIB)
+        for lib, _ in variants:
+            tmp_lib = lib + ".tmp"
+            # -Bsymbolic: each library binds its own internal symbols (both export the same names)
+            link = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,-Bsymbolic", *objs[lib], "-o", tmp_lib]
+            r = subprocess.run(link, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+            if r.returncode != 0:
+                raise RuntimeError(f"libfa link failed:\n{' '.join(link)}\n{r.stdout}")
+            os.replace(tmp_lib, lib)
     if asm_dir:
         os.makedirs(asm_dir, exist_ok=True)
         for src in SOURCES:

@@ -40,47 +40,32 @@ namespace {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-#ifndef FA_BWD_RB
-#define FA_BWD_RB 1
-#endif
-#ifndef FA_BWD_QB
-#define FA_BWD_QB 1
-#endif
-#ifndef FA_BWD_WPE
-#define FA_BWD_WPE 2
-#endif
-#ifndef FA_BWD_KVNS
-#define FA_BWD_KVNS 4
-#endif
-#ifndef FA_BWD_QNS
-#define FA_BWD_QNS 4
-#endif
-
 template <int D>
 struct BwdCfg {
   static constexpr int NW = 4;        // waves per workgroup
   static constexpr int NT = 64 * NW;
+  static constexpr int WAVES_PER_SIMD = 2;  // two waves share a SIMD (256 registers each)
   static constexpr int ROWB = 2 * D;  // bytes per row
   static constexpr int QKS = D / 16;  // 32x32x16 k-steps over d
   static constexpr int NB = D / 32;   // 32-wide blocks over d
   // dK/dV: 32 keys per wave, RB blocks of 32 query rows per step.
   static constexpr int KEYS = 32 * NW;
-  static constexpr int RB = FA_BWD_RB;
+  static constexpr int RB = 1;
   static constexpr int QSTEP = 32 * RB;
   static constexpr int QTILE = QSTEP * ROWB;              // bytes of a Q or dO tile
   static constexpr int KV_STAGE = 2 * QTILE + QSTEP * 8;  // Q | dO | (offset, D) per row
-  static constexpr int KV_NS = FA_BWD_KVNS;               // stages in the ring
+  static constexpr int KV_NS = 4;                         // stages in the ring
   static constexpr int KV_SEGS = QTILE / 1024 / NW;       // 1 KB direct loads per wave and tile
   static constexpr int RV_LANES = QSTEP / NW / 2;         // lanes loading two rows' pairs each
   static constexpr int KV_LOADS = 2 * KV_SEGS + 1;        // direct loads per wave and stage
   // dQ: QB blocks of 32 query rows per wave, 32 keys per step.
-  static constexpr int QB = FA_BWD_QB;
+  static constexpr int QB = 1;
   static constexpr int WROWS = 32 * QB;
   static constexpr int QROWS = WROWS * NW;
   static constexpr int KSTEP = 32;
   static constexpr int KTILE = KSTEP * ROWB;  // bytes of a K or V tile
   static constexpr int Q_STAGE = 2 * KTILE;   // K | V
-  static constexpr int Q_NS = FA_BWD_QNS;
+  static constexpr int Q_NS = 4;
   static constexpr int Q_SEGS = KTILE / 1024 / NW;
   static constexpr int Q_LOADS = 2 * Q_SEGS;
   static_assert(KV_SEGS >= 1 && Q_SEGS >= 1, "tile smaller than one load per wave");
@@ -219,7 +204,7 @@ __global__ __launch_bounds__(256) void bwd_dot_kernel(const BwdArgs a) {
 // ---------------------------------------------------------------------------------------
 // XCD_ORDER: workgroups in the prefill's XCD order (used with GQA, see below).
 template <int D, bool XCD_ORDER>
-__global__ __launch_bounds__(BwdCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(FA_BWD_WPE, FA_BWD_WPE)))
+__global__ __launch_bounds__(BwdCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(BwdCfg<D>::WAVES_PER_SIMD, BwdCfg<D>::WAVES_PER_SIMD)))
 void bwd_dkdv_kernel(const BwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using C = BwdCfg<D>;
@@ -302,6 +287,7 @@ void bwd_dkdv_kernel(const BwdArgs a) {
     char* st = smem + slot * C::KV_STAGE;
     const u32x4 rq = raw_buffer_rsrc(qsrc + row0 * C::ROWB, nrows * C::ROWB);
     const u32x4 rd = raw_buffer_rsrc(dsrc + row0 * C::ROWB, nrows * C::ROWB);
+    serial_fence();
 #pragma unroll
     for (int i = 0; i < C::KV_SEGS; ++i) lds_dma16_buf(rq, toff[i], lds_addr(st + (w * C::KV_SEGS + i) * 1024));
 #pragma unroll
@@ -310,6 +296,7 @@ void bwd_dkdv_kernel(const BwdArgs a) {
     const u32x4 rr = raw_buffer_rsrc(wsrc + row0 * 8, nrows * 8);
     if (lane < C::RV_LANES)
       lds_dma16_buf(rr, (unsigned)(16 * (C::RV_LANES * w + lane)), lds_addr(st + 2 * C::QTILE + 16 * C::RV_LANES * w));
+    serial_fence();
     if (++iqs == nqs) {
       iqs = qs_first;
       ++ihq;
@@ -412,7 +399,7 @@ void bwd_dkdv_kernel(const BwdArgs a) {
 // ---------------------------------------------------------------------------------------
 // XCD_ORDER: workgroups grouped by KV head on the XCDs (used with GQA, see below).
 template <int D, bool XCD_ORDER>
-__global__ __launch_bounds__(BwdCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(FA_BWD_WPE, FA_BWD_WPE)))
+__global__ __launch_bounds__(BwdCfg<D>::NT) __attribute__((amdgpu_waves_per_eu(BwdCfg<D>::WAVES_PER_SIMD, BwdCfg<D>::WAVES_PER_SIMD)))
 void bwd_dq_kernel(const BwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using C = BwdCfg<D>;
@@ -510,11 +497,13 @@ void bwd_dq_kernel(const BwdArgs a) {
     char* st = smem + (t % C::Q_NS) * C::Q_STAGE;
     const u32x4 rk = raw_buffer_rsrc(ksrc + (size_t)k0 * C::ROWB, nrows * C::ROWB);
     const u32x4 rv = raw_buffer_rsrc(vsrc + (size_t)k0 * C::ROWB, nrows * C::ROWB);
+    serial_fence();
 #pragma unroll
     for (int i = 0; i < C::Q_SEGS; ++i) lds_dma16_buf(rk, toff[i], lds_addr(st + (w * C::Q_SEGS + i) * 1024));
 #pragma unroll
     for (int i = 0; i < C::Q_SEGS; ++i)
       lds_dma16_buf(rv, toff[i], lds_addr(st + C::KTILE + (w * C::Q_SEGS + i) * 1024));
+    serial_fence();
   };
 
   __syncthreads();  // the zero fill is done before any direct load lands

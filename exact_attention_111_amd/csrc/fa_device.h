@@ -70,6 +70,20 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Race-check build (FA_SERIAL_PIPELINE defined): every direct-to-LDS stage is preceded and
+// followed by serial_fence(), which waits for all of this wave's loads and then for the whole
+// workgroup. No load is then in flight while anyone computes, and a slot is refilled only
+// after every wave is past its earlier reads. The arithmetic is unchanged, so this build must
+// give results bit for bit equal to the pipelined one; a missing wait or an early slot reuse
+// in the pipelined kernels shows up as a difference. In the product build it is empty.
+// Callers must reach it in every wave the same number of times (it contains a barrier).
+__device__ __forceinline__ void serial_fence() {
+#ifdef FA_SERIAL_PIPELINE
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+#endif
+}
+
 // A wave-uniform pointer, held in SGPRs (the value must be the same in every lane).
 // readfirstlane returns int: each half goes through unsigned before widening, or a low
 // word with bit 31 set would be sign-extended over the high word.

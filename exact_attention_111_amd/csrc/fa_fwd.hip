@@ -239,6 +239,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
     const int k0 = kbase + t * C::BN;
     char* dst = smem + slot;
     const IT* src = which ? vp : kp;
+    serial_fence();
     if constexpr (sizeof(IT) == 2) {
       const u32x4 rsrc = raw_buffer_rsrc(reinterpret_cast<const char*>(src) + (size_t)k0 * C::ROWB,
                                          (unsigned)max(kv_end - k0, 0) * C::ROWB);
@@ -258,6 +259,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
         *reinterpret_cast<u32x4*>(dst + r * C::ROWB + (cp << 4)) = Load8<IT>::load(src + (size_t)key * D + 8 * c);
       }
     }
+    serial_fence();
   };
 
   // Operand reads: K operand f = (half kb = f / QKS, k-step f % QKS) of the tile at byte

@@ -49,10 +49,7 @@ constexpr int kF8BM = 32 * kF8NW;      // query rows per workgroup
 constexpr int kF8BN = 64;              // keys per tile
 constexpr int kF8Tile = kF8BN * kF8D;  // bytes of a K or V tile
 constexpr int kF8Stage = 2 * kF8Tile;  // K | V
-#ifndef FA_FP8_NS
-#define FA_FP8_NS 4
-#endif
-constexpr int kF8NS = FA_FP8_NS;       // stages in the ring
+constexpr int kF8NS = 4;               // stages in the ring
 constexpr int kF8KS = kF8D / 64;       // 32x32x64 k-steps over d
 constexpr int kF8NB = kF8D / 32;       // 32-wide blocks of O^T
 static_assert(kF8Tile == 1024 * kF8NW, "one 1 KB direct load per wave and tile");
@@ -181,8 +178,10 @@ __global__ __launch_bounds__(kF8NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     const int k0 = kbase + t * kF8BN;
     const unsigned nrows = (unsigned)max(kv_end - k0, 0);
     char* st = smem + (t % kF8NS) * kF8Stage;
+    serial_fence();
     lds_dma16_buf(raw_buffer_rsrc(ksrc + (size_t)k0 * kF8D, nrows * kF8D), koff, lds_addr(st + w * 1024));
     lds_dma16_buf(raw_buffer_rsrc(vsrc + (size_t)k0 * kF8D, nrows * kF8D), voff, lds_addr(st + kF8Tile + w * 1024));
+    serial_fence();
   };
 
   if (ntk > 0) {

@@ -201,3 +201,11 @@ def test_fwd_fp8_validation():
     assert call(H=3, Hkv=2) == INV
     assert call(scale=0.0) == INV
     assert call(B=0) == OK
+
+
+def test_race_check_library_exports_the_same_abi():
+    """libfa_serial.so (the fenced race-check build) exports the same entry points."""
+    import ctypes
+    L = ctypes.CDLL(fa.binding.SERIAL_LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(L, name), name
