@@ -8,10 +8,14 @@ One step is one pass of the whole path over resident synthetic inputs:
   * decode:  fa_decode (split-K + combine) on B=64 requests, 32 query / 8 KV heads,
     d=128, bf16 cache with per-request context lengths uniform in [8192, 32768],
     counted as the K and V bytes of every request's context.
-The headline ``value`` is the prefill TFLOP/s; decode KV GB/s is reported beside it, and the
-backward of the same prefill (fa_bwd, timed on its own after the step) beside that.
-Kernel durations come from HIP events on the stream the kernels run on (torch's
-current stream), over exactly K timed steps after W warm-up steps.
+The headline ``value`` is the prefill TFLOP/s from the median launch time; decode KV GB/s is
+reported beside it, and the backward of the same prefill (fa_bwd, timed on its own after the
+step) beside that. ``workloads`` then times each of the five workloads alone (K launches after
+W warm-ups: the single-head fp32 check in microseconds only, the prefills in TFLOP/s and as a
+fraction of the bf16 MFMA peak, decode in KV GB/s), and the FP8 prefill (fa_fwd_fp8) of the
+16,384-token workload against the fp8 MFMA peak. Kernel durations come from HIP events on
+the stream the kernels run on (torch's current stream), over exactly K timed steps after W
+warm-up steps.
 
 ``cpu_baseline`` times the CPU fp64 oracle (as it is, untuned) on a bounded sample of
 the same prefill workload: consecutive blocks of query rows of one head, until about
@@ -34,7 +38,13 @@ sys.path.insert(0, ROOT)
 
 METRIC = "bf16 attn-fwd TFLOP/s & % MFMA peak at L=16k d=128; decode KV-read GB/s"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA
 PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
+# The pages' own figure, quoted as context only: another vendor's part, not a target.
+CONTEXT = {"fa2_forward_flops_utilisation_a100": "50-70% of theoretical peak",
+           "hardware": "NVIDIA A100 (another vendor's part)",
+           "source": "'2.1 FlashAttention-2 的核心思想' §2.1.6 and §2.1.10 (quoting the official report)",
+           "use": "context only; not comparable to an MI355X fraction and not a target"}
 # Backward work counted as five products of the forward's size (S, dP, dV, dK, dQ):
 # 2.5 times the forward's FLOP, whatever the kernels recompute.
 BWD_FLOP_PER_FWD = 2.5
@@ -42,6 +52,7 @@ PREFILL = "causal_prefill_B1_H32_L16384_d128"
 DECODE = "decode_B64_H32_Hkv8_ctx32768_d128"
 # Sources whose compiled kernels a committed counter profile describes.
 KERNEL_SOURCES = {"prefill": ["fa_fwd.hip", "fa_tiles.h", "fa_device.h", "fa_launch.h"],
+                  "fp8": ["fa_fwd_fp8.hip", "fa_tiles.h", "fa_device.h", "fa_launch.h"],
                   "decode": ["fa_decode.hip", "fa_device.h", "fa_launch.h"],
                   "backward": ["fa_bwd.hip", "fa_tiles.h", "fa_device.h", "fa_launch.h"]}
 
@@ -77,10 +88,11 @@ def source_digest(part):
     return h.hexdigest()[:16]
 
 
-def traffic_record(part):
-    """Calibrated HBM bytes per launch of one part, from the `traffic-record:` line of a
-    rocprofv3 FETCH_SIZE/WRITE_SIZE summary under profiles/. Returned only while the
-    kernel sources are byte-identical to the ones profiled; otherwise (None, reason)."""
+def traffic_record(part, workload=None):
+    """Calibrated HBM bytes per launch of one part (and workload, if given; records without a
+    workload are the part's bench workload), from the `traffic-record:` line of a rocprofv3
+    FETCH_SIZE/WRITE_SIZE summary under profiles/. Returned only while the kernel sources
+    are byte-identical to the ones profiled; otherwise (None, reason)."""
     want = source_digest(part)
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
         with open(path, encoding="utf-8") as fh:
@@ -88,12 +100,26 @@ def traffic_record(part):
                 if not line.startswith("traffic-record:"):
                     continue
                 rec = json.loads(line.split(":", 1)[1])
-                if rec.get("part") != part:
+                if rec.get("part") != part or rec.get("workload") != workload:
                     continue
                 if rec.get("source_sha256_16") != want:
                     return None, f"{os.path.relpath(path, ROOT)} profiled other sources"
                 return rec, os.path.relpath(path, ROOT)
     return None, "no counter profile"
+
+
+def host_cpu():
+    """The host CPU model and its logical core count (for the CPU baseline)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    return model, os.cpu_count()
 
 
 def cpu_baseline(w, x, seconds):
@@ -129,7 +155,9 @@ def cpu_baseline(w, x, seconds):
             rows_done += len(rows)
             hi -= block
     dt = time.perf_counter() - t0
+    model, ncpu = host_cpu()
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "host_cpu": model, "os_cpu_count": ncpu,
             "sample": f"{rows_done} query rows over {heads_touched} head(s) of {w.name} (newest rows first), "
                       f"fp64, {dt:.1f} s",
             "seconds": round(dt, 2)}
@@ -179,6 +207,131 @@ def _window_pairs(lens, W):
     return float(tot)
 
 
+def workload_call(w, dev, window=None, page=None, fp8=False):
+    """One launch of a named workload on resident inputs, as a callable, with its algorithmic
+    work per launch: (fn, work, unit). Prefill work is 4 H d per visible (query, key) pair,
+    causal counted as half the square (TFLOP/s); decode work is the K and V bytes of every
+    request's context (GB/s)."""
+    import torch
+
+    import exact_attention_111_amd as fa
+    import fa_inputs
+    if w.kind == "decode" and page is not None:
+        x = fa_inputs.paged_decode_inputs(w.B, w.H, w.Hkv, w.L, w.d, page, seed=w.seed, device=dev,
+                                          len_range=w.len_range)
+    elif w.kind == "prefill" and fp8:
+        x = fa_inputs.fp8_prefill_inputs(w.B, w.H, w.Hkv, w.L, w.L, w.d, seed=w.seed, device=dev,
+                                         len_range=w.len_range)
+    else:
+        x = fa_inputs.workload_inputs(w, device=dev)
+    if w.kind == "decode" and page is not None:
+        o = torch.empty_like(x["q"])
+        lse = torch.empty((w.B, w.H), dtype=torch.float32, device=dev)
+        cap = x["block_table"].shape[1] * page
+        ws = torch.empty(max(16, fa.decode_workspace_bytes(w.B, w.H, cap, w.d)), dtype=torch.uint8, device=dev)
+        fn = lambda: fa.decode_paged(x["q"], x["k_pages"], x["v_pages"], x["block_table"],  # noqa: E731
+                                     x["ctx_lens"], scale=w.scale, window=window, workspace=ws, out=o, lse=lse)
+        ctx = x["ctx_lens_cpu"].to(torch.int64)
+        if window is not None:
+            ctx = ctx.clamp(max=window)
+        work, unit = float(2 * w.Hkv * w.d * 2 * int(ctx.sum())), "GB/s"
+    elif w.kind == "decode":
+        o = torch.empty_like(x["q"])
+        lse = torch.empty((w.B, w.H), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(16, fa.decode_workspace_bytes(w.B, w.H, w.L, w.d)), dtype=torch.uint8, device=dev)
+        fn = lambda: fa.decode(x["q"], x["k_cache"], x["v_cache"], x["ctx_lens"], scale=w.scale,  # noqa: E731
+                               workspace=ws, out=o, lse=lse, window=window)
+        ctx = x["ctx_lens_cpu"].to(torch.int64)
+        if window is not None:
+            ctx = ctx.clamp(max=window)
+        work, unit = float(2 * w.Hkv * w.d * 2 * int(ctx.sum())), "GB/s"
+    elif fp8:
+        o = torch.empty((w.B, w.H, w.L, w.d), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((w.B, w.H, w.L), dtype=torch.float32, device=dev)
+        sl = x.get("seqlens")
+        fn = lambda: fa.fwd_fp8(x["q"], x["k"], x["v"], x["q_descale"], x["k_descale"],  # noqa: E731
+                                x["v_descale"], causal=w.causal, scale=w.scale, seqlens=sl, window=window,
+                                out=o, lse=lse)
+        lens = x["seqlens_cpu"].to(torch.float64) if sl is not None else torch.full((w.B,), float(w.L))
+        pairs = float((lens * lens).sum()) * (0.5 if w.causal else 1.0)
+        if window is not None:
+            pairs = _window_pairs(lens.tolist(), window)
+        work, unit = 4.0 * w.H * w.d * pairs, "TFLOP/s"
+    else:
+        o = torch.empty_like(x["q"])
+        lse = torch.empty((w.B, w.H, w.L), dtype=torch.float32, device=dev)
+        sl = x.get("seqlens")
+        fn = lambda: fa.fwd(x["q"], x["k"], x["v"], causal=w.causal, scale=w.scale, seqlens=sl,  # noqa: E731
+                            out=o, lse=lse, window=window)
+        lens = x["seqlens_cpu"].to(torch.float64) if sl is not None else torch.full((w.B,), float(w.L))
+        pairs = float((lens * lens).sum()) * (0.5 if w.causal else 1.0)
+        if window is not None:
+            pairs = _window_pairs(lens.tolist(), window)
+        work, unit = 4.0 * w.H * w.d * pairs, "TFLOP/s"
+    return fn, work, unit
+
+
+def time_launches(fn, steps, warmup):
+    """Per-launch times (ms) of `steps` launches of fn after `warmup` untimed ones, from HIP
+    events on torch's current stream (the stream the kernels are launched on)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
+def median(ms):
+    import statistics
+    return statistics.median(ms)
+
+
+def workload_lines(steps, warmup, dev, prefill_median_ms):
+    """Each of the five workloads timed alone (bench.py's launch configuration), plus the FP8
+    prefill of the 16,384-token workload. Rates come from the median launch time."""
+    import fa_inputs
+    out = {}
+    for name, w in fa_inputs.WORKLOADS.items():
+        fn, work, unit = workload_call(w, dev)
+        ms = time_launches(fn, steps, warmup)
+        med = median(ms)
+        sp = spread(ms)
+        if w.name == "single_head_fp32_L128_d64":
+            out[name] = {"us_median": round(1e3 * med, 2), "us_p10": round(1e3 * sp["ms_p10"], 2),
+                         "us_p90": round(1e3 * sp["ms_p90"], 2),
+                         "note": "launch-bound (4.19 MFLOP); reported in microseconds only"}
+        elif unit == "TFLOP/s":
+            rate = work / (med * 1e-3) / 1e12
+            tr, src = traffic_record("prefill", None if name == PREFILL else name)
+            out[name] = {**sp, "tflops": round(rate, 2), "frac": round(rate / PEAK_BF16_TFLOPS, 4),
+                         "flop_per_launch": work, "bound": "mfma", "peak_tflops": PEAK_BF16_TFLOPS,
+                         "traffic": tr["bytes_per_launch"] if tr else None, "traffic_source": src}
+        else:
+            rate = work / (med * 1e-3) / 1e9
+            out[name] = {**sp, "gbps": round(rate, 1), "frac": round(rate / PEAK_HBM_GBPS, 4),
+                         "kv_bytes_per_launch": work, "bound": "hbm", "peak_gbps": PEAK_HBM_GBPS}
+        del fn
+    w = fa_inputs.WORKLOADS[PREFILL]
+    fn, work, _ = workload_call(w, dev, fp8=True)
+    ms = time_launches(fn, steps, warmup)
+    med = median(ms)
+    rate = work / (med * 1e-3) / 1e12
+    tr, src = traffic_record("fp8")
+    out["fp8:" + PREFILL] = {**spread(ms), "tflops": round(rate, 2), "frac": round(rate / PEAK_FP8_TFLOPS, 4),
+                             "peak_tflops": PEAK_FP8_TFLOPS, "bound": "mfma (fp8)",
+                             "speedup_vs_bf16": round(prefill_median_ms / med, 3),
+                             "kernel": "fwd_fp8_kernel (E4M3 Q/K/V, per-head descales)",
+                             "traffic": tr["bytes_per_launch"] if tr else None, "traffic_source": src}
+    del fn
+    return out
+
+
 def run_only(part, steps, warmup, window=None, page=None, fp8=False):
     """Time one part alone (for profiling): the prefill or decode part of the step, a plain
     1 GiB device copy, or any named workload. Prints the kernel time and, for workloads,
@@ -214,58 +367,7 @@ def run_only(part, steps, warmup, window=None, page=None, fp8=False):
         dst = torch.empty_like(src)
         fn = lambda: dst.copy_(src)  # noqa: E731
     elif name in fa_inputs.WORKLOADS:
-        w = fa_inputs.WORKLOADS[name]
-        if w.kind == "decode" and page is not None:
-            x = fa_inputs.paged_decode_inputs(w.B, w.H, w.Hkv, w.L, w.d, page, seed=w.seed, device=dev,
-                                              len_range=w.len_range)
-        else:
-            x = fa_inputs.workload_inputs(w, device=dev)
-        if w.kind == "decode" and page is not None:
-            o = torch.empty_like(x["q"])
-            lse = torch.empty((w.B, w.H), dtype=torch.float32, device=dev)
-            cap = x["block_table"].shape[1] * page
-            ws = torch.empty(max(16, fa.decode_workspace_bytes(w.B, w.H, cap, w.d)), dtype=torch.uint8, device=dev)
-            fn = lambda: fa.decode_paged(x["q"], x["k_pages"], x["v_pages"], x["block_table"],  # noqa: E731
-                                         x["ctx_lens"], scale=w.scale, window=window, workspace=ws, out=o, lse=lse)
-            ctx = x["ctx_lens_cpu"].to(torch.int64)
-            if window is not None:
-                ctx = ctx.clamp(max=window)
-            work, unit = float(2 * w.Hkv * w.d * 2 * int(ctx.sum())), "GB/s"
-        elif w.kind == "decode":
-            o = torch.empty_like(x["q"])
-            lse = torch.empty((w.B, w.H), dtype=torch.float32, device=dev)
-            ws = torch.empty(max(16, fa.decode_workspace_bytes(w.B, w.H, w.L, w.d)), dtype=torch.uint8, device=dev)
-            fn = lambda: fa.decode(x["q"], x["k_cache"], x["v_cache"], x["ctx_lens"], scale=w.scale,  # noqa: E731
-                                   workspace=ws, out=o, lse=lse, window=window)
-            ctx = x["ctx_lens_cpu"].to(torch.int64)
-            if window is not None:
-                ctx = ctx.clamp(max=window)
-            work, unit = float(2 * w.Hkv * w.d * 2 * int(ctx.sum())), "GB/s"
-        elif fp8:
-            x = fa_inputs.fp8_prefill_inputs(w.B, w.H, w.Hkv, w.L, w.L, w.d, seed=w.seed, device=dev,
-                                             len_range=w.len_range)
-            o = torch.empty((w.B, w.H, w.L, w.d), dtype=torch.bfloat16, device=dev)
-            lse = torch.empty((w.B, w.H, w.L), dtype=torch.float32, device=dev)
-            sl = x.get("seqlens")
-            fn = lambda: fa.fwd_fp8(x["q"], x["k"], x["v"], x["q_descale"], x["k_descale"],  # noqa: E731
-                                    x["v_descale"], causal=w.causal, scale=w.scale, seqlens=sl, window=window,
-                                    out=o, lse=lse)
-            lens = x["seqlens_cpu"].to(torch.float64) if sl is not None else torch.full((w.B,), float(w.L))
-            pairs = float((lens * lens).sum()) * (0.5 if w.causal else 1.0)
-            if window is not None:
-                pairs = _window_pairs(lens.tolist(), window)
-            work, unit = 4.0 * w.H * w.d * pairs, "TFLOP/s"
-        else:
-            o = torch.empty_like(x["q"])
-            lse = torch.empty((w.B, w.H, w.L), dtype=torch.float32, device=dev)
-            sl = x.get("seqlens")
-            fn = lambda: fa.fwd(x["q"], x["k"], x["v"], causal=w.causal, scale=w.scale, seqlens=sl,  # noqa: E731
-                                out=o, lse=lse, window=window)
-            lens = x["seqlens_cpu"].to(torch.float64) if sl is not None else torch.full((w.B,), float(w.L))
-            pairs = float((lens * lens).sum()) * (0.5 if w.causal else 1.0)
-            if window is not None:
-                pairs = _window_pairs(lens.tolist(), window)
-            work, unit = 4.0 * w.H * w.d * pairs, "TFLOP/s"
+        fn, work, unit = workload_call(fa_inputs.WORKLOADS[name], dev, window, page, fp8)
         rate = (work, unit)
     else:
         raise SystemExit(f"unknown part or workload: {part}")
@@ -336,12 +438,15 @@ def main():
     dec_ms = [e[1].elapsed_time(e[2]) for e in events]
     fwd_avg = sum(fwd_ms) / len(fwd_ms)
     dec_avg = sum(dec_ms) / len(dec_ms)
+    fwd_med = median(fwd_ms)
+    dec_med = median(dec_ms)
 
+    # Rates from the median launch time (the mean is reported beside it).
     flop = 4.0 * wp.B * wp.H * wp.L * wp.L * wp.d / 2.0
-    tflops = flop / (fwd_avg * 1e-3) / 1e12
+    tflops = flop / (fwd_med * 1e-3) / 1e12
     ctx = xd["ctx_lens_cpu"].to(torch.int64)
     kv_bytes = float(2 * wd.Hkv * wd.d * 2 * int(ctx.sum()))
-    gbps = kv_bytes / (dec_avg * 1e-3) / 1e9
+    gbps = kv_bytes / (dec_med * 1e-3) / 1e9
 
     # Backward of the same prefill (the gradients of that step for a synthetic dO), timed on
     # its own after the step: K launches of fa_bwd after W warm-up launches.
@@ -364,8 +469,10 @@ def main():
     bwd_ms = [a_.elapsed_time(b_) for a_, b_ in bev]
     bwd_avg = sum(bwd_ms) / len(bwd_ms)
     bwd_flop = BWD_FLOP_PER_FWD * 4.0 * wp.B * wp.H * wp.L * wp.L * wp.d / 2.0
-    bwd_tflops = bwd_flop / (bwd_avg * 1e-3) / 1e12
+    bwd_tflops = bwd_flop / (median(bwd_ms) * 1e-3) / 1e12
+    del grads, ws_b, do_p
 
+    workloads = workload_lines(args.steps, args.warmup, dev, fwd_med)
     gemm = library_gemm_tflops(dev)
 
     tr_p, src_p = traffic_record("prefill")
@@ -390,12 +497,14 @@ def main():
                    "decode": {"B": wd.B, "H": wd.H, "Hkv": wd.Hkv, "Lmax": wd.L, "d": wd.d,
                               "ctx_range": list(wd.len_range), "seed": wd.seed,
                               "ctx_sum": int(ctx.sum())}},
-        "prefill": {"ms": round(fwd_avg, 4), "ms_min": round(min(fwd_ms), 4), **spread(fwd_ms), "tflops": round(tflops, 2),
+        "prefill": {"ms_mean": round(fwd_avg, 4), "ms_min": round(min(fwd_ms), 4), **spread(fwd_ms),
+                    "tflops": round(tflops, 2),
                     "pct_mfma_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2), "flop_per_launch": flop},
-        "decode": {"value": round(gbps, 1), "unit": "GB/s", "ms": round(dec_avg, 4), "ms_min": round(min(dec_ms), 4),
+        "decode": {"value": round(gbps, 1), "unit": "GB/s", "ms_mean": round(dec_avg, 4),
+                   "ms_min": round(min(dec_ms), 4),
                    **spread(dec_ms),
                    "pct_hbm_peak": round(100 * gbps / PEAK_HBM_GBPS, 2), "kv_bytes_per_launch": kv_bytes},
-        "backward": {"ms": round(bwd_avg, 4), "ms_min": round(min(bwd_ms), 4), **spread(bwd_ms),
+        "backward": {"ms_mean": round(bwd_avg, 4), "ms_min": round(min(bwd_ms), 4), **spread(bwd_ms),
                      "tflops": round(bwd_tflops, 2),
                      "pct_mfma_peak": round(100 * bwd_tflops / PEAK_BF16_TFLOPS, 2), "flop_per_launch": bwd_flop,
                      "flop_counting": "5 products of the forward's size (2.5x forward FLOP)",
@@ -403,7 +512,8 @@ def main():
                      "traffic": tr_b["bytes_per_launch"] if tr_b else None, "traffic_unit": "bytes/launch",
                      "traffic_source": src_b},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "timing": "median launch",
+                     "achieved_from_mean": round(flop / (fwd_avg * 1e-3) / 1e12, 2),
                      "traffic": tr_p["bytes_per_launch"] if tr_p else None, "traffic_unit": "bytes/launch",
                      "traffic_algorithmic": alg_p, "traffic_source": src_p,
                      "kernel": "fwd_kernel<128, bf16, bf16, false>",
@@ -413,6 +523,8 @@ def main():
                             "traffic": tr_d["bytes_per_launch"] if tr_d else None, "traffic_unit": "bytes/launch",
                             "traffic_algorithmic": kv_bytes, "traffic_source": src_d,
                             "kernels": "decode_split_kernel<128, false, true> + decode_combine_kernel<128, true>"},
+        "workloads": workloads,
+        "context": CONTEXT,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
