@@ -16,8 +16,9 @@ import torch
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 SERIAL_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa_serial.so")
 
-FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
-SYMBOLS = ("fa_fwd", "fa_fwd_sliding_window", "fa_fwd_fp8", "fa_fwd_f32", "fa_decode", "fa_decode_sliding_window", "fa_decode_paged",
+FA_OK, FA_ERR_INVALID, FA_ERR_UNSUPPORTED, FA_ERR_HIP, FA_ERR_TOO_LARGE = 0, 1, 2, 3, 4
+SYMBOLS = ("fa_fwd", "fa_fwd_sliding_window", "fa_fwd_fp8", "fa_fwd_f32", "fa_decode", "fa_decode_sliding_window",
+           "fa_decode_noalloc", "fa_decode_paged",
            "fa_decode_workspace_bytes", "fa_bwd", "fa_bwd_sliding_window", "fa_bwd_workspace_bytes",
            "fa_status_string")
 
@@ -76,6 +77,8 @@ def _declare(L: ctypes.CDLL) -> ctypes.CDLL:
     L.fa_decode_workspace_bytes.restype = ctypes.c_size_t
     L.fa_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, vp, vp, ctypes.c_size_t, vp]
     L.fa_decode.restype = i32
+    L.fa_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, vp, vp]
+    L.fa_decode_noalloc.restype = i32
     L.fa_decode_sliding_window.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, vp, i32, vp,
                                            ctypes.c_size_t, vp]
     L.fa_decode_sliding_window.restype = i32
@@ -269,6 +272,39 @@ def decode(q, k_cache, v_cache, ctx_lens, *, scale: float | None = None, workspa
                                             Lmax, d, float(scale), _ptr(ctx_lens), int(window), _ptr(workspace), wsb,
                                             _stream(q.device))
         _check(st, "fa_decode_sliding_window")
+    return out, lse
+
+
+def decode_noalloc(q, k_cache, v_cache, ctx_lens, *, scale: float | None = None, out=None, lse=None):
+    """Single-token decode through ``fa_decode_noalloc``: as ``decode`` without a workspace
+    (the library's fixed per-GPU array holds the split partials; calls that need more than
+    FA_DECODE_NOALLOC_MAX_WORKSPACE_BYTES raise FaError with FA_ERR_TOO_LARGE). Pass ``out``
+    and ``lse`` to make the call allocate nothing at all."""
+    _need(q.dim() == 3 and k_cache.dim() == 4 and v_cache.dim() == 4,
+          "q must be [B, H, d] and the caches [B, Hkv, Lmax, d]")
+    B, H, d = q.shape
+    Hkv, Lmax = k_cache.shape[1], k_cache.shape[2]
+    _shape(k_cache, (B, Hkv, Lmax, d), "k_cache")
+    _shape(v_cache, (B, Hkv, Lmax, d), "v_cache")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    _shape(out, (B, H, d), "out")
+    _shape(lse, (B, H), "lse")
+    if not (q.dtype == k_cache.dtype == v_cache.dtype == out.dtype == torch.bfloat16):
+        raise ValueError("decode needs bfloat16 q, caches and out")
+    _need(lse.dtype == torch.float32, "lse must be float32")
+    _need(ctx_lens is not None, "ctx_lens is required")
+    _lengths(ctx_lens, B, "ctx_lens")
+    named = (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("out", out), ("lse", lse), ("ctx_lens", ctx_lens))
+    _contiguous(named)
+    _on_device(q.device, named)
+    st = lib().fa_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse), B, H, Hkv, Lmax, d,
+                                 float(scale), _ptr(ctx_lens), _stream(q.device))
+    _check(st, "fa_decode_noalloc")
     return out, lse
 
 

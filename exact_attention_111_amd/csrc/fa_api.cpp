@@ -8,6 +8,7 @@
 #include "fa.h"
 
 #include <math.h>
+#include <stdint.h>
 
 #include "fa_launch.h"
 
@@ -40,8 +41,9 @@ fa_status validate_fwd(const void* q, const void* k, const void* v, const void* 
   return FA_OK;
 }
 
-fa_status validate_decode(const void* q, const void* kc, const void* vc, const void* o, const void* lse, int B, int H,
-                          int Hkv, int Lmax, int d, float scale, const int32_t* ctx, const void* ws, size_t ws_bytes) {
+// Everything of a decode call but its workspace.
+fa_status validate_decode_args(const void* q, const void* kc, const void* vc, const void* o, const void* lse, int B,
+                               int H, int Hkv, int Lmax, int d, float scale, const int32_t* ctx) {
   if (B < 0 || H < 0 || Hkv < 1 || Lmax < 0 || d < 1) return FA_ERR_INVALID;
   if (H % Hkv != 0) return FA_ERR_INVALID;
   if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_INVALID;
@@ -51,10 +53,20 @@ fa_status validate_decode(const void* q, const void* kc, const void* vc, const v
   if (!tensor_ok(lse, (long long)B * H)) return FA_ERR_INVALID;
   if (B > 0 && (ctx == nullptr || (reinterpret_cast<uintptr_t>(ctx) & 3u) != 0)) return FA_ERR_INVALID;
   if (!supported_d(d)) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+fa_status validate_decode(const void* q, const void* kc, const void* vc, const void* o, const void* lse, int B, int H,
+                          int Hkv, int Lmax, int d, float scale, const int32_t* ctx, const void* ws, size_t ws_bytes) {
+  const fa_status s = validate_decode_args(q, kc, vc, o, lse, B, H, Hkv, Lmax, d, scale, ctx);
+  if (s != FA_OK) return s;
   const size_t need = fa_decode_workspace_bytes(B, H, Lmax, d);
   if (need > 0 && (ws == nullptr || !aligned16(ws) || ws_bytes < need)) return FA_ERR_INVALID;
   return FA_OK;
 }
+
+static_assert(fa::kDecodeScratchBytes == FA_DECODE_NOALLOC_MAX_WORKSPACE_BYTES,
+              "the fixed decode workspace and its documented size agree");
 
 fa_status validate_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                        const void* lse, const void* dq, const void* dk, const void* dv, int B, int H, int Hkv, int Lq,
@@ -166,6 +178,18 @@ fa_status fa_decode(const void* q, const void* k_cache, const void* v_cache, voi
                     stream);
 }
 
+fa_status fa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse, int B,
+                            int H, int Hkv, int Lmax, int d, float scale, const int32_t* ctx_lens, void* stream) {
+  // Arguments as fa_decode checks them, then the call's workspace against the fixed one.
+  const fa_status s = validate_decode_args(q, k_cache, v_cache, o, lse, B, H, Hkv, Lmax, d, scale, ctx_lens);
+  if (s != FA_OK) return s;
+  if (fa_decode_workspace_bytes(B, H, Lmax, d) > FA_DECODE_NOALLOC_MAX_WORKSPACE_BYTES) return FA_ERR_TOO_LARGE;
+  if (B == 0 || H == 0) return FA_OK;
+  void* ws = nullptr;
+  if (fa::decode_scratch(&ws) != hipSuccess) return FA_ERR_HIP;
+  return decode_run(q, k_cache, v_cache, o, lse, B, H, Hkv, Lmax, d, scale, ctx_lens, 0, nullptr, 0, 0, 0, ws, stream);
+}
+
 fa_status fa_decode_sliding_window(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
                                    int B, int H, int Hkv, int Lmax, int d, float scale, const int32_t* ctx_lens,
                                    int window, void* workspace, size_t workspace_bytes, void* stream) {
@@ -228,6 +252,7 @@ const char* fa_status_string(fa_status s) {
     case FA_ERR_INVALID: return "FA_ERR_INVALID";
     case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
     case FA_ERR_HIP: return "FA_ERR_HIP";
+    case FA_ERR_TOO_LARGE: return "FA_ERR_TOO_LARGE";
   }
   return "FA_ERR_UNKNOWN";
 }

@@ -36,6 +36,8 @@
 //     numbers of up to 128 pages (two per lane; a balanced run reloads them when it moves
 //     past them) and takes each step's page with a uniform readlane, so the K/V loads stay
 //     16-byte row loads.
+#include <mutex>
+
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -524,6 +526,31 @@ hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   if (p.table != nullptr) return p.d == 64 ? launch_d<64, true>(p, stream) : launch_d<128, true>(p, stream);
   return p.d == 64 ? launch_d<64, false>(p, stream) : launch_d<128, false>(p, stream);
+}
+
+// The decode workspace of fa_decode_noalloc: a fixed device array, one copy per GPU, held for
+// the life of the process. Its name is only a host-side handle; the kernels get its device
+// address, looked up once per device (with that device current) and kept.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace fa

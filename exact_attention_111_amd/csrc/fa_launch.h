@@ -63,6 +63,11 @@ struct DecodeParams {
 inline int decode_num_chunks(int Lmax) { return (Lmax + kDecodeChunk - 1) / kDecodeChunk; }
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 
+// Size of the fixed per-GPU decode workspace of fa_decode_noalloc, and its device address on
+// the current device (looked up once per device, then cached).
+constexpr size_t kDecodeScratchBytes = (size_t)32 << 20;
+hipError_t decode_scratch(void** ptr);
+
 // Backward (bf16): per query row the exp2 offset of the saved LSE and D = rowsum(dO * O),
 // then dK/dV per key block and dQ per query block, both recomputing P from Q, K and the LSE.
 struct BwdParams {

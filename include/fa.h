@@ -32,7 +32,8 @@
  *     synchronisation; the kernels clamp each to [0, capacity].
  *   - Head dimensions 64 and 128 are supported; any other d returns
  *     FA_ERR_UNSUPPORTED (never a slower fallback path).
- *   - Calls are reentrant; the library has no global mutable state.
+ *   - Calls are reentrant; the library has no global mutable state, except the fixed
+ *     workspace of fa_decode_noalloc (see there).
  */
 #ifndef FA_H_
 #define FA_H_
@@ -48,7 +49,8 @@ typedef enum fa_status {
   FA_OK = 0,
   FA_ERR_INVALID = 1,     /* a null/misaligned pointer, a negative size, H % Hkv != 0, ... */
   FA_ERR_UNSUPPORTED = 2, /* valid request this library does not implement (e.g. d = 96) */
-  FA_ERR_HIP = 3          /* the HIP runtime refused the launch */
+  FA_ERR_HIP = 3,         /* the HIP runtime refused the launch */
+  FA_ERR_TOO_LARGE = 4    /* fa_decode_noalloc: the call needs more than its fixed workspace */
 } fa_status;
 
 /*
@@ -141,6 +143,29 @@ size_t fa_decode_workspace_bytes(int B, int H, int Lmax, int d);
 fa_status fa_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
                     int B, int H, int Hkv, int Lmax, int d, float scale, const int32_t* ctx_lens,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_decode_noalloc — fa_decode for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. It takes no
+ * workspace argument and calls no allocating routine (no hipMalloc / hipFree): the split
+ * partials go to a fixed device array inside the library, one per GPU, of
+ * FA_DECODE_NOALLOC_MAX_WORKSPACE_BYTES (32 MiB), held by each GPU the library runs on until
+ * the process ends. Its device address is looked up once per device, on that device's first
+ * call. Everything else (arguments, layouts, results, errors) is as for fa_decode; the
+ * results are bit for bit those of fa_decode with a caller workspace.
+ *   - A call whose fa_decode_workspace_bytes(B, H, Lmax, d) exceeds the fixed size returns
+ *     FA_ERR_TOO_LARGE and enqueues nothing (the 64-request, 32k-context workload of
+ *     32 query heads needs 16.25 MiB).
+ *   - Every call on a GPU shares that GPU's array, which keeps the last call's partials.
+ *     Nothing in it needs to start at zero: a call writes every partial it later reads.
+ *   - Calls that may run at the same time on one GPU (on different streams, or from
+ *     different threads without ordering) race on the array and give wrong results; order
+ *     them (one stream, or events between streams).
+ */
+#define FA_DECODE_NOALLOC_MAX_WORKSPACE_BYTES ((size_t)32 << 20)
+fa_status fa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                            int B, int H, int Hkv, int Lmax, int d, float scale, const int32_t* ctx_lens,
+                            void* stream);
 
 /*
  * fa_decode_sliding_window — fa_decode with a sliding window (reading as for

@@ -22,7 +22,7 @@ def test_library_exports_every_declared_symbol():
     L = fa.lib()
     names = _declared_functions()
     assert set(names) == {"fa_fwd", "fa_fwd_sliding_window", "fa_fwd_fp8", "fa_fwd_f32", "fa_decode", "fa_decode_sliding_window",
-                          "fa_decode_paged",
+                          "fa_decode_noalloc", "fa_decode_paged",
                           "fa_decode_workspace_bytes", "fa_bwd", "fa_bwd_sliding_window", "fa_bwd_workspace_bytes",
                           "fa_status_string"}
     assert set(names) == set(fa.binding.SYMBOLS)
@@ -35,6 +35,7 @@ def test_status_strings():
     assert fa.status_string(1) == "FA_ERR_INVALID"
     assert fa.status_string(2) == "FA_ERR_UNSUPPORTED"
     assert fa.status_string(3) == "FA_ERR_HIP"
+    assert fa.status_string(4) == "FA_ERR_TOO_LARGE"
 
 
 # Fake, never-dereferenced device addresses: validation only looks at their values.
@@ -209,3 +210,24 @@ def test_race_check_library_exports_the_same_abi():
     L = ctypes.CDLL(fa.binding.SERIAL_LIB_PATH)
     for name in _declared_functions():
         assert hasattr(L, name), name
+
+
+def test_decode_noalloc_validation():
+    """The allocation-free decode checks its arguments as fa_decode does, and rejects a call
+    whose workspace would exceed the fixed 32 MiB array, all on the host (nothing enqueued)."""
+    L = fa.lib()
+    INV, UNS, BIG, OK = (fa.binding.FA_ERR_INVALID, fa.binding.FA_ERR_UNSUPPORTED, fa.binding.FA_ERR_TOO_LARGE,
+                         fa.binding.FA_OK)
+
+    def call(q=A, k=A, v=A, o=A2, lse=A2, B=2, H=4, Hkv=2, Lmax=100, d=128, scale=0.1, ctx=A):
+        return L.fa_decode_noalloc(q, k, v, o, lse, B, H, Hkv, Lmax, d, scale, ctx, None)
+    assert call(q=None) == INV
+    assert call(ctx=None) == INV
+    assert call(H=5) == INV
+    assert call(scale=0.0) == INV
+    assert call(d=96) == UNS
+    # the decode workload (64 requests, 32 heads, 32k keys) fits: 16.25 MiB of partials
+    assert L.fa_decode_workspace_bytes(64, 32, 32768, 128) <= 32 << 20
+    # 256 requests of 64 heads at 64k keys would need 260 MiB
+    assert call(B=256, H=64, Hkv=8, Lmax=65536) == BIG
+    assert call(B=0) == OK  # empty: nothing to do, no device touched
