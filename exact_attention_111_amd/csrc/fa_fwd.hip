@@ -362,6 +362,15 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
     const int qb = e / 32, h = (e % 32) / 16, r = e % 16;
     lc[qb][e & 1] += pv[e];
     pb[qb][2 * h + (r >> 3)][r & 7] = (__bf16)pv[e];
+    if (e & 1) {
+      // The pair (e - 1, e) is complete: convert it here, beside this step's MFMA, rather
+      // than after the part's check (where nothing overlaps the conversions).
+      u32x4 u = as_u32x4(pb[qb][2 * h + (r >> 3)]);
+      unsigned wd = u[(r & 7) >> 1];
+      asm volatile("" : "+v"(wd));
+      u[(r & 7) >> 1] = wd;
+      pb[qb][2 * h + (r >> 3)] = as_bf16x8(u);
+    }
   };
   // The rows' sums as they stood before a part was added (kept for the rare rescale).
   auto snapshot = [&](float (&lo)[QB][2]) {
