@@ -62,4 +62,18 @@ __device__ __forceinline__ void xcd_tile_order(int hw, int nwg, int ntq, int& bh
   }
 }
 
+// Tile id (as numbered for xcd_tile_order) that workgroup p of nprog takes in its round r, or
+// -1 when it has no more. With one workgroup per tile (nprog == ntiles) workgroup p takes tile
+// p. Otherwise nprog is a multiple of 8: workgroup p stays on XCD p % 8 (the tiles whose ids
+// are p mod 8, which xcd_tile_order lists heaviest first) and takes one of them in each round
+// of nprog / 8, forward through the round in even rounds and backward in odd ones, so that
+// the workgroup with a round's heaviest tile gets the next round's lightest.
+__device__ __forceinline__ int tile_of_program(int p, int r, int nprog, int ntiles) {
+  if (nprog == ntiles) return r == 0 ? p : -1;
+  const int x = p & 7, s = p >> 3, S = nprog >> 3;
+  const int slot = S * r + ((r & 1) ? S - 1 - s : s);
+  const int id = 8 * slot + x;
+  return id < ntiles ? id : -1;
+}
+
 }  // namespace fa

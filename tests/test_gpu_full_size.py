@@ -28,13 +28,11 @@ import torch
 
 import fa_inputs
 import oracle
-from parity import compare, report
+from parity import check_written, compare, nan_filled_outputs, report, rows_per_workgroup
 
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
-QTILE = 256  # query rows per prefill workgroup
-WBLK = 32    # query rows per wave
 
 
 def _fa():
@@ -45,38 +43,6 @@ def _fa():
 def announce(**case):
     print("\n[case] " + " ".join(f"{k}={v}" for k, v in case.items()), flush=True)
     sys.stdout.flush()
-
-
-def rows_per_workgroup(n_valid, rng):
-    """One random row of every 32-row block below n_valid, plus the first and last row of every
-    256-row query tile (clipped to n_valid)."""
-    rows = set()
-    for t0 in range(0, n_valid, QTILE):
-        rows.add(t0)
-        rows.add(min(t0 + QTILE, n_valid) - 1)
-    for b0 in range(0, n_valid, WBLK):
-        rows.add(int(rng.integers(b0, min(b0 + WBLK, n_valid))))
-    return np.array(sorted(rows), dtype=np.int64)
-
-
-def nan_filled_outputs(shape_o, shape_lse, dtype):
-    o = torch.full(shape_o, float("nan"), dtype=dtype, device=DEV)
-    lse = torch.full(shape_lse, float("nan"), dtype=torch.float32, device=DEV)
-    return o, lse
-
-
-def check_written(o, lse, n_valid):
-    """Whole-tensor check on the GPU: rows below n_valid[b] finite, rows at or past it O = 0
-    and LSE = -inf (n_valid None: every row valid)."""
-    B = o.shape[0]
-    L = o.shape[2]
-    for b in range(B):
-        n = L if n_valid is None else int(n_valid[b])
-        assert torch.isfinite(o[b, :, :n]).all(), f"batch {b}: a valid O row is not finite (unwritten?)"
-        assert torch.isfinite(lse[b, :, :n]).all(), f"batch {b}: a valid LSE is not finite (unwritten?)"
-        if n < L:
-            assert torch.all(o[b, :, n:] == 0), f"batch {b}: padding rows of O are not 0"
-            assert torch.all(torch.isneginf(lse[b, :, n:])), f"batch {b}: padding LSE is not -inf"
 
 
 def run_prefill_workload(name, every_row):

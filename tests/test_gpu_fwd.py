@@ -8,7 +8,7 @@ import torch
 
 import fa_inputs
 import oracle
-from parity import compare
+from parity import check_written, compare, nan_filled_outputs, rows_per_workgroup
 
 pytestmark = pytest.mark.gpu
 
@@ -260,3 +260,37 @@ def test_empty_and_degenerate_calls():
     with pytest.raises(fa.FaError) as e:
         fa.fwd(q96, q96, q96)
     assert e.value.status == 2
+
+
+@pytest.mark.parametrize("B,H,Hkv,L,d,causal,window", [
+    (3, 37, 37, 1100, 64, True, None),    # 555 tiles; a head count that is not a multiple of 8
+    (2, 24, 24, 2500, 128, False, None),  # 480 tiles: the second round is only partly filled
+    (2, 32, 8, 2300, 128, True, None),    # GQA, 576 tiles
+    (2, 16, 16, 3000, 64, True, 700),     # sliding window, 384 tiles
+])
+def test_more_tiles_than_compute_units(B, H, Hkv, L, d, causal, window):
+    """Dense inputs with more 256-row query tiles than the GPU has compute units run several
+    tiles per workgroup. Outputs start NaN: every row of every tile must be written, and every
+    (batch, head) matches the oracle on a row of every 32-row wave block and on the first and
+    last row of every query tile ("2.1 FlashAttention-2 的核心思想" §2.1.5: the tiled
+    computation equals the plain one, whatever the order the tiles are taken in)."""
+    announce(entry="fa_fwd" if window is None else "fa_fwd_sliding_window", B=B, H=H, Hkv=Hkv, L=L, d=d,
+             causal=causal, window=window, seed=900 + d)
+    x = fa_inputs.prefill_inputs(B, H, Hkv, L, L, d, seed=900 + d, device=DEV)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = nan_filled_outputs((B, H, L, d), (B, H, L), torch.bfloat16, device=DEV)
+    _fa().fwd(x["q"], x["k"], x["v"], causal=causal, scale=scale, out=o, lse=lse, window=window)
+    torch.cuda.synchronize()
+    check_written(o, lse, None)
+    rng = np.random.default_rng(901)
+    rows = rows_per_workgroup(L, rng)
+    group = H // Hkv
+    o_h, lse_h = o.cpu(), lse.cpu()
+    for b in range(B):
+        for h in range(H):
+            O, LSE = oracle.attention_head(
+                fa_inputs.as_oracle_f64(x["q"][b, h]), fa_inputs.as_oracle_f64(x["k"][b, h // group]),
+                fa_inputs.as_oracle_f64(x["v"][b, h // group]), scale=scale, causal=causal, rows=rows,
+                window=window)
+            ri = torch.from_numpy(rows)
+            compare(o_h[b, h, ri], lse_h[b, h, ri], O, LSE, bf16_out=True, what=f"B{B} H{H}/{Hkv} L{L} b{b} h{h}")
