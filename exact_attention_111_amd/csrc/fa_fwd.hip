@@ -631,7 +631,9 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
       // Zero the buffers once, so that operand reads of a slot never written (dummy work at
       // the end of the pipeline) see finite values.
       for (int i = tid; i < (int)sizeof(smem) / 16; i += C::NT) *reinterpret_cast<u32x4*>(smem + 16 * i) = u32x4{0u, 0u, 0u, 0u};
-      __syncthreads();
+      // Only the LDS writes must be done before the loads land: a full __syncthreads() would
+      // also wait for this wave's Q loads and put their latency before the K/V loads' own.
+      lds_barrier();
       stage(0, 0, k_slot(0));
       stage(0, 1, v_slot(0));
       if (1 < ntk) stage(1, 0, k_slot(1));
@@ -677,8 +679,9 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
     constexpr bool kStaged = sizeof(OT) == 2;
     constexpr int RS = 2 * D + 16;  // bytes per staged row; the pad spreads the rows over the banks
     static_assert(!kStaged || C::NW * 32 * QB * RS <= (int)sizeof(smem), "staged O must fit in LDS");
-    // Every wave's loads have landed and its last operand reads have returned: LDS is free.
-    if constexpr (kStaged) __syncthreads();
+    // Every wave has waited for its own loads, so once all have returned their last operand
+    // reads LDS is free (an LDS-only barrier: the O stores need not wait for anything else).
+    if constexpr (kStaged) lds_barrier();
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const float lh = lc[qb][0] + lc[qb][1];
@@ -713,9 +716,10 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
       if (my_q[qb] < a.Lq && half == 0)
         a.lse[(size_t)(b * a.H + h) * a.Lq + my_q[qb]] = row_ok ? (m[qb] + __log2f(lt)) * kLn2 : kNegInf;
     }
-    // The next tile clears and refills the LDS buffers: every wave must be done with them
-    // (its last loads landed, its last reads returned) first.
-    __syncthreads();
+    // The next tile clears and refills the LDS buffers: every wave must be done with them (its
+    // loads landed before the epilogue, its staged-O reads returned) first. The O stores may
+    // still be in flight.
+    lds_barrier();
   }
 #endif
 }
