@@ -53,6 +53,8 @@ constexpr int kF8NS = 4;               // stages in the ring
 constexpr int kF8KS = kF8D / 64;       // 32x32x64 k-steps over d
 constexpr int kF8NB = kF8D / 32;       // 32-wide blocks of O^T
 static_assert(kF8Tile == 1024 * kF8NW, "one 1 KB direct load per wave and tile");
+constexpr int kF8RS = 2 * kF8D + 16;   // bytes per row of staged O (the pad spreads rows over banks)
+constexpr int kF8Smem = kF8NS * kF8Stage > kF8NW * 32 * kF8RS ? kF8NS * kF8Stage : kF8NW * 32 * kF8RS;
 
 __device__ __forceinline__ int f8_kxor(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int f8_vxor(int r) { return 2 * (((r >> 1) & 1) | (((r >> 3) & 1) << 1)); }
@@ -75,6 +77,7 @@ struct Fp8Args {
   float* lse;
   int B, H, Hkv, Lq, Lk;
   int group, ntq, nwg;
+  int nprog;  // workgroups launched (tile_of_program)
   float scale_log2;
   int causal, window;
   const int32_t* seqlens;
@@ -82,258 +85,278 @@ struct Fp8Args {
 
 __global__ __launch_bounds__(kF8NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd_fp8_kernel(const Fp8Args a) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __shared__ __attribute__((aligned(1024))) char smem[kF8NS * kF8Stage];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int col = lane & 31, half = lane >> 5;
+  __shared__ __attribute__((aligned(1024))) char smem[kF8Smem];
 
-  // Workgroup order as in the bf16 prefill: (batch, KV head) pairs with group x ntq tiles
-  // each, so the query heads that share a KV head run side by side on one XCD.
-  int pair, u;
-  xcd_tile_order(blockIdx.x, a.nwg, a.group * a.ntq, pair, u);
-  const int qt = u / a.group;
-  const int b = pair / a.Hkv, kvh = pair - b * a.Hkv;
-  const int h = kvh * a.group + (u - qt * a.group);
-  int n_kv = a.Lk, n_q = a.Lq;
-  if (a.seqlens != nullptr) {
-    const int n = min(max(a.seqlens[b], 0), a.Lk);
-    n_kv = n;
-    n_q = n;
-  }
-  const int delta = a.Lk - a.Lq;
-  const int q0 = qt * kF8BM;
-  // Waves w and w + 4 share a SIMD; they take row blocks s and 7 - s, a top block of the tile
-  // with a bottom one, so that every SIMD is left the same work on causal diagonal tiles.
-  const int rblk = w < kF8NW / 2 ? w : 3 * kF8NW / 2 - 1 - w;
-  const int qw0 = q0 + 32 * rblk;
-  const int my_q = qw0 + col;
+  // Tiles of this workgroup, one per round (tile_of_program, as in the bf16 prefill).
+  for (int round = 0;; ++round) {
+    const int tile_id = tile_of_program(blockIdx.x, round, a.nprog, a.nwg);
+    if (tile_id < 0) break;
+    // Per-lane values are rebuilt in every round rather than hoisted out of the round loop.
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 31, half = lane >> 5;
 
-  int kv_end = 0;
-  if (q0 < n_q) {
-    kv_end = n_kv;
-    if (a.causal) kv_end = min(kv_end, min(q0 + kF8BM, n_q) + delta);
-    kv_end = max(kv_end, 0);
-  }
-  kv_end = __builtin_amdgcn_readfirstlane(kv_end);
-  const int kbase = __builtin_amdgcn_readfirstlane(
-      a.window > 0 ? (max(q0 + delta - a.window + 1, 0) / kF8BN) * kF8BN : 0);
-  const int ntk = max((kv_end - kbase + kF8BN - 1) / kF8BN, 0);
-  // Tiles this wave has keys in (causal: up to its last row's newest key); past them it only
-  // moves its share of the tiles into LDS and meets the barriers.
-  const int ntw = __builtin_amdgcn_readfirstlane(
-      a.causal ? min(ntk, max((qw0 + 31 + delta - kbase) / kF8BN + 1, 1)) : ntk);
-
-  // Combined score factor (base 2) and the output descale.
-  const float c = a.scale_log2 * a.q_descale[b * a.H + h] * a.k_descale[b * a.Hkv + kvh];
-  const float dv = a.v_descale[b * a.Hkv + kvh];
-
-  // Q rows as B operands.
-  i32x8 qf[kF8KS];
-  const unsigned char* qrow = a.q + ((size_t)(b * a.H + h) * a.Lq + my_q) * kF8D;
-#pragma unroll
-  for (int ks = 0; ks < kF8KS; ++ks) {
-    u32x4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
-    if (my_q < n_q && ntk > 0) {
-      lo = *reinterpret_cast<const u32x4*>(qrow + 64 * ks + 32 * half);
-      hi = *reinterpret_cast<const u32x4*>(qrow + 64 * ks + 32 * half + 16);
+    // Workgroup order as in the bf16 prefill: (batch, KV head) pairs with group x ntq tiles
+    // each, so the query heads that share a KV head run side by side on one XCD.
+    int pair, u;
+    xcd_tile_order(tile_id, a.nwg, a.group * a.ntq, pair, u);
+    const int qt = u / a.group;
+    const int b = pair / a.Hkv, kvh = pair - b * a.Hkv;
+    const int h = kvh * a.group + (u - qt * a.group);
+    int n_kv = a.Lk, n_q = a.Lq;
+    if (a.seqlens != nullptr) {
+      const int n = min(max(a.seqlens[b], 0), a.Lk);
+      n_kv = n;
+      n_q = n;
     }
-    qf[ks] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-  }
+    const int delta = a.Lk - a.Lq;
+    const int q0 = qt * kF8BM;
+    // Waves w and w + 4 share a SIMD; they take row blocks s and 7 - s, a top block of the tile
+    // with a bottom one, so that every SIMD is left the same work on causal diagonal tiles.
+    const int rblk = w < kF8NW / 2 ? w : 3 * kF8NW / 2 - 1 - w;
+    const int qw0 = q0 + 32 * rblk;
+    const int my_q = qw0 + col;
 
-  f32x16 oacc[kF8NB];
-#pragma unroll
-  for (int nb = 0; nb < kF8NB; ++nb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[nb][r] = 0.f;
-  float m = kNegInf, l = 0.f;
-
-  // LDS addresses. K: lane (half, col) reads row 32 kb + col, logical chunks 4 ks + 2 half
-  // (+1); kv rows of the two key blocks share the swizzle, so kb is an immediate offset.
-  int kaddr[kF8KS][2];
-#pragma unroll
-  for (int ks = 0; ks < kF8KS; ++ks)
-#pragma unroll
-    for (int p = 0; p < 2; ++p) kaddr[ks][p] = col * kF8D + (((4 * ks + 2 * half + p) ^ f8_kxor(col)) << 4);
-  // V^T: lane 16 g + p, read u (keys of bytes 8 u .. 8 u + 7), block nb; reads u + 2 are
-  // 32 rows further on with the same swizzle.
-  int vaddr[2][kF8NB];
-  {
-    const int g = lane >> 4, p = lane & 15;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int key = f8_key(half, 8 * u + (p >> 1));
-#pragma unroll
-      for (int nb = 0; nb < kF8NB; ++nb)
-        vaddr[u][nb] = key * kF8D + (((2 * nb + (g & 1)) ^ f8_vxor(key)) << 4) + 8 * (p & 1);
+    int kv_end = 0;
+    if (q0 < n_q) {
+      kv_end = n_kv;
+      if (a.causal) kv_end = min(kv_end, min(q0 + kF8BM, n_q) + delta);
+      kv_end = max(kv_end, 0);
     }
-  }
-  // Direct-load source offsets of this wave's 1 KB of each tile.
-  const int lrow = w * 8 + (lane >> 3), pch = lane & 7;
-  const unsigned koff = (unsigned)(lrow * kF8D + ((pch ^ f8_kxor(lrow)) << 4));
-  const unsigned voff = (unsigned)(lrow * kF8D + ((pch ^ f8_vxor(lrow)) << 4));
-  const size_t kv_row0 = (size_t)(b * a.Hkv + kvh) * a.Lk;
-  const char* const ksrc = reinterpret_cast<const char*>(a.k) + kv_row0 * kF8D;
-  const char* const vsrc = reinterpret_cast<const char*>(a.v) + kv_row0 * kF8D;
-  auto issue = [&](int t) {
-    const int k0 = kbase + t * kF8BN;
-    const unsigned nrows = (unsigned)max(kv_end - k0, 0);
-    char* st = smem + (t % kF8NS) * kF8Stage;
-    serial_fence();
-    lds_dma16_buf(raw_buffer_rsrc(ksrc + (size_t)k0 * kF8D, nrows * kF8D), koff, lds_addr(st + w * 1024));
-    lds_dma16_buf(raw_buffer_rsrc(vsrc + (size_t)k0 * kF8D, nrows * kF8D), voff, lds_addr(st + kF8Tile + w * 1024));
-    serial_fence();
-  };
+    kv_end = __builtin_amdgcn_readfirstlane(kv_end);
+    const int kbase = __builtin_amdgcn_readfirstlane(
+        a.window > 0 ? (max(q0 + delta - a.window + 1, 0) / kF8BN) * kF8BN : 0);
+    const int ntk = max((kv_end - kbase + kF8BN - 1) / kF8BN, 0);
+    // Tiles this wave has keys in (causal: up to its last row's newest key); past them it only
+    // moves its share of the tiles into LDS and meets the barriers.
+    const int ntw = __builtin_amdgcn_readfirstlane(
+        a.causal ? min(ntk, max((qw0 + 31 + delta - kbase) / kF8BN + 1, 1)) : ntk);
 
-  if (ntk > 0) {
-    for (int i = tid; i < (int)sizeof(smem) / 16; i += kF8NT) reinterpret_cast<u32x4*>(smem)[i] = u32x4{0u, 0u, 0u, 0u};
-    __syncthreads();  // the zero fill is done before any direct load lands
-  }
-#pragma unroll
-  for (int t = 0; t < kF8NS - 1; ++t)
-    if (t < ntk) issue(t);
+    // Combined score factor (base 2) and the output descale.
+    const float c = a.scale_log2 * a.q_descale[b * a.H + h] * a.k_descale[b * a.Hkv + kvh];
+    const float dv = a.v_descale[b * a.Hkv + kvh];
 
-  // S^T of tile t (K from its slot) and its mask on boundary tiles (selects).
-  auto scores = [&](int t, f32x16 (&s)[2]) {
-    const char* kt = smem + (t % kF8NS) * kF8Stage;
+    // Q rows as B operands.
+    i32x8 qf[kF8KS];
+    const unsigned char* qrow = a.q + ((size_t)(b * a.H + h) * a.Lq + my_q) * kF8D;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
+    for (int ks = 0; ks < kF8KS; ++ks) {
+      u32x4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
+      if (my_q < n_q && ntk > 0) {
+        lo = *reinterpret_cast<const u32x4*>(qrow + 64 * ks + 32 * half);
+        hi = *reinterpret_cast<const u32x4*>(qrow + 64 * ks + 32 * half + 16);
+      }
+      qf[ks] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    }
+
+    f32x16 oacc[kF8NB];
 #pragma unroll
-      for (int ks = 0; ks < kF8KS; ++ks) {
-        const u32x4 lo = *reinterpret_cast<const u32x4*>(kt + kaddr[ks][0] + 32 * kb * kF8D);
-        const u32x4 hi = *reinterpret_cast<const u32x4*>(kt + kaddr[ks][1] + 32 * kb * kF8D);
-        const i32x8 ka = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-        s[kb] = mfma_f8(ka, qf[ks], s[kb]);
+    for (int nb = 0; nb < kF8NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[nb][r] = 0.f;
+    float m = kNegInf, l = 0.f;
+
+    // LDS addresses. K: lane (half, col) reads row 32 kb + col, logical chunks 4 ks + 2 half
+    // (+1); kv rows of the two key blocks share the swizzle, so kb is an immediate offset.
+    int kaddr[kF8KS][2];
+#pragma unroll
+    for (int ks = 0; ks < kF8KS; ++ks)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) kaddr[ks][p] = col * kF8D + (((4 * ks + 2 * half + p) ^ f8_kxor(col)) << 4);
+    // V^T: lane 16 g + p, read u (keys of bytes 8 u .. 8 u + 7), block nb; reads u + 2 are
+    // 32 rows further on with the same swizzle.
+    int vaddr[2][kF8NB];
+    {
+      const int g = lane >> 4, p = lane & 15;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int key = f8_key(half, 8 * u + (p >> 1));
+#pragma unroll
+        for (int nb = 0; nb < kF8NB; ++nb)
+          vaddr[u][nb] = key * kF8D + (((2 * nb + (g & 1)) ^ f8_vxor(key)) << 4) + 8 * (p & 1);
       }
     }
-  };
-  auto mask = [&](int t, f32x16 (&s)[2]) {
-    const int k0 = kbase + t * kF8BN;
-    const bool need_mask = (k0 + kF8BN > n_kv) || (a.causal && k0 + kF8BN - 1 > qw0 + delta) ||
-                           (a.window > 0 && k0 < qw0 + 32 + delta - a.window);
-    if (!need_mask) return;
-    // visible: lo <= (key - base) < lim, with base the lane's first key of the tile
-    const int base = k0 + 4 * half;
-    const int lim = min(n_kv - base, a.causal ? my_q + delta + 1 - base : n_kv - base);
-    const int lo = a.window > 0 ? my_q + delta - a.window + 1 - base : -kF8BN;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
-        s[kb][r] = (off >= lim || off < lo) ? kNegInf : s[kb][r];
-      }
-  };
+    // Direct-load source offsets of this wave's 1 KB of each tile.
+    const int lrow = w * 8 + (lane >> 3), pch = lane & 7;
+    const unsigned koff = (unsigned)(lrow * kF8D + ((pch ^ f8_kxor(lrow)) << 4));
+    const unsigned voff = (unsigned)(lrow * kF8D + ((pch ^ f8_vxor(lrow)) << 4));
+    const size_t kv_row0 = (size_t)(b * a.Hkv + kvh) * a.Lk;
+    const char* const ksrc = reinterpret_cast<const char*>(a.k) + kv_row0 * kF8D;
+    const char* const vsrc = reinterpret_cast<const char*>(a.v) + kv_row0 * kF8D;
+    auto issue = [&](int t) {
+      const int k0 = kbase + t * kF8BN;
+      const unsigned nrows = (unsigned)max(kv_end - k0, 0);
+      char* st = smem + (t % kF8NS) * kF8Stage;
+      serial_fence();
+      lds_dma16_buf(raw_buffer_rsrc(ksrc + (size_t)k0 * kF8D, nrows * kF8D), koff, lds_addr(st + w * 1024));
+      lds_dma16_buf(raw_buffer_rsrc(vsrc + (size_t)k0 * kF8D, nrows * kF8D), voff, lds_addr(st + kF8Tile + w * 1024));
+      serial_fence();
+    };
 
-  // Software pipeline: iteration t issues the S products of tile t + 1 before the softmax of
-  // tile t, so a wave's own matrix-core work runs under its VALU work; then P V of tile t.
-  // Tile t + 1's K|V stage must have landed at iteration t, and the slot refilled there (of
-  // tile t + 3) was last read at iteration t - 1.
-  f32x16 sc[2], sn[2];
-  if (ntk > 0) {
-    if (kF8NS - 1 <= ntk) wait_vmcnt<(kF8NS - 2) * 2>();
-    else wait_vmcnt<0>();
+    if (ntk > 0) {
+      for (int i = tid; i < kF8NS * kF8Stage / 16; i += kF8NT) reinterpret_cast<u32x4*>(smem)[i] = u32x4{0u, 0u, 0u, 0u};
+      lds_barrier();  // the zero fill is done before any direct load lands
+    }
+#pragma unroll
+    for (int t = 0; t < kF8NS - 1; ++t)
+      if (t < ntk) issue(t);
+
+    // S^T of tile t (K from its slot) and its mask on boundary tiles (selects).
+    auto scores = [&](int t, f32x16 (&s)[2]) {
+      const char* kt = smem + (t % kF8NS) * kF8Stage;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < kF8KS; ++ks) {
+          const u32x4 lo = *reinterpret_cast<const u32x4*>(kt + kaddr[ks][0] + 32 * kb * kF8D);
+          const u32x4 hi = *reinterpret_cast<const u32x4*>(kt + kaddr[ks][1] + 32 * kb * kF8D);
+          const i32x8 ka = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+          s[kb] = mfma_f8(ka, qf[ks], s[kb]);
+        }
+      }
+    };
+    auto mask = [&](int t, f32x16 (&s)[2]) {
+      const int k0 = kbase + t * kF8BN;
+      const bool need_mask = (k0 + kF8BN > n_kv) || (a.causal && k0 + kF8BN - 1 > qw0 + delta) ||
+                             (a.window > 0 && k0 < qw0 + 32 + delta - a.window);
+      if (!need_mask) return;
+      // visible: lo <= (key - base) < lim, with base the lane's first key of the tile
+      const int base = k0 + 4 * half;
+      const int lim = min(n_kv - base, a.causal ? my_q + delta + 1 - base : n_kv - base);
+      const int lo = a.window > 0 ? my_q + delta - a.window + 1 - base : -kF8BN;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
+          s[kb][r] = (off >= lim || off < lo) ? kNegInf : s[kb][r];
+        }
+    };
+
+    // Software pipeline: iteration t issues the S products of tile t + 1 before the softmax of
+    // tile t, so a wave's own matrix-core work runs under its VALU work; then P V of tile t.
+    // Tile t + 1's K|V stage must have landed at iteration t, and the slot refilled there (of
+    // tile t + 3) was last read at iteration t - 1.
+    f32x16 sc[2], sn[2];
+    if (ntk > 0) {
+      if (kF8NS - 1 <= ntk) wait_vmcnt<(kF8NS - 2) * 2>();
+      else wait_vmcnt<0>();
+      lds_barrier();
+      scores(0, sc);
+      mask(0, sc);
+    }
+    // One tile: its softmax and P V from `cur`, the next tile's scores into `nxt`. The loop
+    // runs two tiles per trip with the buffers swapped, so no scores are copied.
+    auto tile = [&](int t, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+      const bool more = t + 1 < ntk;   // another tile for the workgroup
+      const bool mine = t + 1 < ntw;   // and this wave has keys in it
+      if (more) {
+        if (t + 2 < ntk) wait_vmcnt<2>();  // stage t + 2 may stay in flight
+        else wait_vmcnt<0>();
+        lds_barrier();
+        if (t + kF8NS - 1 < ntk) issue(t + kF8NS - 1);
+        if (mine) scores(t + 1, nxt);
+      }
+      const char* vt = smem + (t % kF8NS) * kF8Stage + kF8Tile;
+
+      // Integer reference: raised to ceil(tile max) when the tile passes it.
+      float mx = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, cur[kb][r]);
+      mx = max_of_halves(mx) * c;
+      const float m_new = mx > m ? ceilf(mx) : m;
+      // 0 when there was no reference, 1 when unchanged, else an exact power of two
+      const float alpha = m == kNegInf ? 0.f : __builtin_amdgcn_ldexpf(1.f, (int)(m - m_new));
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
+        l *= alpha;
+#pragma unroll
+        for (int nb = 0; nb < kF8NB; ++nb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[nb][r] *= alpha;
+      }
+      m = m_new;
+      // x = 2^(t - m + 8) <= 256; a row with no reference yet has only masked scores here.
+      const float off = m == kNegInf ? 0.f : 8.f - m;
+      int pk[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        // bytes 4 i .. 4 i + 3 = elements (kb, r) with 16 kb + r = 4 i .. 4 i + 3
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int T = 4 * i + e;
+          x[e] = exp2_hw(fmaf(cur[T >> 4][T & 15], c, off));
+          l += x[e];
+        }
+        int word = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+        word = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], word, true);
+        pk[i] = word;
+      }
+      const i32x8 pb = {pk[0], pk[1], pk[2], pk[3], pk[4], pk[5], pk[6], pk[7]};
+      // O^T += V^T P^T.
+#pragma unroll
+      for (int nb = 0; nb < kF8NB; ++nb) {
+        const i32x2 r0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vt + vaddr[0][nb]));
+        const i32x2 r1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vt + vaddr[1][nb]));
+        const i32x2 r2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vt + vaddr[0][nb] + 32 * kF8D));
+        const i32x2 r3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vt + vaddr[1][nb] + 32 * kF8D));
+        const i32x8 va = {r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
+        oacc[nb] = mfma_f8(va, pb, oacc[nb]);
+      }
+      if (mine) mask(t + 1, nxt);
+    };
+    int t = 0;
+    while (t < ntw) {
+      tile(t, sc, sn);
+      if (++t >= ntw) break;
+      tile(t, sn, sc);
+      ++t;
+    }
+    for (; t < ntk; ++t) {  // tiles past this wave's rows: loads and barriers only
+      if (t + 1 < ntk) {
+        if (t + 2 < ntk) wait_vmcnt<2>();
+        else wait_vmcnt<0>();
+        lds_barrier();
+        if (t + kF8NS - 1 < ntk) issue(t + kF8NS - 1);
+      }
+    }
+    if (ntk > 0) wait_vmcnt<0>();
+
+    // Epilogue: O = descale_v * o / l, LSE = ln(2) (m - 8 + log2 l); rows that saw nothing
+    // (and padding rows) get O = 0 and LSE = -inf. O leaves through LDS as whole rows (as in
+    // the bf16 prefill): every wave has waited for its loads, so LDS is free once all have
+    // returned their last reads.
     lds_barrier();
-    scores(0, sc);
-    mask(0, sc);
-  }
-  // One tile: its softmax and P V from `cur`, the next tile's scores into `nxt`. The loop
-  // runs two tiles per trip with the buffers swapped, so no scores are copied.
-  auto tile = [&](int t, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
-    const bool more = t + 1 < ntk;   // another tile for the workgroup
-    const bool mine = t + 1 < ntw;   // and this wave has keys in it
-    if (more) {
-      if (t + 2 < ntk) wait_vmcnt<2>();  // stage t + 2 may stay in flight
-      else wait_vmcnt<0>();
-      lds_barrier();
-      if (t + kF8NS - 1 < ntk) issue(t + kF8NS - 1);
-      if (mine) scores(t + 1, nxt);
-    }
-    const char* vt = smem + (t % kF8NS) * kF8Stage + kF8Tile;
-
-    // Integer reference: raised to ceil(tile max) when the tile passes it.
-    float mx = kNegInf;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, cur[kb][r]);
-    mx = max_of_halves(mx) * c;
-    const float m_new = mx > m ? ceilf(mx) : m;
-    // 0 when there was no reference, 1 when unchanged, else an exact power of two
-    const float alpha = m == kNegInf ? 0.f : __builtin_amdgcn_ldexpf(1.f, (int)(m - m_new));
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
-      l *= alpha;
-#pragma unroll
-      for (int nb = 0; nb < kF8NB; ++nb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[nb][r] *= alpha;
-    }
-    m = m_new;
-    // x = 2^(t - m + 8) <= 256; a row with no reference yet has only masked scores here.
-    const float off = m == kNegInf ? 0.f : 8.f - m;
-    int pk[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      // bytes 4 i .. 4 i + 3 = elements (kb, r) with 16 kb + r = 4 i .. 4 i + 3
-      float x[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int T = 4 * i + e;
-        x[e] = exp2_hw(fmaf(cur[T >> 4][T & 15], c, off));
-        l += x[e];
-      }
-      int word = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
-      word = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], word, true);
-      pk[i] = word;
-    }
-    const i32x8 pb = {pk[0], pk[1], pk[2], pk[3], pk[4], pk[5], pk[6], pk[7]};
-    // O^T += V^T P^T.
-#pragma unroll
-    for (int nb = 0; nb < kF8NB; ++nb) {
-      const i32x2 r0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vt + vaddr[0][nb]));
-      const i32x2 r1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vt + vaddr[1][nb]));
-      const i32x2 r2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vt + vaddr[0][nb] + 32 * kF8D));
-      const i32x2 r3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vt + vaddr[1][nb] + 32 * kF8D));
-      const i32x8 va = {r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
-      oacc[nb] = mfma_f8(va, pb, oacc[nb]);
-    }
-    if (mine) mask(t + 1, nxt);
-  };
-  int t = 0;
-  while (t < ntw) {
-    tile(t, sc, sn);
-    if (++t >= ntw) break;
-    tile(t, sn, sc);
-    ++t;
-  }
-  for (; t < ntk; ++t) {  // tiles past this wave's rows: loads and barriers only
-    if (t + 1 < ntk) {
-      if (t + 2 < ntk) wait_vmcnt<2>();
-      else wait_vmcnt<0>();
-      lds_barrier();
-      if (t + kF8NS - 1 < ntk) issue(t + kF8NS - 1);
-    }
-  }
-  if (ntk > 0) wait_vmcnt<0>();
-
-  // Epilogue: O = descale_v * o / l, LSE = ln(2) (m - 8 + log2 l); rows that saw nothing
-  // (and padding rows) get O = 0 and LSE = -inf.
-  unsigned lo_bits, hi_bits;
-  wave_halves(__builtin_bit_cast(unsigned, l), lo_bits, hi_bits);
-  const float lt = __builtin_bit_cast(float, lo_bits) + __builtin_bit_cast(float, hi_bits);
-  const bool row_ok = my_q < n_q && lt > 0.f;
-  const float inv = row_ok ? dv / lt : 0.f;
-  if (my_q < a.Lq) {
-    __bf16* op = a.o + ((size_t)(b * a.H + h) * a.Lq + my_q) * kF8D;
+    unsigned lo_bits, hi_bits;
+    wave_halves(__builtin_bit_cast(unsigned, l), lo_bits, hi_bits);
+    const float lt = __builtin_bit_cast(float, lo_bits) + __builtin_bit_cast(float, hi_bits);
+    const bool row_ok = my_q < n_q && lt > 0.f;
+    const float inv = row_ok ? dv / lt : 0.f;
+    char* const stage_o = smem + w * 32 * kF8RS;
 #pragma unroll
     for (int nb = 0; nb < kF8NB; ++nb)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int d0 = 32 * nb + 8 * jj + 4 * half;
-        Store4<__bf16>::store(op + d0, oacc[nb][4 * jj] * inv, oacc[nb][4 * jj + 1] * inv,
-                              oacc[nb][4 * jj + 2] * inv, oacc[nb][4 * jj + 3] * inv);
+        Store4<__bf16>::store(reinterpret_cast<__bf16*>(stage_o + col * kF8RS) + d0, oacc[nb][4 * jj] * inv,
+                              oacc[nb][4 * jj + 1] * inv, oacc[nb][4 * jj + 2] * inv, oacc[nb][4 * jj + 3] * inv);
       }
-    if (half == 0) a.lse[(size_t)(b * a.H + h) * a.Lq + my_q] = row_ok ? (m - 8.f + __log2f(lt)) * kLn2 : kNegInf;
+    __bf16* const ob = a.o + (size_t)(b * a.H + h) * a.Lq * kF8D;
+#pragma unroll
+    for (int i = 0; i < 32 * (kF8D / 8) / 64; ++i) {
+      const int idx = 64 * i + lane, r = idx / (kF8D / 8), c16 = idx - r * (kF8D / 8);
+      const u32x4 val = *reinterpret_cast<const u32x4*>(stage_o + r * kF8RS + 16 * c16);
+      if (qw0 + r < a.Lq) *reinterpret_cast<u32x4*>(ob + (size_t)(qw0 + r) * kF8D + 8 * c16) = val;
+    }
+    if (my_q < a.Lq && half == 0)
+      a.lse[(size_t)(b * a.H + h) * a.Lq + my_q] = row_ok ? (m - 8.f + __log2f(lt)) * kLn2 : kNegInf;
+    // The next tile clears and refills LDS: every wave's staged-O reads must have returned.
+    lds_barrier();
   }
 #endif
 }
@@ -360,9 +383,12 @@ hipError_t launch_fwd_fp8(const Fp8FwdParams& p, hipStream_t stream) {
   const long long nwg = (long long)a.ntq * p.B * p.H;
   if (nwg > 0x7fffffffLL || (long long)p.Lk * kF8D > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   a.nwg = (int)nwg;
+  // Dense inputs on a persistent grid, variable lengths one workgroup per tile (as for bf16).
+  const int P = p.seqlens == nullptr ? persistent_programs() : 0;
+  a.nprog = (P > 0 && a.nwg > P) ? P : a.nwg;
   void* args[] = {&a};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_fp8_kernel), dim3((unsigned)nwg), dim3(kF8NT), args, 0,
-                         stream);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_fp8_kernel), dim3((unsigned)a.nprog), dim3(kF8NT), args,
+                         0, stream);
 }
 
 }  // namespace fa

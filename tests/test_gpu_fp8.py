@@ -72,6 +72,12 @@ def test_fp8_unequal_lengths(Lq, Lk):
     run_fp8(1, 2, 1, Lq, Lk, causal=True, seed=610 + Lq)
 
 
+def test_fp8_more_tiles_than_compute_units():
+    # 261 query tiles (more than the GPU's compute units): several tiles per workgroup, the
+    # last round nearly empty; 29 heads, not a multiple of the 8 XCDs.
+    run_fp8(3, 29, 29, 768, 768, causal=True, seed=630)
+
+
 def test_fp8_varlen():
     run_fp8(3, 4, 2, 700, 700, causal=True, seed=620, len_range=(1, 700))
 
