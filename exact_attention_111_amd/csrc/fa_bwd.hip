@@ -167,6 +167,32 @@ struct TileAddr {
   }
 };
 
+// A wave's 32 x D result block, held in the accumulator layout (lane (col, half): row col,
+// dims 32 nb + 8 m + 4 half + (0..3) in acc[nb][4 m .. 4 m + 3]), times `mul`, stored as
+// whole rows: it goes through this wave's LDS region `stage` (32 rows of 2 D + 16 bytes, the
+// pad spreading the rows over the banks) and out 16 contiguous bytes per lane, rows below
+// `nrows` only. Stored straight from the accumulators, each store instruction would write 8
+// bytes into each of 32 rows. LDS must be free; the same region may be used again at once.
+template <int D>
+__device__ __forceinline__ void store_block_rows(char* stage, const f32x16 (&acc)[D / 32], float mul, __bf16* out,
+                                                 int nrows, int lane) {
+  constexpr int RS = 2 * D + 16, CPR = D / 8;
+  const int col = lane & 31, half = lane >> 5;
+#pragma unroll
+  for (int nb = 0; nb < D / 32; ++nb)
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      Store4<__bf16>::store(reinterpret_cast<__bf16*>(stage + col * RS) + 32 * nb + 8 * m + 4 * half,
+                            acc[nb][4 * m] * mul, acc[nb][4 * m + 1] * mul, acc[nb][4 * m + 2] * mul,
+                            acc[nb][4 * m + 3] * mul);
+#pragma unroll
+  for (int i = 0; i < 32 * CPR / 64; ++i) {
+    const int idx = 64 * i + lane, r = idx / CPR, c = idx - r * CPR;
+    const u32x4 val = *reinterpret_cast<const u32x4*>(stage + r * RS + 16 * c);
+    if (r < nrows) *reinterpret_cast<u32x4*>(out + (size_t)r * D + 8 * c) = val;
+  }
+}
+
 // ---------------------------------------------------------------------------------------
 // Per query row: exp2 offset LSE * log2(e) (+inf for a row that sees nothing, so P = 0)
 // and D = sum_c dO_ic O_ic; (+inf, 0) on padding rows.
@@ -379,19 +405,15 @@ void bwd_dkdv_kernel(const BwdArgs a) {
   }
 
   // dK = scale * dK^T-accumulator, dV: lane holds key my_key, dims 32 nb + 8 (r / 4) +
-  // 4 half + r % 4.
-  if (my_key < a.Lk) {
-    __bf16* dkp = a.dk + kv_off + (size_t)my_key * D;
-    __bf16* dvp = a.dv + kv_off + (size_t)my_key * D;
-#pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int d0 = 32 * nb + 8 * m + 4 * half;
-        Store4<__bf16>::store(dkp + d0, dka[nb][4 * m] * a.scale, dka[nb][4 * m + 1] * a.scale,
-                              dka[nb][4 * m + 2] * a.scale, dka[nb][4 * m + 3] * a.scale);
-        Store4<__bf16>::store(dvp + d0, dva[nb][4 * m], dva[nb][4 * m + 1], dva[nb][4 * m + 2], dva[nb][4 * m + 3]);
-      }
+  // 4 half + r % 4. Every wave's loads landed at its last step; once all have done their
+  // last reads, LDS holds the blocks on their way out.
+  static_assert(C::NW * 32 * (2 * D + 16) <= (int)sizeof(smem), "staged blocks fit in LDS");
+  lds_barrier();
+  {
+    char* const stage = smem + w * 32 * (2 * D + 16);
+    const int nrows = min(a.Lk - kw0, 32);
+    store_block_rows<D>(stage, dka, a.scale, a.dk + kv_off + (size_t)kw0 * D, nrows, lane);
+    store_block_rows<D>(stage, dva, 1.f, a.dv + kv_off + (size_t)kw0 * D, nrows, lane);
   }
 #endif
 }
@@ -574,22 +596,13 @@ void bwd_dq_kernel(const BwdArgs a) {
   }
 
   // dQ = scale * accumulator: lane holds query qw0 + 32 qb + col, dims 32 nb + 8 jj +
-  // 4 half + (0..3).
+  // 4 half + (0..3); out through LDS as whole rows once every wave has done its last reads.
+  static_assert(C::NW * 32 * (2 * D + 16) <= (int)sizeof(smem), "staged blocks fit in LDS");
+  lds_barrier();
 #pragma unroll
-  for (int qb = 0; qb < C::QB; ++qb) {
-    const int my_q = qw0 + 32 * qb + col;
-    if (my_q < a.Lq) {
-      __bf16* dqp = a.dq + (q_off + my_q) * D;
-#pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int d0 = 32 * nb + 8 * jj + 4 * half;
-          Store4<__bf16>::store(dqp + d0, dqa[qb][nb][4 * jj] * a.scale, dqa[qb][nb][4 * jj + 1] * a.scale,
-                                dqa[qb][nb][4 * jj + 2] * a.scale, dqa[qb][nb][4 * jj + 3] * a.scale);
-        }
-    }
-  }
+  for (int qb = 0; qb < C::QB; ++qb)
+    store_block_rows<D>(smem + w * 32 * (2 * D + 16), dqa[qb], a.scale, a.dq + (q_off + qw0 + 32 * qb) * D,
+                        min(a.Lq - qw0 - 32 * qb, 32), lane);
 #endif
 }
 

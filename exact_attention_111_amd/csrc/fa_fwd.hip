@@ -45,7 +45,7 @@
 //   * Heads are dealt round-robin to the 8 XCDs (dispatch is round-robin over them), and
 //     each XCD works through its heads one at a time, heaviest query tile first, so that its
 //     CUs share that head's K/V in the XCD's L2.
-#include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "fa_device.h"
@@ -744,28 +744,37 @@ hipError_t launch(const FwdParams& p, hipStream_t stream) {
   // compute unit that finishes early idles until its engine's turn comes round. Variable lengths
   // keep one workgroup per tile: their tiles' work is only known on the device, and the
   // hardware's dynamic dispatch balances it.
-  const int P = p.seqlens == nullptr && sizeof(IT) == 2 ? persistent_programs() : 0;
+  const void* fn = reinterpret_cast<const void*>(&fwd_kernel<D, IT, OT, WIN>);
+  const int P = p.seqlens == nullptr && sizeof(IT) == 2 ? persistent_programs(fn, C::NT) : 0;
   a.nprog = (P > 0 && a.nwg > P) ? P : a.nwg;
   void* args[] = {&a};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_kernel<D, IT, OT, WIN>), dim3((unsigned)a.nprog),
-                         dim3(C::NT), args, 0, stream);
+  return hipLaunchKernel(fn, dim3((unsigned)a.nprog), dim3(C::NT), args, 0, stream);
 }
 
 }  // namespace
 
-int persistent_programs() {
-  constexpr int kMaxDevices = 64;
-  static std::atomic<int> cached[kMaxDevices];  // 0: not looked up yet, else programs + 1
+int persistent_programs(const void* kernel, int block_threads) {
+  struct Entry {
+    int dev;
+    const void* kernel;
+    int programs;
+  };
+  constexpr int kMaxEntries = 64;
+  static std::mutex mu;
+  static Entry cache[kMaxEntries];
+  static int used = 0;
   int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
-  int c = cached[dev].load(std::memory_order_relaxed);
-  if (c == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
-    c = (n >= 8 ? n - n % 8 : 0) + 1;
-    cached[dev].store(c, std::memory_order_relaxed);
-  }
-  return c - 1;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  for (int i = 0; i < used; ++i)
+    if (cache[i].dev == dev && cache[i].kernel == kernel) return cache[i].programs;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block_threads, 0) != hipSuccess) per_cu = 0;
+  const int n = cus * per_cu;
+  const int programs = n >= 8 ? n - n % 8 : 0;
+  if (used < kMaxEntries) cache[used++] = Entry{dev, kernel, programs};
+  return programs;
 }
 
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream) {

@@ -384,7 +384,7 @@ hipError_t launch_fwd_fp8(const Fp8FwdParams& p, hipStream_t stream) {
   if (nwg > 0x7fffffffLL || (long long)p.Lk * kF8D > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   a.nwg = (int)nwg;
   // Dense inputs on a persistent grid, variable lengths one workgroup per tile (as for bf16).
-  const int P = p.seqlens == nullptr ? persistent_programs() : 0;
+  const int P = p.seqlens == nullptr ? persistent_programs(reinterpret_cast<const void*>(&fwd_fp8_kernel), kF8NT) : 0;
   a.nprog = (P > 0 && a.nwg > P) ? P : a.nwg;
   void* args[] = {&a};
   return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_fp8_kernel), dim3((unsigned)a.nprog), dim3(kF8NT), args,

@@ -22,10 +22,11 @@ struct FwdParams {
 };
 hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t stream);
 
-// Workgroups of a persistent prefill grid on the current device: its compute units rounded
+// Workgroups of a persistent grid of `kernel` (blocks of block_threads) on the current
+// device: as many as can be resident at once (compute units x workgroups per unit), rounded
 // down to a multiple of 8 (the XCDs workgroups are dealt to in turn), or 0 (no persistent
-// grid) when that is not known or under 8. Looked up once per device.
-int persistent_programs();
+// grid) when that is not known or under 8. Looked up once per device and kernel.
+int persistent_programs(const void* kernel, int block_threads);
 
 // FP8 prefill (d = 128): E4M3 q, k, v with per-(batch, head) fp32 descales, bf16 o.
 struct Fp8FwdParams {
