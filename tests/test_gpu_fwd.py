@@ -267,6 +267,8 @@ def test_empty_and_degenerate_calls():
     (2, 24, 24, 2500, 128, False, None),  # 480 tiles: the second round is only partly filled
     (2, 32, 8, 2300, 128, True, None),    # GQA, 576 tiles
     (2, 16, 16, 3000, 64, True, 700),     # sliding window, 384 tiles
+    (1, 257, 257, 256, 64, False, None),  # one tile more than 256 compute units: one in its last round
+    (1, 264, 264, 200, 128, True, None),  # 256 + 8 tiles: one per XCD in the last round, ragged rows
 ])
 def test_more_tiles_than_compute_units(B, H, Hkv, L, d, causal, window):
     """Dense inputs with more 256-row query tiles than the GPU has compute units run several
