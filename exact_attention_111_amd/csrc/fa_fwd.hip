@@ -8,8 +8,8 @@
 // o are multiplied by exp(m_old - m_new). At the end O = o / l and the row's log-sum-exp
 // is written. Score and probability tiles never leave the compute unit.
 //
-// gfx950 mapping. One workgroup = one 256-row query tile of one head: 8 wave64s of 32 query
-// rows, two waves per SIMD, so a wave fits in 256 VGPRs (d = 64 and 128).
+// gfx950 mapping. A workgroup computes 256-row query tiles of one head at a time: 8 wave64s of
+// 32 query rows, two waves per SIMD, so a wave fits in 256 VGPRs (d = 64 and 128).
 //   * One body per 64-key tile j, one workgroup barrier each, in two regions: (X) the MFMAs
 //     of S for tile j + 1 beside exp / row sum / bf16 conversion of most of tile j, then
 //     (Y) the MFMAs of P V for tile j beside the rest of tile j's exps and the scale-and-
@@ -44,7 +44,10 @@
 //     SIMD is left the same work there.
 //   * Heads are dealt round-robin to the 8 XCDs (dispatch is round-robin over them), and
 //     each XCD works through its heads one at a time, heaviest query tile first, so that its
-//     CUs share that head's K/V in the XCD's L2.
+//     CUs share that head's K/V in the XCD's L2. Dense inputs run on a persistent grid (one
+//     workgroup per CU taking its XCD's tiles in rounds); with per-sequence lengths each tile
+//     is a workgroup of its own and the hardware hands them out.
+//   * O leaves through LDS as whole rows (16 contiguous bytes per lane).
 #include <mutex>
 #include <type_traits>
 
@@ -628,8 +631,9 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
     };
 
     if (ntk > 0) {
-      // Zero the buffers once, so that operand reads of a slot never written (dummy work at
-      // the end of the pipeline) see finite values.
+      // Zero the buffers at the start of every tile, so that operand reads of a slot or rows
+      // not written for this tile (dummy work at the end of the pipeline, rows past kv_end)
+      // see finite values.
       for (int i = tid; i < (int)sizeof(smem) / 16; i += C::NT) *reinterpret_cast<u32x4*>(smem + 16 * i) = u32x4{0u, 0u, 0u, 0u};
       // Only the LDS writes must be done before the loads land: a full __syncthreads() would
       // also wait for this wave's Q loads and put their latency before the K/V loads' own.

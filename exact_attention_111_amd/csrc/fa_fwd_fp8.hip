@@ -14,7 +14,8 @@
 // tiling: it is the whole-row definition with the final reference.
 //
 // gfx950 mapping (v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales for both products):
-//   * Workgroup: 256 query rows of one (batch, head), 8 waves of 32 rows, two per SIMD. Each
+//   * Workgroup: 256 query rows of one (batch, head) at a time (dense inputs: a persistent grid
+//     taking tiles in rounds, as the bf16 prefill), 8 waves of 32 rows, two per SIMD. Each
 //     wave keeps its Q rows as B operands: lane (half, col) holds dims 64 ks + 32 half ..
 //     + 31 of query row col (the operands' byte t of half h pair up in the product). On the
 //     causal diagonal a wave stops computing after the last tile its rows can see; the two
