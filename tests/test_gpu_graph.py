@@ -122,3 +122,55 @@ def test_all_entry_points_replay_in_a_graph():
             assert torch.equal(gbuf[name], ebuf[name]), f"replay {rep}: {name} differs from the eager call"
         assert torch.isfinite(gbuf["o1"].float()).all() and torch.isfinite(gbuf["dq"].float()).all()
     graph.reset()
+
+
+def test_persistent_grid_prefill_replays_in_a_graph():
+    """Dense prefills with more query tiles than compute units (288: the persistent grid, tiles
+    taken in rounds), bf16 and FP8, recorded into a graph and replayed on refilled inputs: each
+    replay equals the eager calls bit for bit."""
+    announce(entry="fa_fwd + fa_fwd_fp8 (graph capture, persistent grid)", B=1, H=48, L=1536, seed=950)
+    fa = _fa()
+    sc = 1.0 / math.sqrt(128)
+
+    def inputs(seed):
+        return {"pre": fa_inputs.prefill_inputs(1, 48, 48, 1536, 1536, 128, seed=seed, device=DEV),
+                "fp8": fa_inputs.fp8_prefill_inputs(1, 48, 48, 1536, 1536, 128, seed=seed + 1, device=DEV)}
+
+    def buffers(inp):
+        q = inp["pre"]["q"]
+        return {"o": torch.empty_like(q), "l": torch.empty(q.shape[:3], dtype=torch.float32, device=DEV),
+                "o8": torch.empty(q.shape, dtype=torch.bfloat16, device=DEV),
+                "l8": torch.empty(q.shape[:3], dtype=torch.float32, device=DEV)}
+
+    def calls(inp, buf):
+        x, x8 = inp["pre"], inp["fp8"]
+        fa.fwd(x["q"], x["k"], x["v"], causal=True, scale=sc, out=buf["o"], lse=buf["l"])
+        fa.fwd_fp8(x8["q"], x8["k"], x8["v"], x8["q_descale"], x8["k_descale"], x8["v_descale"], causal=True,
+                   scale=sc, out=buf["o8"], lse=buf["l8"])
+
+    static = inputs(950)
+    gbuf, ebuf = buffers(static), buffers(static)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls(static, gbuf)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls(static, gbuf)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        announce(replay=rep, seed=951 + rep)
+        _refill(static, inputs(951 + 2 * rep))
+        for name in gbuf:
+            gbuf[name].zero_()
+            ebuf[name].zero_()
+        calls(static, ebuf)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name in gbuf:
+            assert torch.equal(gbuf[name], ebuf[name]), f"replay {rep}: {name} differs from the eager call"
+        assert torch.isfinite(gbuf["o"].float()).all() and torch.isfinite(gbuf["o8"].float()).all()
+    graph.reset()
