@@ -32,8 +32,10 @@ __device__ __forceinline__ int kv_xor(int r) {
   return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 
-// Query tile and (batch, head) of prefill workgroup `hw` (ntq query tiles per head, nwg
-// workgroups), heaviest tile first. Hardware id i runs on XCD i % 8 as that XCD's slot i / 8.
+// Query tile and (batch, head) of prefill tile id `hw` (ntq query tiles per head, nwg tiles),
+// heaviest tile first. Tile id i is meant for XCD i % 8 as that XCD's slot i / 8: it is the
+// hardware workgroup id when every tile is a workgroup (hardware id i runs on XCD i % 8), and
+// tile_of_program keeps a persistent workgroup on the XCD its tile ids belong to.
 // When the (batch, head) count is a multiple of 8, head bh belongs to XCD bh % 8, so every
 // XCD gets the same mix of sequences (equal work even when lengths vary) and its L2 serves
 // the K/V of its own heads only. An XCD goes through its heads in groups of just enough
