@@ -333,6 +333,11 @@ void bwd_dkdv_kernel(const BwdArgs a) {
 #pragma unroll
   for (int t = 0; t < C::KV_NS - 1; ++t)
     if (t < T) issue(t);
+  // Wait for every load once here, on every path into the step loop. The K and V rows were
+  // loaded into registers above; the compiler does not see the ring's direct loads, so unless
+  // it sees a complete wait after those register loads it waits for all loads before their
+  // first use in every step, the ring stages just issued for later steps included.
+  wait_vmcnt<0>();
 
   int qs = qs_first;  // block of the step being computed
   for (int t = 0; t < T; ++t) {
@@ -532,6 +537,9 @@ void bwd_dq_kernel(const BwdArgs a) {
 #pragma unroll
   for (int t = 0; t < C::Q_NS - 1; ++t)
     if (t < T) issue(t);
+  // One complete wait on every path into the step loop, for the reason given in bwd_dkdv
+  // (here the Q and dO rows were loaded into registers above).
+  wait_vmcnt<0>();
 
   for (int t = 0; t < T; ++t) {
     if (t + C::Q_NS - 1 <= T) wait_vmcnt<(C::Q_NS - 2) * C::Q_LOADS>();

@@ -139,18 +139,8 @@ __global__ __launch_bounds__(kF8NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     const float c = a.scale_log2 * a.q_descale[b * a.H + h] * a.k_descale[b * a.Hkv + kvh];
     const float dv = a.v_descale[b * a.Hkv + kvh];
 
-    // Q rows as B operands.
+    // Q rows as B operands (read from LDS in the prologue below).
     i32x8 qf[kF8KS];
-    const unsigned char* qrow = a.q + ((size_t)(b * a.H + h) * a.Lq + my_q) * kF8D;
-#pragma unroll
-    for (int ks = 0; ks < kF8KS; ++ks) {
-      u32x4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
-      if (my_q < n_q && ntk > 0) {
-        lo = *reinterpret_cast<const u32x4*>(qrow + 64 * ks + 32 * half);
-        hi = *reinterpret_cast<const u32x4*>(qrow + 64 * ks + 32 * half + 16);
-      }
-      qf[ks] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-    }
 
     f32x16 oacc[kF8NB];
 #pragma unroll
@@ -196,13 +186,50 @@ __global__ __launch_bounds__(kF8NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
       serial_fence();
     };
 
+    // The tile's Q rows come through LDS as well, into stages 2 and 3 (refilled only after
+    // every wave has read its rows): row r at byte 128 r, 16-byte chunk c at c ^ (r & 7), so
+    // that the 16 rows of a 128-bit read hit distinct banks. With no Q row loaded directly into
+    // registers, the compiler tracks no load on the tile path; otherwise it cannot tell, past
+    // the direct loads it does not see, that the Q loads are done, and waits for every load
+    // before the first score product of each tile (the stage just issued included).
+    constexpr int kQBase = 2 * kF8Stage;
+    static_assert(kF8BM * kF8D <= (kF8NS - 2) * kF8Stage, "the Q tile fits in stages 2 and 3");
+    auto issue_q = [&] {
+      const u32x4 rq = raw_buffer_rsrc(a.q + ((size_t)(b * a.H + h) * a.Lq + q0) * kF8D,
+                                       (unsigned)max(min(n_q, a.Lq) - q0, 0) * kF8D);
+      serial_fence();
+#pragma unroll
+      for (int i = 0; i < kF8BM * kF8D / 1024 / kF8NW; ++i) {  // wave w: rows 32 w .. 32 w + 31
+        const int seg = (kF8BM * kF8D / 1024 / kF8NW) * w + i;
+        const int row = 8 * seg + (lane >> 3), pch = lane & 7;
+        lds_dma16_buf(rq, (unsigned)(row * kF8D + ((pch ^ (row & 7)) << 4)), lds_addr(smem + kQBase + seg * 1024));
+      }
+      serial_fence();
+    };
+
     if (ntk > 0) {
       for (int i = tid; i < kF8NS * kF8Stage / 16; i += kF8NT) reinterpret_cast<u32x4*>(smem)[i] = u32x4{0u, 0u, 0u, 0u};
       lds_barrier();  // the zero fill is done before any direct load lands
-    }
+      issue_q();
+      issue(0);
+      wait_vmcnt<0>();
+      lds_barrier();  // everyone's Q rows and stage 0 have landed
+      const int rr = qw0 - q0 + col;  // this lane's row of the tile (rows past n_q are zero)
 #pragma unroll
-    for (int t = 0; t < kF8NS - 1; ++t)
-      if (t < ntk) issue(t);
+      for (int ks = 0; ks < kF8KS; ++ks) {
+        const char* qr = smem + kQBase + rr * kF8D;
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(qr + (((4 * ks + 2 * half) ^ (rr & 7)) << 4));
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(qr + (((4 * ks + 2 * half + 1) ^ (rr & 7)) << 4));
+        qf[ks] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      }
+      lds_barrier();  // every wave holds its Q rows before stages 2 and 3 are refilled
+#pragma unroll
+      for (int t = 1; t < kF8NS - 1; ++t)
+        if (t < ntk) issue(t);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < kF8KS; ++ks) qf[ks] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
 
     // S^T of tile t (K from its slot) and its mask on boundary tiles (selects).
     auto scores = [&](int t, f32x16 (&s)[2]) {
@@ -243,9 +270,6 @@ __global__ __launch_bounds__(kF8NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     // tile t + 3) was last read at iteration t - 1.
     f32x16 sc[2], sn[2];
     if (ntk > 0) {
-      if (kF8NS - 1 <= ntk) wait_vmcnt<(kF8NS - 2) * 2>();
-      else wait_vmcnt<0>();
-      lds_barrier();
       scores(0, sc);
       mask(0, sc);
     }
