@@ -234,17 +234,27 @@ __global__ __launch_bounds__(kF8NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     // S^T of tile t (K from its slot) and its mask on boundary tiles (selects).
     auto scores = [&](int t, f32x16 (&s)[2]) {
       const char* kt = smem + (t % kF8NS) * kF8Stage;
+      // K operand f = (key block f / KS, k-step f % KS); operand f + 1 is read before the
+      // product of operand f, so each product waits for one LDS round trip less.
+      auto read_k = [&](int f) {
+        const int kb = f / kF8KS, ks = f % kF8KS;
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(kt + kaddr[ks][0] + 32 * kb * kF8D);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(kt + kaddr[ks][1] + 32 * kb * kF8D);
+        return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      };
+      // (A scheduling fence per step keeps that order; left alone, the scheduler moves each
+      // read behind the previous product.)
+      i32x8 buf[2];
+      buf[0] = read_k(0);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < kF8KS; ++ks) {
-          const u32x4 lo = *reinterpret_cast<const u32x4*>(kt + kaddr[ks][0] + 32 * kb * kF8D);
-          const u32x4 hi = *reinterpret_cast<const u32x4*>(kt + kaddr[ks][1] + 32 * kb * kF8D);
-          const i32x8 ka = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-          s[kb] = mfma_f8(ka, qf[ks], s[kb]);
-        }
+      for (int f = 0; f < 2 * kF8KS; ++f) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (f + 1 < 2 * kF8KS) buf[(f + 1) & 1] = read_k(f + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        const int kb = f / kF8KS, ks = f % kF8KS;
+        s[kb] = mfma_f8(buf[f & 1], qf[ks], ks == 0 ? f32x16{} : s[kb]);
       }
+      __builtin_amdgcn_sched_barrier(0);
     };
     auto mask = [&](int t, f32x16 (&s)[2]) {
       const int k0 = kbase + t * kF8BN;
