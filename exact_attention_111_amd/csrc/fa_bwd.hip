@@ -555,19 +555,34 @@ void bwd_dq_kernel(const BwdArgs a) {
 
     // S^T and dP^T of both row blocks: element r is key k0 + 8 (r / 4) + 4 half + r % 4,
     // query qw0 + 32 qb + col.
+    // Operand f of these products is the K (f even) or V (f odd) row chunk of k-step f / 2,
+    // read kRowPF operands ahead; the operands of the dQ products after them are read kTrPF
+    // ahead, the first ones before the softmax work. Scheduling fences keep each read ahead of
+    // the product it precedes: left alone, the scheduler puts every read right before its
+    // product and each product waits for a whole LDS round trip.
+    constexpr int kRowPF = 4, kTrPF = 3;
+    constexpr int NF = 2 * C::QKS, NT = 2 * C::NB;
+    auto read_rowop = [&](int f) { return (f & 1) ? ta.read_row(vt, 0, f >> 1) : ta.read_row(kt, 0, f >> 1); };
+    auto read_trop = [&](int f) { return ta.read_tr(kt, f / C::NB, f % C::NB, hi); };
     f32x16 sx[C::QB], dpx[C::QB];
+    bf16x8 rbuf[kRowPF], tbuf[kTrPF];
 #pragma unroll
-    for (int qb = 0; qb < C::QB; ++qb) sx[qb] = dpx[qb] = f32x16{};
+    for (int f = 0; f < kRowPF; ++f) rbuf[f] = read_rowop(f);
 #pragma unroll
-    for (int ks = 0; ks < C::QKS; ++ks) {
-      const bf16x8 ka = ta.read_row(kt, 0, ks);
-      const bf16x8 va = ta.read_row(vt, 0, ks);
+    for (int f = 0; f < NF; ++f) {
+      __builtin_amdgcn_sched_barrier(0);
+      const bf16x8 x = rbuf[f % kRowPF];
+      if (f + kRowPF < NF) rbuf[f % kRowPF] = read_rowop(f + kRowPF);
+      else if (f + kRowPF - NF < kTrPF) tbuf[f + kRowPF - NF] = read_trop(f + kRowPF - NF);
+      __builtin_amdgcn_sched_barrier(0);
+      const int ks = f >> 1;
 #pragma unroll
       for (int qb = 0; qb < C::QB; ++qb) {
-        sx[qb] = mfma_32x32x16(ka, qf[qb][ks], sx[qb]);
-        dpx[qb] = mfma_32x32x16(va, dof[qb][ks], dpx[qb]);
+        if (f & 1) dpx[qb] = mfma_32x32x16(x, dof[qb][ks], ks == 0 ? f32x16{} : dpx[qb]);
+        else sx[qb] = mfma_32x32x16(x, qf[qb][ks], ks == 0 ? f32x16{} : sx[qb]);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
     const bool need_mask = (k0 + C::KSTEP > n_kv) || (qw0 + C::WROWS > n_q) ||
                            (a.causal && k0 + C::KSTEP - 1 > qw0 + delta) ||
                            (a.window > 0 && k0 <= qw0 + C::WROWS - 1 + delta - a.window);
@@ -593,14 +608,17 @@ void bwd_dq_kernel(const BwdArgs a) {
         const float p = exp2_hw(fmaf(sx[qb][r], a.scale_log2, -off[qb]));
         dsb[qb][r >> 3][r & 7] = (__bf16)(p * (dpx[qb][r] - dd[qb]));
       }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int f = 0; f < NT; ++f) {
+      __builtin_amdgcn_sched_barrier(0);
+      const bf16x8 x = tbuf[f % kTrPF];
+      if (f + kTrPF < NT) tbuf[f % kTrPF] = read_trop(f + kTrPF);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb) {
-        const bf16x8 kta = ta.read_tr(kt, ks, nb, hi);
-#pragma unroll
-        for (int qb = 0; qb < C::QB; ++qb) dqa[qb][nb] = mfma_32x32x16(kta, dsb[qb][ks], dqa[qb][nb]);
-      }
+      for (int qb = 0; qb < C::QB; ++qb) dqa[qb][f % C::NB] = mfma_32x32x16(x, dsb[qb][f / C::NB], dqa[qb][f % C::NB]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // dQ = scale * accumulator: lane holds query qw0 + 32 qb + col, dims 32 nb + 8 jj +
