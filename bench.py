@@ -179,6 +179,7 @@ def library_gemm_tflops(dev, n=16384, reps=10):
     a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
     b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
     c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+    settle([lambda: torch.matmul(a, b, out=c)])
     for _ in range(3):
         torch.matmul(a, b, out=c)
     ts = []
@@ -271,10 +272,31 @@ def workload_call(w, dev, window=None, page=None, fp8=False):
     return fn, work, unit
 
 
+# After an idle second the GPU runs its first launches at a low clock and takes about 40 ms of
+# load to reach the clock it holds under sustained load (per-launch times of the 16k prefill
+# after 2 s idle: 3.7, 2.4, 2.2, 2.1, ... ms, settling at 1.78 ms after about 20 launches). Every
+# timed section therefore first runs its own call for SETTLE_MS of wall time, untimed, before
+# its W warm-up launches; the figures are those of sustained load.
+SETTLE_MS = 150.0
+
+
+def settle(fns, min_ms=SETTLE_MS):
+    """Launch the calls in turn, untimed, until `min_ms` of wall time has passed."""
+    import time
+    import torch
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < min_ms:
+        for fn in fns:
+            fn()
+        torch.cuda.synchronize()
+
+
 def time_launches(fn, steps, warmup):
     """Per-launch times (ms) of `steps` launches of fn after `warmup` untimed ones, from HIP
-    events on torch's current stream (the stream the kernels are launched on)."""
+    events on torch's current stream (the stream the kernels are launched on), after the clock
+    has settled under this call's load."""
     import torch
+    settle([fn])
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -292,6 +314,7 @@ def time_interleaved(fns, steps, warmup, rounds=4):
     launching every call `steps // rounds` times in turn (after `warmup` untimed launches of
     each), so that all of them see the same clock and temperature."""
     import torch
+    settle(fns)
     for fn in fns:
         for _ in range(warmup):
             fn()
@@ -453,6 +476,7 @@ def main():
         if ev is not None:
             ev[2].record()
 
+    settle([step])
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -488,6 +512,7 @@ def main():
         fa.bwd(xp["q"], xp["k"], xp["v"], o_p, do_p, lse_p, causal=True, scale=wp.scale, workspace=ws_b,
                dq=grads[0], dk=grads[1], dv=grads[2])
 
+    settle([bwd_call])
     for _ in range(args.warmup):
         bwd_call()
     torch.cuda.synchronize()
@@ -515,6 +540,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": SETTLE_MS,
         "ms_per_step": round(wall * 1e3 / args.steps, 4),
         "higher_is_better": True,
         "scaling": "weak",
