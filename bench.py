@@ -13,9 +13,11 @@ reported beside it, and the backward of the same prefill (fa_bwd, timed on its o
 step) beside that. ``workloads`` then times each of the five workloads alone (K launches after
 W warm-ups: the single-head fp32 check in microseconds only, the prefills in TFLOP/s and as a
 fraction of the bf16 MFMA peak, decode in KV GB/s), and the FP8 prefill (fa_fwd_fp8) of the
-16,384-token workload against the fp8 MFMA peak. Kernel durations come from HIP events on
-the stream the kernels run on (torch's current stream), over exactly K timed steps after W
-warm-up steps.
+16,384-token workload against the fp8 MFMA peak, launched in turn with the bf16 prefill of the
+same workload for its speed-up. Kernel durations come from HIP events on the stream the kernels
+run on (torch's current stream), over exactly K timed steps after W warm-up steps. Before its
+warm-ups every timed section runs its call untimed for SETTLE_MS of wall time, so that the
+GPU has left the low clock it starts from after being idle.
 
 ``cpu_baseline`` times the CPU fp64 oracle (as it is, untuned) on a bounded sample of
 the same prefill workload: consecutive blocks of query rows of one head, until about
