@@ -356,12 +356,14 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
     // work into stretches with no MFMA beside them. `mid` runs at step kDmaStep (tile loads).
 
     // The exp work of a tile is split between the two regions so that both carry about the
-    // same VALU load: region X takes elements [0, kExpX), region Y the last quarter (their
-    // operands belong to the last P V k-step, which region Y reaches only in its second half).
-    // Accumulator element r of key half h of row block qb is element e = 32 qb + 16 h + r; P^T
-    // operand 2 h + r / 8 (k-step) holds its elements r % 8.
+    // same VALU load: region X takes elements [0, kExpX), region Y the rest (their operands
+    // belong to the last P V k-steps, which region Y reaches only in its second half). At
+    // d = 128 region X takes three quarters; at d = 64, whose regions have half the steps,
+    // 20 of 32 (measured: 2.5-3% faster than 24 on B=4, L=2048; 18 did as well, 16 and 22
+    // less). Accumulator element r of key half h of row block qb is element e = 32 qb + 16 h
+    // + r; P^T operand 2 h + r / 8 (k-step) holds its elements r % 8.
     constexpr int kElems = 32 * QB;
-    constexpr int kExpX = kElems - kElems / 4;
+    constexpr int kExpX = D == 64 ? 20 : kElems - kElems / 4;
     auto elem = [](const f32x16 (&x)[QB][2], int e) { return x[e / 32][(e % 32) / 16][e % 16]; };
     // Keep running sums where they are computed: without this, chains of adds are linearised
     // after the region's last MFMA, where nothing else overlaps them.
