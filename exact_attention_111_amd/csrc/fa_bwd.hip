@@ -355,16 +355,32 @@ void bwd_dkdv_kernel(const BwdArgs a) {
     const char* dt = qt + C::QTILE;
     const float* rv = reinterpret_cast<const float*>(qt + 2 * C::QTILE);
 
+    // S and dP of the step (one row block): operand f is the Q (f even) or dO (f odd) row chunk
+    // of k-step f / 2, read one product ahead; the operands of the dV and dK products below are
+    // read two products ahead. Scheduling fences keep each read ahead of the product it
+    // precedes (left alone, the scheduler puts every read right before its product, which then
+    // waits for a whole LDS round trip). Deeper read-ahead of the row chunks does not fit the
+    // 256 registers at d = 128.
+    static_assert(C::RB == 1, "one row block of queries per step");
+    constexpr int kRowPF = 1, kTrPF = 2;
     f32x16 s[C::RB], dp[C::RB];
+    {
+      constexpr int NF = 2 * C::QKS;
+      auto read_rowop = [&](int f) { return (f & 1) ? ta.read_row(dt, 0, f >> 1) : ta.read_row(qt, 0, f >> 1); };
+      bf16x8 rbuf[kRowPF];
 #pragma unroll
-    for (int rb = 0; rb < C::RB; ++rb) {
-      s[rb] = f32x16{};
-      dp[rb] = f32x16{};
+      for (int f = 0; f < kRowPF; ++f) rbuf[f] = read_rowop(f);
 #pragma unroll
-      for (int ks = 0; ks < C::QKS; ++ks) {
-        s[rb] = mfma_32x32x16(ta.read_row(qt, rb, ks), kf[ks], s[rb]);
-        dp[rb] = mfma_32x32x16(ta.read_row(dt, rb, ks), vf[ks], dp[rb]);
+      for (int f = 0; f < NF; ++f) {
+        __builtin_amdgcn_sched_barrier(0);
+        const bf16x8 x = rbuf[f % kRowPF];
+        if (f + kRowPF < NF) rbuf[f % kRowPF] = read_rowop(f + kRowPF);
+        __builtin_amdgcn_sched_barrier(0);
+        const int ks = f >> 1;
+        if (f & 1) dp[0] = mfma_32x32x16(x, vf[ks], ks == 0 ? f32x16{} : dp[0]);
+        else s[0] = mfma_32x32x16(x, kf[ks], ks == 0 ? f32x16{} : s[0]);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
     // Element r of block rb: query row q0 + 32 rb + 8 (r / 4) + 4 half + r % 4, key my_key.
     const bool need_mask = (q0 + C::QSTEP > n_q) || (kw0 + 32 > n_kv) || (a.causal && kw0 + 31 > q0 + delta) ||
@@ -400,13 +416,29 @@ void bwd_dkdv_kernel(const BwdArgs a) {
           dsb[2 * rb + (r >> 3)][r & 7] = (__bf16)ds;
         }
       }
+    // dV^T += dO^T P and dK^T += Q^T dS: product f is dV (f even) or dK (f odd) of block
+    // (f / 2) % NB at k-step (f / 2) / NB.
+    {
+      constexpr int NT = 2 * 2 * C::RB * C::NB;
+      auto read_trop = [&](int f) {
+        const int g = f >> 1, kk = g / C::NB, nb = g % C::NB;
+        return (f & 1) ? ta.read_tr(qt, kk, nb, hi) : ta.read_tr(dt, kk, nb, hi);
+      };
+      bf16x8 tbuf[kTrPF];
 #pragma unroll
-    for (int kk = 0; kk < 2 * C::RB; ++kk)
+      for (int f = 0; f < kTrPF; ++f) tbuf[f] = read_trop(f);
 #pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb) {
-        dva[nb] = mfma_32x32x16(ta.read_tr(dt, kk, nb, hi), pb[kk], dva[nb]);
-        dka[nb] = mfma_32x32x16(ta.read_tr(qt, kk, nb, hi), dsb[kk], dka[nb]);
+      for (int f = 0; f < NT; ++f) {
+        __builtin_amdgcn_sched_barrier(0);
+        const bf16x8 x = tbuf[f % kTrPF];
+        if (f + kTrPF < NT) tbuf[f % kTrPF] = read_trop(f + kTrPF);
+        __builtin_amdgcn_sched_barrier(0);
+        const int g = f >> 1, kk = g / C::NB, nb = g % C::NB;
+        if (f & 1) dka[nb] = mfma_32x32x16(x, dsb[kk], dka[nb]);
+        else dva[nb] = mfma_32x32x16(x, pb[kk], dva[nb]);
       }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
   // dK = scale * dK^T-accumulator, dV: lane holds key my_key, dims 32 nb + 8 (r / 4) +
