@@ -386,13 +386,18 @@ void bwd_dkdv_kernel(const BwdArgs a) {
     const bool need_mask = (q0 + C::QSTEP > n_q) || (kw0 + 32 > n_kv) || (a.causal && kw0 + 31 > q0 + delta) ||
                            (a.window > 0 && kw0 <= q0 + C::QSTEP - 1 + delta - a.window);
     if (need_mask) {
+      // The rows my_key is visible to, as bounds on the element's row offset from
+      // q0 + 4 half: row i sees the key when i < n_q, i >= my_key - delta (causal) and
+      // i < my_key - delta + W (window), and the key exists (my_key < n_kv). Compares and
+      // selects only: the same test written with && and || compiled to a branch per element.
+      const bool key_ok = my_key < n_kv;
 #pragma unroll
       for (int rb = 0; rb < C::RB; ++rb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int i = q0 + 32 * rb + 8 * (r >> 2) + 4 * half + (r & 3);
-          const bool vis = i < n_q && my_key < n_kv && (!a.causal || my_key <= i + delta) &&
-                           (a.window <= 0 || my_key > i + delta - a.window);
+          const bool vis = key_ok & (i < n_q) & (!a.causal | (my_key <= i + delta)) &
+                           ((a.window <= 0) | (my_key > i + delta - a.window));
           s[rb][r] = vis ? s[rb][r] : kNegInf;
           dp[rb][r] = vis ? dp[rb][r] : 0.f;
         }
@@ -619,14 +624,20 @@ void bwd_dq_kernel(const BwdArgs a) {
                            (a.causal && k0 + C::KSTEP - 1 > qw0 + delta) ||
                            (a.window > 0 && k0 <= qw0 + C::WROWS - 1 + delta - a.window);
     if (need_mask) {
+      // The keys row my_q sees, as bounds on the element's key offset from k0 + 4 half: key j
+      // is visible when j < n_kv, j <= my_q + delta (causal) and j > my_q + delta - W
+      // (window), and the row exists (my_q < n_q). Compares and selects only, as above.
+      const int base = k0 + 4 * half;
 #pragma unroll
       for (int qb = 0; qb < C::QB; ++qb) {
         const int my_q = qw0 + 32 * qb + col;
+        const int lo = (a.window > 0 ? my_q + delta - a.window + 1 : -(1 << 30)) - base;
+        int hi = a.causal ? min(n_kv, my_q + delta + 1) : n_kv;
+        hi = my_q < n_q ? hi - base : -(1 << 30);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int j = k0 + 8 * (r >> 2) + 4 * half + (r & 3);
-          const bool vis = my_q < n_q && j < n_kv && (!a.causal || j <= my_q + delta) &&
-                           (a.window <= 0 || j > my_q + delta - a.window);
+          const int off = 8 * (r >> 2) + (r & 3);
+          const bool vis = (off >= lo) & (off < hi);
           sx[qb][r] = vis ? sx[qb][r] : kNegInf;
           dpx[qb][r] = vis ? dpx[qb][r] : 0.f;
         }
