@@ -1,0 +1,151 @@
+"""GPU parity at long sequences and large tensors, through the C ABI.
+
+The workloads of bench.py keep every tensor under 2 GiB except the decode cache. These cases
+put Q (and O) past 2^31 bytes, run the persistent prefill grid for 128 rounds, and give the
+decode split a context of 2^18 keys, so that an offset computed in 32-bit arithmetic, or a
+round or split index that wraps, shows up as a wrong or unwritten row.
+
+Each case checks the whole output tensor for writes (NaN-filled outputs: finite on valid rows,
+O = 0 and LSE = -inf on padding) and sampled rows against the fp64 oracle. Sampled rows cover
+the first and last rows of the sequence, tile edges, and random rows, in the first and last
+heads (the latter at the largest offsets). Tolerances are those of the other parity tests
+(tests/parity.py). The pages' tiled computation is exact ("2.1 FlashAttention-2 的核心思想"
+§2.1.5), and its shapes must be checked (§2.1.7)."""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import fa_inputs
+import oracle
+from parity import check_written, compare, compare_fp8_exact, fp8_flip_slack, nan_filled_outputs, report
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _fa():
+    import exact_attention_111_amd as fa
+    return fa
+
+
+def announce(**case):
+    print("\n[case] " + " ".join(f"{k}={v}" for k, v in case.items()), flush=True)
+    sys.stdout.flush()
+
+
+def sampled_rows(L, rng, n_random=16):
+    edges = [0, 1, 255, 256, L // 2, L - 257, L - 256, L - 2, L - 1]
+    return np.array(sorted(set(edges) | set(rng.choice(L, n_random, replace=False).tolist())), dtype=np.int64)
+
+
+def test_prefill_q_past_2gib_gqa_causal():
+    """B=1, H=64, Hkv=8, L=131072, d=128, causal: Q and O are 2 GiB each (head 63 starts past
+    2^31 bytes); 32,768 query tiles on the persistent grid."""
+    B, H, Hkv, L, d = 1, 64, 8, 131072, 128
+    announce(entry="fa_fwd", B=B, H=H, Hkv=Hkv, L=L, d=d, causal=True)
+    x = fa_inputs.prefill_inputs(B, H, Hkv, L, L, d, seed=71, device=DEV)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = nan_filled_outputs((B, H, L, d), (B, H, L), torch.bfloat16)
+    _fa().fwd(x["q"], x["k"], x["v"], causal=True, scale=scale, out=o, lse=lse)
+    torch.cuda.synchronize()
+    check_written(o, lse, None)
+    rng = np.random.default_rng(72)
+    rows = sampled_rows(L, rng)
+    for h in (0, 37, 63):
+        kvh = h // (H // Hkv)
+        K = x["k"][0, kvh].cpu().double().numpy()
+        V = x["v"][0, kvh].cpu().double().numpy()
+        O, LSE = oracle.attention_head(x["q"][0, h].cpu().double().numpy(), K, V, scale=scale, causal=True, rows=rows)
+        ri = torch.from_numpy(rows).to(DEV)
+        st = compare(o[0, h].index_select(0, ri).cpu(), lse[0, h].index_select(0, ri).cpu(), O, LSE, bf16_out=True,
+                     what=f"L{L} head {h}")
+        report(f"fa_fwd B{B} H{H}/{Hkv} L{L} d{d} causal, head {h}, {len(rows)} rows: O beyond rounding "
+               f"{st['o_max']:.3g}, LSE {st['lse_max']:.3g}")
+
+
+def test_prefill_long_varlen_d64():
+    """Per-sequence lengths up to 2^16 at d=64 (one workgroup per query tile, no persistent grid),
+    the longest sequence last in the batch."""
+    B, H, Hkv, L, d = 3, 8, 2, 65536, 64
+    announce(entry="fa_fwd", B=B, H=H, Hkv=Hkv, L=L, d=d, causal=True, varlen=True)
+    x = fa_inputs.prefill_inputs(B, H, Hkv, L, L, d, seed=73, device=DEV)
+    lens = torch.tensor([40001, 257, L], dtype=torch.int32)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = nan_filled_outputs((B, H, L, d), (B, H, L), torch.bfloat16)
+    _fa().fwd(x["q"], x["k"], x["v"], causal=True, scale=scale, seqlens=lens.to(DEV), out=o, lse=lse)
+    torch.cuda.synchronize()
+    check_written(o, lse, lens.numpy())
+    rng = np.random.default_rng(74)
+    for b in range(B):
+        n = int(lens[b])
+        rows = sampled_rows(n, rng, n_random=min(8, n)) if n > 512 else np.arange(n)
+        for h in (0, H - 1):
+            kvh = h // (H // Hkv)
+            K = x["k"][b, kvh].cpu().double().numpy()
+            V = x["v"][b, kvh].cpu().double().numpy()
+            O, LSE = oracle.attention_head(x["q"][b, h].cpu().double().numpy(), K, V, scale=scale, causal=True,
+                                           n_valid=n, rows=rows)
+            ri = torch.from_numpy(rows).to(DEV)
+            compare(o[b, h].index_select(0, ri).cpu(), lse[b, h].index_select(0, ri).cpu(), O, LSE, bf16_out=True,
+                    what=f"varlen b{b} (n={n}) head {h}")
+
+
+def test_fp8_prefill_long_sequence():
+    """FP8 prefill at L=131072 (H=16, Hkv=2): sampled rows of the first and last heads against
+    the FP8 oracle and against exact attention of the dequantised inputs."""
+    B, H, Hkv, L, d = 1, 16, 2, 131072, 128
+    announce(entry="fa_fwd_fp8", B=B, H=H, Hkv=Hkv, L=L, d=d, causal=True)
+    x = fa_inputs.fp8_prefill_inputs(B, H, Hkv, L, L, d, seed=75, device=DEV)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = nan_filled_outputs((B, H, L, d), (B, H, L), torch.bfloat16)
+    _fa().fwd_fp8(x["q"], x["k"], x["v"], x["q_descale"], x["k_descale"], x["v_descale"], causal=True, scale=scale,
+                  out=o, lse=lse)
+    torch.cuda.synchronize()
+    check_written(o, lse, None)
+    rng = np.random.default_rng(76)
+    rows = sampled_rows(L, rng)
+    for h in (0, H - 1):
+        kvh = h // (H // Hkv)
+        Q = oracle.e4m3_decode(x["q"][0, h].cpu().numpy()) * float(x["q_descale"][0, h])
+        K = oracle.e4m3_decode(x["k"][0, kvh].cpu().numpy()) * float(x["k_descale"][0, kvh])
+        V = oracle.e4m3_decode(x["v"][0, kvh].cpu().numpy()) * float(x["v_descale"][0, kvh])
+        O, LSE = oracle.attention_fp8_head(Q, K, V, scale=scale, causal=True, rows=rows)
+        slack = fp8_flip_slack(Q, K, V, scale=scale, causal=True, rows=rows)
+        ri = torch.from_numpy(rows).to(DEV)
+        o_r, lse_r = o[0, h].index_select(0, ri).cpu(), lse[0, h].index_select(0, ri).cpu()
+        st = compare(o_r, lse_r, O, LSE, bf16_out=True, what=f"fp8 L{L} head {h}", o_slack=slack)
+        r = compare_fp8_exact(o_r, lse_r, Q, K, V, scale=scale, causal=True, rows=rows, what=f"fp8 L{L} head {h}")
+        report(f"fa_fwd_fp8 L{L}, head {h}, {len(rows)} rows: vs FP8 oracle O {st['o_max']:.3g}; "
+               f"vs exact attention max err/allowance {r:.3f}")
+
+
+def test_decode_context_of_2_18_keys():
+    """Decode with a 2^18-key cache: one full context, one odd length and one single key, every
+    (request, head) against the oracle."""
+    B, H, Hkv, Lmax, d = 3, 16, 2, 262144, 128
+    announce(entry="fa_decode", B=B, H=H, Hkv=Hkv, Lmax=Lmax, d=d)
+    x = fa_inputs.decode_inputs(B, H, Hkv, Lmax, d, seed=77, device=DEV)
+    ctx = torch.tensor([Lmax, 150001, 1], dtype=torch.int32)
+    scale = 1.0 / math.sqrt(d)
+    o = torch.full((B, H, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = torch.full((B, H), float("nan"), dtype=torch.float32, device=DEV)
+    _fa().decode(x["q"], x["k_cache"], x["v_cache"], ctx.to(DEV), scale=scale, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all(), "an output of the decode is not finite"
+    group = H // Hkv
+    Os, Ls = np.empty((B, H, d)), np.empty((B, H))
+    for b in range(B):
+        n = int(ctx[b])
+        for kvh in range(Hkv):
+            K = x["k_cache"][b, kvh, :n].cpu().double().numpy()
+            V = x["v_cache"][b, kvh, :n].cpu().double().numpy()
+            for h in range(kvh * group, (kvh + 1) * group):
+                Oh, Lh = oracle.attention_head(x["q"][b, h][None].cpu().double().numpy(), K, V, scale=scale)
+                Os[b, h], Ls[b, h] = Oh[0], Lh[0]
+    st = compare(o.cpu(), lse.cpu(), Os, Ls, bf16_out=True, what=f"decode Lmax {Lmax}")
+    report(f"fa_decode B{B} H{H}/{Hkv} Lmax {Lmax} (contexts {ctx.tolist()}): O beyond rounding {st['o_max']:.3g}, "
+           f"LSE {st['lse_max']:.3g}")
