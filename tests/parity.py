@@ -252,3 +252,56 @@ def check_written(o, lse, n_valid):
         if n < L:
             assert torch.all(o[b, :, n:] == 0), f"batch {b}: padding rows of O are not 0"
             assert torch.all(torch.isneginf(lse[b, :, n:])), f"batch {b}: padding LSE is not -inf"
+
+
+# Exact gradients of selected rows (dQ) or keys (dK, dV) of one head, for long sequences where
+# the whole-tensor oracle is too slow; each returns the elements' allowances beside them.
+def _attention_head(*args, **kw):
+    import importlib
+    return importlib.import_module("oracle.attention").attention_head(*args, **kw)
+
+
+def grad_rows_oracle(q, k, v, do, rows, *, scale, causal):
+    """dQ rows exactly: each row needs only its own P and dP rows. Also returns each element's
+    allowance (``parity.grad_tolerances``, restricted to these rows)."""
+    dQ, tQ = [], []
+    for i in rows:
+        O, _, P = _attention_head(q, k, v, scale=scale, causal=causal, rows=[i], return_p=True)
+        dP = do[i] @ v.T
+        D = float(do[i] @ O[0])
+        dQ.append(scale * ((P[0] * (dP - D)) @ k))
+        delta = float(np.abs(do[i]) @ (P[0] @ np.abs(v)))
+        W = np.abs(P[0] * (dP - D)) + 2.0 * P[0] * delta
+        tQ.append(GRAD_REL * scale * (W @ np.abs(k)))
+    return np.stack(dQ), np.stack(tQ)
+
+
+def grad_keys_oracle(q, k, v, do, keys, *, scale, causal, block=1024, row_from=0):
+    """dK, dV rows of the given keys exactly: O and LSE of every row first (in row blocks),
+    then the columns of P and dS for those keys. With a causal mask and every key at or after
+    row_from, rows before row_from see none of them and are left out."""
+    L = q.shape[0]
+    assert row_from == 0 or (causal and min(keys) >= row_from)
+    R = np.arange(row_from, L)
+    O = np.empty((len(R), q.shape[1]))
+    OA = np.empty_like(O)  # P |V|, for the allowances
+    LSE = np.empty(len(R))
+    for r0 in range(0, len(R), block):
+        sel = np.arange(r0, min(len(R), r0 + block))
+        O[sel], LSE[sel] = _attention_head(q, k, v, scale=scale, causal=causal, rows=R[sel])
+        OA[sel], _ = _attention_head(q, k, np.abs(v), scale=scale, causal=causal, rows=R[sel])
+    qR, doR = q[R], do[R]
+    D = (doR * O).sum(axis=1)
+    delta = (np.abs(doR) * OA).sum(axis=1)
+    dK, dV, tK, tV = [], [], [], []
+    for j in keys:
+        s = scale * (qR @ k[j])
+        vis = (R >= j) if causal else np.ones(len(R), bool)
+        p = np.where(vis, np.exp(np.where(vis, s, 0.0) - LSE), 0.0)
+        dp = doR @ v[j]
+        ds = p * (dp - D)
+        dK.append(scale * (ds @ qR))
+        dV.append(p @ doR)
+        tK.append(GRAD_REL * scale * ((np.abs(ds) + 2.0 * p * delta) @ np.abs(qR)))
+        tV.append(GRAD_REL * (p @ np.abs(doR)))
+    return np.stack(dK), np.stack(dV), np.stack(tK), np.stack(tV)

@@ -16,8 +16,7 @@ import torch
 
 import fa_inputs
 import oracle
-from oracle.attention import attention_head
-from parity import GRAD_REL, compare_grad as _close, grad_tolerances, report
+from parity import GRAD_REL, compare_grad as _close, grad_keys_oracle, grad_rows_oracle, grad_tolerances, report
 
 pytestmark = pytest.mark.gpu
 
@@ -116,48 +115,6 @@ def test_bwd_empty_calls():
     assert torch.all(dq == 0)
 
 
-def _rows_oracle(q, k, v, do, rows, *, scale, causal):
-    """dQ rows exactly: each row needs only its own P and dP rows. Also returns each element's
-    allowance (``parity.grad_tolerances``, restricted to these rows)."""
-    dQ, tQ = [], []
-    for i in rows:
-        O, _, P = attention_head(q, k, v, scale=scale, causal=causal, rows=[i], return_p=True)
-        dP = do[i] @ v.T
-        D = float(do[i] @ O[0])
-        dQ.append(scale * ((P[0] * (dP - D)) @ k))
-        delta = float(np.abs(do[i]) @ (P[0] @ np.abs(v)))
-        W = np.abs(P[0] * (dP - D)) + 2.0 * P[0] * delta
-        tQ.append(GRAD_REL * scale * (W @ np.abs(k)))
-    return np.stack(dQ), np.stack(tQ)
-
-
-def _keys_oracle(q, k, v, do, keys, *, scale, causal, block=1024):
-    """dK, dV rows of the given keys exactly: O and LSE of every row first (in row blocks),
-    then the columns of P and dS for those keys."""
-    L = q.shape[0]
-    O = np.empty_like(q)
-    OA = np.empty_like(q)  # P |V|, for the allowances
-    LSE = np.empty(L)
-    for r0 in range(0, L, block):
-        rows = np.arange(r0, min(L, r0 + block))
-        O[rows], LSE[rows] = attention_head(q, k, v, scale=scale, causal=causal, rows=rows)
-        OA[rows], _ = attention_head(q, k, np.abs(v), scale=scale, causal=causal, rows=rows)
-    D = (do * O).sum(axis=1)
-    delta = (np.abs(do) * OA).sum(axis=1)
-    dK, dV, tK, tV = [], [], [], []
-    for j in keys:
-        s = scale * (q @ k[j])
-        vis = (np.arange(L) >= j) if causal else np.ones(L, bool)
-        p = np.where(vis, np.exp(np.where(vis, s, 0.0) - LSE), 0.0)
-        dp = do @ v[j]
-        ds = p * (dp - D)
-        dK.append(scale * (ds @ q))
-        dV.append(p @ do)
-        tK.append(GRAD_REL * scale * ((np.abs(ds) + 2.0 * p * delta) @ np.abs(q)))
-        tV.append(GRAD_REL * (p @ np.abs(do)))
-    return np.stack(dK), np.stack(dV), np.stack(tK), np.stack(tV)
-
-
 def test_bwd_full_size_causal_L16384_d128_sampled():
     """The 16,384-token causal workload at full size: sampled dQ rows of two heads and
     sampled dK/dV keys of one head against the oracle."""
@@ -174,11 +131,11 @@ def test_bwd_full_size_causal_L16384_d128_sampled():
     keys = np.sort(np.concatenate([[0, 1, 63, 64, w.L - 1], rng.choice(w.L, 11, replace=False)]))
     for h in (0, 21):
         q64, k64, v64, do64 = (fa_inputs.as_oracle_f64(t[0, h]) for t in (x["q"], x["k"], x["v"], do))
-        dQ, tQ = _rows_oracle(q64, k64, v64, do64, rows, scale=w.scale, causal=True)
+        dQ, tQ = grad_rows_oracle(q64, k64, v64, do64, rows, scale=w.scale, causal=True)
         r = _close(dq[0, h, rows], dQ, f"dQ rows head {h}", tQ)
         report(f"fa_bwd {w.name}: dQ, {len(rows)} rows of head {h}: max err/allowance {r:.3f}")
         if h == 0:
-            dK, dV, tK, tV = _keys_oracle(q64, k64, v64, do64, keys, scale=w.scale, causal=True)
+            dK, dV, tK, tV = grad_keys_oracle(q64, k64, v64, do64, keys, scale=w.scale, causal=True)
             rk = _close(dk[0, h, keys], dK, "dK keys head 0", tK)
             rv = _close(dv[0, h, keys], dV, "dV keys head 0", tV)
             report(f"fa_bwd {w.name}: dK, dV, {len(keys)} keys of head 0: max err/allowance {rk:.3f}, {rv:.3f}")

@@ -1,9 +1,10 @@
 """GPU parity at long sequences and large tensors, through the C ABI.
 
 The workloads of bench.py keep every tensor under 2 GiB except the decode cache. These cases
-put Q (and O) past 2^31 bytes, run the persistent prefill grid for 128 rounds, and give the
-decode split a context of 2^18 keys, so that an offset computed in 32-bit arithmetic, or a
-round or split index that wraps, shows up as a wrong or unwritten row.
+put Q (and O) past 2^31 bytes, run the persistent prefill grid for 128 rounds, give the
+decode split a context of 2^18 keys, and run the backward with every tensor at 2 GiB, so that
+an offset computed in 32-bit arithmetic, or a round or split index that wraps, shows up as a
+wrong or unwritten row.
 
 Each case checks the whole output tensor for writes (NaN-filled outputs: finite on valid rows,
 O = 0 and LSE = -inf on padding) and sampled rows against the fp64 oracle. Sampled rows cover
@@ -20,7 +21,8 @@ import torch
 
 import fa_inputs
 import oracle
-from parity import check_written, compare, compare_fp8_exact, fp8_flip_slack, nan_filled_outputs, report
+from parity import (check_written, compare, compare_fp8_exact, compare_grad, fp8_flip_slack, grad_keys_oracle,
+                    grad_rows_oracle, nan_filled_outputs, report)
 
 pytestmark = pytest.mark.gpu
 
@@ -149,3 +151,38 @@ def test_decode_context_of_2_18_keys():
     st = compare(o.cpu(), lse.cpu(), Os, Ls, bf16_out=True, what=f"decode Lmax {Lmax}")
     report(f"fa_decode B{B} H{H}/{Hkv} Lmax {Lmax} (contexts {ctx.tolist()}): O beyond rounding {st['o_max']:.3g}, "
            f"LSE {st['lse_max']:.3g}")
+
+
+def test_bwd_tensors_of_2gib_long_causal():
+    """Backward with every tensor of 2 GiB (B=1, H=Hkv=128, L=65536, d=128, causal): sampled dQ
+    rows of the first and last heads, and dK/dV of keys in the last 256 positions (which only
+    the last 256 rows see) of the last head, against the oracle."""
+    B, H, L, d = 1, 128, 65536, 128
+    announce(entry="fa_bwd", B=B, H=H, Hkv=H, L=L, d=d, causal=True)
+    fa = _fa()
+    x = fa_inputs.prefill_inputs(B, H, H, L, L, d, seed=78, device=DEV)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = fa.fwd(x["q"], x["k"], x["v"], causal=True, scale=scale)
+    g = torch.Generator(device=DEV).manual_seed(79)
+    do = torch.randn(o.shape, generator=g, device=DEV, dtype=torch.float32).to(torch.bfloat16)
+    dq, dk, dv = (torch.full_like(x[n], float("nan")) for n in ("q", "k", "v"))
+    fa.bwd(x["q"], x["k"], x["v"], o, do, lse, causal=True, scale=scale, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    for name, t in (("dQ", dq), ("dK", dk), ("dV", dv)):
+        assert torch.isfinite(t).all(), f"{name}: an element is not finite (unwritten?)"
+    rng = np.random.default_rng(80)
+    rows = np.sort(np.concatenate([[0, 1, 127, 128, L - 1], rng.choice(L, 7, replace=False)]))
+    keys = np.array([L - 256, L - 255, L - 129, L - 128, L - 2, L - 1])
+    for h in (0, H - 1):
+        q64, k64, v64, do64 = (fa_inputs.as_oracle_f64(t[0, h]) for t in (x["q"], x["k"], x["v"], do))
+        dQ, tQ = grad_rows_oracle(q64, k64, v64, do64, rows, scale=scale, causal=True)
+        ri = torch.from_numpy(rows).to(DEV)
+        r = compare_grad(dq[0, h].index_select(0, ri), dQ, f"dQ rows head {h}", tQ)
+        report(f"fa_bwd B{B} H{H} L{L} d{d} causal: dQ, {len(rows)} rows of head {h}: max err/allowance {r:.3f}")
+        if h == H - 1:
+            dK, dV, tK, tV = grad_keys_oracle(q64, k64, v64, do64, keys, scale=scale, causal=True, row_from=L - 256)
+            ki = torch.from_numpy(keys).to(DEV)
+            rk = compare_grad(dk[0, h].index_select(0, ki), dK, f"dK keys head {h}", tK)
+            rv = compare_grad(dv[0, h].index_select(0, ki), dV, f"dV keys head {h}", tV)
+            report(f"fa_bwd B{B} H{H} L{L} d{d} causal: dK, dV, {len(keys)} keys of head {h}: "
+                   f"max err/allowance {rk:.3f}, {rv:.3f}")
