@@ -186,3 +186,28 @@ def test_bwd_tensors_of_2gib_long_causal():
             rv = compare_grad(dv[0, h].index_select(0, ki), dV, f"dV keys head {h}", tV)
             report(f"fa_bwd B{B} H{H} L{L} d{d} causal: dK, dV, {len(keys)} keys of head {h}: "
                    f"max err/allowance {rk:.3f}, {rv:.3f}")
+
+
+def test_sliding_window_prefill_long_sequence():
+    """A 4096-key causal band over L=131072 (H=4, Hkv=1, d=128): the tiles before each query
+    tile's band are never loaded; sampled rows against the windowed oracle."""
+    B, H, Hkv, L, d, W = 1, 4, 1, 131072, 128, 4096
+    announce(entry="fa_fwd_sliding_window", B=B, H=H, Hkv=Hkv, L=L, d=d, window=W)
+    x = fa_inputs.prefill_inputs(B, H, Hkv, L, L, d, seed=81, device=DEV)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = nan_filled_outputs((B, H, L, d), (B, H, L), torch.bfloat16)
+    _fa().fwd(x["q"], x["k"], x["v"], causal=True, scale=scale, window=W, out=o, lse=lse)
+    torch.cuda.synchronize()
+    check_written(o, lse, None)
+    rng = np.random.default_rng(82)
+    rows = sampled_rows(L, rng)
+    K = x["k"][0, 0].cpu().double().numpy()
+    V = x["v"][0, 0].cpu().double().numpy()
+    for h in (0, H - 1):
+        O, LSE = oracle.attention_head(x["q"][0, h].cpu().double().numpy(), K, V, scale=scale, causal=True, rows=rows,
+                                       window=W)
+        ri = torch.from_numpy(rows).to(DEV)
+        st = compare(o[0, h].index_select(0, ri).cpu(), lse[0, h].index_select(0, ri).cpu(), O, LSE, bf16_out=True,
+                     what=f"window {W} L{L} head {h}")
+        report(f"fa_fwd_sliding_window L{L} W{W}, head {h}, {len(rows)} rows: O beyond rounding {st['o_max']:.3g}, "
+               f"LSE {st['lse_max']:.3g}")
