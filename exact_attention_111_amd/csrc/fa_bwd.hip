@@ -13,16 +13,17 @@
 //   * bwd_dot: per query row, the exp2 offset LSE*log2(e) and D, as one (offset, D) pair
 //     (+inf and 0 on padding rows); d / 8 lanes per row.
 //   * bwd_dkdv: one workgroup per (batch, KV head, 128 keys): 4 waves x 32 keys, whose K
-//     and V rows stay in registers as B operands. Steps of 64 query rows of every query head
-//     of the group stream through a ring of LDS stages (Q tile, dO tile, the rows' pairs),
-//     filled by direct buffer-to-LDS loads issued three steps ahead. Per step: S = Q K^T and
-//     dP = dO V^T (row reads; the accumulators hold one key column per lane), P and dS, then
-//     dV^T += dO^T P and dK^T += Q^T dS (transposed reads; P and dS go from the accumulators
-//     straight into B operands).
-//   * bwd_dq: one workgroup per (batch, head, 256 query rows): 4 waves x 64 rows, with their
-//     Q and dO rows in registers. 32-key K/V tiles stream through a ring of LDS stages loaded
-//     five steps ahead. S^T = K Q^T and dP^T = V dO^T leave one query column per lane, then
-//     dQ^T += K^T dS^T; every K/V operand read from LDS serves both 32-row halves of a wave.
+//     and V rows stay in registers as B operands; two workgroups per CU (two waves per SIMD).
+//     Steps of 32 query rows of every query head of the group stream through a 4-stage ring
+//     of LDS stages (Q tile, dO tile, the rows' pairs), filled by direct buffer-to-LDS loads
+//     issued three steps ahead. Per step: S = Q K^T and dP = dO V^T (row reads; the
+//     accumulators hold one key column per lane), P and dS, then dV^T += dO^T P and
+//     dK^T += Q^T dS (transposed reads; P and dS go from the accumulators straight into B
+//     operands). Operands are read one (rows) and two (transposed) products ahead.
+//   * bwd_dq: one workgroup per (batch, head, 128 query rows): 4 waves x 32 rows, with their
+//     Q and dO rows in registers. 32-key K/V tiles stream through a 4-stage ring loaded
+//     three steps ahead. S^T = K Q^T and dP^T = V dO^T leave one query column per lane, then
+//     dQ^T += K^T dS^T. Operands are read four (rows) and three (transposed) products ahead.
 //   Each tile sits in LDS once, in a layout (kv_xor) that serves both its row and its
 //   transposed reads without bank conflicts. Rows past the sequence are not read: their LDS
 //   rows keep earlier input rows or the zeros the kernels start from, and the mask gives
