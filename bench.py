@@ -16,8 +16,10 @@ fraction of the bf16 MFMA peak, decode in KV GB/s), and the FP8 prefill (fa_fwd_
 16,384-token workload against the fp8 MFMA peak, launched in turn with the bf16 prefill of the
 same workload for its speed-up. Kernel durations come from HIP events on the stream the kernels
 run on (torch's current stream), over exactly K timed steps after W warm-up steps. Before its
-warm-ups every timed section runs its call untimed for SETTLE_MS of wall time, so that the
-GPU has left the low clock it starts from after being idle.
+warm-ups every timed section runs its calls untimed until their times have stopped falling
+(at least SETTLE_MS of wall time, at most SETTLE_MAX_MS), so that the GPU has left the low
+clock it starts from after being idle or after a lighter load; ``settle`` reports what each
+section took.
 
 ``cpu_baseline`` times the CPU fp64 oracle (as it is, untuned) on a bounded sample of
 the same prefill workload: consecutive blocks of query rows of one head, until about
@@ -181,7 +183,7 @@ def library_gemm_tflops(dev, n=16384, reps=10):
     a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
     b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
     c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
-    settle([lambda: torch.matmul(a, b, out=c)])
+    settle([lambda: torch.matmul(a, b, out=c)], "library_gemm")
     for _ in range(3):
         torch.matmul(a, b, out=c)
     ts = []
@@ -276,29 +278,52 @@ def workload_call(w, dev, window=None, page=None, fp8=False):
 
 # After an idle second the GPU runs its first launches at a low clock and takes about 40 ms of
 # load to reach the clock it holds under sustained load (per-launch times of the 16k prefill
-# after 2 s idle: 3.7, 2.4, 2.2, 2.1, ... ms, settling at 1.78 ms after about 20 launches). Every
-# timed section therefore first runs its own call for SETTLE_MS of wall time, untimed, before
-# its W warm-up launches; the figures are those of sustained load.
+# after 2 s idle: 3.7, 2.4, 2.2, 2.1, ... ms, settling at 1.78 ms after about 20 launches). A
+# change of load can take longer: FP8 prefills launched in turn with bf16 ones, right after the
+# decode workload, went 1.93, 1.76, 1.68, ... 1.48, ... 1.33 ms over their first 70 ms while the
+# bf16 launches beside them held steady. Every timed section therefore first runs its own
+# calls untimed, each round of them bracketed by HIP events, for at least SETTLE_MS of wall
+# time and then until the median round time of the last SETTLE_WINDOW rounds is no more than
+# SETTLE_TOL below that of the SETTLE_WINDOW before them (the times have stopped falling), or
+# SETTLE_MAX_MS has passed; then come its W warm-up launches. The figures are those of
+# sustained load. The wall time each section took to settle is reported (SETTLE_LOG).
 SETTLE_MS = 150.0
+SETTLE_MAX_MS = 1500.0
+SETTLE_WINDOW = 8
+SETTLE_TOL = 0.01
+SETTLE_LOG = {}
 
 
-def settle(fns, min_ms=SETTLE_MS):
-    """Launch the calls in turn, untimed, until `min_ms` of wall time has passed."""
+def settle(fns, label, min_ms=SETTLE_MS, max_ms=SETTLE_MAX_MS):
+    """Launch the calls in turn, untimed, until the round times have stopped falling (see
+    above); records the wall time taken under `label` in SETTLE_LOG."""
     import time
     import torch
     t0 = time.perf_counter()
-    while (time.perf_counter() - t0) * 1e3 < min_ms:
+    rounds = []
+    while True:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
         for fn in fns:
             fn()
+        b.record()
         torch.cuda.synchronize()
+        rounds.append(a.elapsed_time(b))
+        el = (time.perf_counter() - t0) * 1e3
+        if el >= max_ms:
+            break
+        if el >= min_ms and len(rounds) >= 2 * SETTLE_WINDOW and \
+                median(rounds[-SETTLE_WINDOW:]) >= (1.0 - SETTLE_TOL) * median(rounds[-2 * SETTLE_WINDOW:-SETTLE_WINDOW]):
+            break
+    SETTLE_LOG[label] = {"ms": round(el, 1), "rounds": len(rounds)}
 
 
-def time_launches(fn, steps, warmup):
+def time_launches(fn, steps, warmup, label):
     """Per-launch times (ms) of `steps` launches of fn after `warmup` untimed ones, from HIP
     events on torch's current stream (the stream the kernels are launched on), after the clock
     has settled under this call's load."""
     import torch
-    settle([fn])
+    settle([fn], label)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -311,12 +336,12 @@ def time_launches(fn, steps, warmup):
     return [a.elapsed_time(b) for a, b in ev]
 
 
-def time_interleaved(fns, steps, warmup, rounds=4):
+def time_interleaved(fns, steps, warmup, label, rounds=4):
     """Per-launch times (ms) of several calls timed in the same window: `rounds` rounds, each
     launching every call `steps // rounds` times in turn (after `warmup` untimed launches of
     each), so that all of them see the same clock and temperature."""
     import torch
-    settle(fns)
+    settle(fns, label)
     for fn in fns:
         for _ in range(warmup):
             fn()
@@ -347,7 +372,7 @@ def workload_lines(steps, warmup, dev):
     out = {}
     for name, w in fa_inputs.WORKLOADS.items():
         fn, work, unit = workload_call(w, dev)
-        ms = time_launches(fn, steps, warmup)
+        ms = time_launches(fn, steps, warmup, name)
         med = median(ms)
         sp = spread(ms)
         if w.name == "single_head_fp32_L128_d64":
@@ -370,7 +395,7 @@ def workload_lines(steps, warmup, dev):
     w = fa_inputs.WORKLOADS[PREFILL]
     fn, work, _ = workload_call(w, dev, fp8=True)
     fn_bf16, _, _ = workload_call(w, dev)
-    ms, ms_bf16 = time_interleaved([fn, fn_bf16], steps, warmup)
+    ms, ms_bf16 = time_interleaved([fn, fn_bf16], steps, warmup, "fp8+bf16:" + PREFILL)
     med = median(ms)
     rate = work / (med * 1e-3) / 1e12
     tr, src = traffic_record("fp8")
@@ -478,7 +503,7 @@ def main():
         if ev is not None:
             ev[2].record()
 
-    settle([step])
+    settle([step], "step")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -514,7 +539,7 @@ def main():
         fa.bwd(xp["q"], xp["k"], xp["v"], o_p, do_p, lse_p, causal=True, scale=wp.scale, workspace=ws_b,
                dq=grads[0], dk=grads[1], dv=grads[2])
 
-    settle([bwd_call])
+    settle([bwd_call], "backward")
     for _ in range(args.warmup):
         bwd_call()
     torch.cuda.synchronize()
@@ -542,7 +567,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "settle_ms": SETTLE_MS,
+        "settle": {"min_ms": SETTLE_MS, "max_ms": SETTLE_MAX_MS, "window_rounds": SETTLE_WINDOW,
+                   "tol": SETTLE_TOL, "taken": SETTLE_LOG},
         "ms_per_step": round(wall * 1e3 / args.steps, 4),
         "higher_is_better": True,
         "scaling": "weak",

@@ -90,6 +90,8 @@ struct BwdArgs {
   int causal;
   int window;  // sliding window W (0: none): key j needs j > i + Lk - Lq - W
   const int32_t* seqlens;
+  TileOrder order;             // tile_order of the launch (used with GQA)
+  Divisor group_div, hkv_div;  // H / Hkv and Hkv as divisors
 };
 
 // Valid query rows / keys of batch entry b.
@@ -97,7 +99,7 @@ __device__ __forceinline__ void seq_extent(const BwdArgs& a, int b, int& n_q, in
   n_q = a.Lq;
   n_kv = a.Lk;
   if (a.seqlens != nullptr) {
-    const int n = min(max(a.seqlens[b], 0), a.Lk);
+    const int n = min(max(load_const(a.seqlens + b), 0), a.Lk);
     n_q = n;
     n_kv = n;
   }
@@ -243,16 +245,15 @@ void bwd_dkdv_kernel(const BwdArgs a) {
   // Key blocks in order of decreasing work under a causal mask (the first keys are seen by
   // the most rows). Without GQA: all (batch, KV head) pairs of one key block together. With
   // GQA (XCD_ORDER) a workgroup streams the Q and dO rows of every query head of its group,
-  // so the order of the prefill is used instead (xcd_tile_order): pairs dealt to the XCDs,
+  // so the order of the prefill is used instead (tile_order): pairs dealt to the XCDs,
   // each XCD working through its pairs a few at a time, so that the key blocks it runs at
   // once share those rows in its L2.
   const int nbk = a.B * a.Hkv;
   int kbi, bk;
   if constexpr (XCD_ORDER) {
-    const int nkb = (int)(gridDim.x / nbk);
     int qt;
-    xcd_tile_order(blockIdx.x, gridDim.x, nkb, bk, qt);
-    kbi = nkb - 1 - qt;
+    tile_order(a.order, blockIdx.x, bk, qt);  // a.order.ntq key blocks per pair
+    kbi = a.order.ntq - 1 - qt;
   } else {
     kbi = blockIdx.x / nbk;
     bk = blockIdx.x - kbi * nbk;
@@ -476,16 +477,16 @@ void bwd_dq_kernel(const BwdArgs a) {
   // Query blocks in order of decreasing work under a causal mask (the last rows see the
   // most keys). Without GQA: all (batch, head) pairs of one block together. With GQA
   // (XCD_ORDER) the query heads of a group read the same K and V rows, so the order of the
-  // prefill (xcd_tile_order) is applied to (batch, KV head) pairs, each with `group` x ntq
+  // prefill (tile_order) is applied to (batch, KV head) pairs, each with `group` x ntq
   // blocks: a pair's blocks run on one XCD, and the group's heads take the same query block
   // next to each other, so their K/V tiles are shared in that XCD's L2.
   const int ntq = (a.Lq + C::QROWS - 1) / C::QROWS;
   int qt, b, h;
   if constexpr (XCD_ORDER) {
     int pair, u;
-    xcd_tile_order(blockIdx.x, gridDim.x, a.group * ntq, pair, u);
-    qt = u / a.group;
-    b = pair / a.Hkv;
+    tile_order(a.order, blockIdx.x, pair, u);
+    qt = div_by(u, a.group_div);
+    b = div_by(pair, a.hkv_div);
     h = (pair - b * a.Hkv) * a.group + (u - qt * a.group);
   } else {
     const int nbh = a.B * a.H;
@@ -697,6 +698,8 @@ hipError_t launch_b(const BwdParams& p, hipStream_t stream) {
   a.causal = p.causal;
   a.window = p.window;
   a.seqlens = p.seqlens;
+  a.group_div = make_divisor(a.group);
+  a.hkv_div = make_divisor(p.Hkv);
   void* args[] = {&a};
   const long long rows = (long long)p.B * p.H * p.Lq;
   const long long ndot = (rows + (256 / (D / 8)) - 1) / (256 / (D / 8));
@@ -717,13 +720,20 @@ hipError_t launch_b(const BwdParams& p, hipStream_t stream) {
     // without it (B=4, H=16, L=2048, d=64), so it is used with GQA only.
     const void* kfn = p.H > p.Hkv ? reinterpret_cast<const void*>(&bwd_dkdv_kernel<D, true>)
                                   : reinterpret_cast<const void*>(&bwd_dkdv_kernel<D, false>);
-    e = hipLaunchKernel(kfn, dim3((unsigned)nkv), dim3(C::NT), args, 0, stream);
+    BwdArgs ak = a;
+    ak.order = make_tile_order((int)nkv, (p.Lk + C::KEYS - 1) / C::KEYS);
+    void* kargs[] = {&ak};
+    e = hipLaunchKernel(kfn, dim3((unsigned)nkv), dim3(C::NT), kargs, 0, stream);
     if (e != hipSuccess) return e;
   }
-  if (nq > 0)
+  if (nq > 0) {
+    BwdArgs aq = a;
+    aq.order = make_tile_order((int)nq, a.group * ((p.Lq + C::QROWS - 1) / C::QROWS));
+    void* qargs[] = {&aq};
     e = hipLaunchKernel(p.H > p.Hkv ? reinterpret_cast<const void*>(&bwd_dq_kernel<D, true>)
                                     : reinterpret_cast<const void*>(&bwd_dq_kernel<D, false>),
-                        dim3((unsigned)nq), dim3(C::NT), args, 0, stream);
+                        dim3((unsigned)nq), dim3(C::NT), qargs, 0, stream);
+  }
   return e;
 }
 

@@ -95,6 +95,13 @@ __device__ __forceinline__ const T* uniform_ptr(const T* p) {
   return reinterpret_cast<const T*>((hi << 32) | lo);
 }
 
+// A load at a wave-uniform address of memory that no kernel writes while this one runs,
+// through the scalar cache (s_load): it waits on the scalar counter, not on the vector memory
+// counter that also tracks the tile loads and stores.
+__device__ __forceinline__ int load_const(const int* p) {
+  return *(const __attribute__((address_space(4))) int*)p;
+}
+
 // Both halves of a wave at once: v_permlane32_swap exchanges the upper 32 lanes of its
 // first operand with the lower 32 lanes of its second, so swapping a value with itself
 // leaves [x_lo, x_lo] and [x_hi, x_hi]: every lane then holds its own value and that of

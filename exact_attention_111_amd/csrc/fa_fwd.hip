@@ -98,8 +98,10 @@ struct FwdArgs {
   int B, H, Hkv, Lq, Lk;
   int group;        // H / Hkv
   int ntq;          // query tiles per head
-  int nwg;          // query tiles (ids of xcd_tile_order)
+  int nwg;          // query tiles (ids of tile_order)
   int nprog;        // workgroups launched (tile_of_program)
+  TileOrder order;  // tile_order over (batch, KV head) pairs, group x ntq tiles each
+  Divisor group_div, hkv_div;  // H / Hkv and Hkv as divisors
   float scale_log2; // scale * log2(e)
   int causal;
   int window;       // sliding window W (0: none): key j needs j > i + Lk - Lq - W
@@ -132,20 +134,20 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D>::WAVES_PER_SIMD, FwdCfg<D>::WAVES_P
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, provably uniform
     const int col = lane & 31;   // this lane's query row within a 32-row block
     const int half = lane >> 5;  // which 8-element half of a 16-wide k-step
-    // Workgroup order: xcd_tile_order over (batch, KV head) pairs with group x ntq tiles
+    // Workgroup order: tile_order over (batch, KV head) pairs with group x ntq tiles
     // each, so the query heads that share a KV head run on one XCD and take the same query
     // tile side by side (their K/V tiles are then shared in that XCD's L2). Without GQA the
     // pairs are the heads themselves.
     int pair, u;
-    xcd_tile_order(tile, a.nwg, a.group * a.ntq, pair, u);
-    const int qt = u / a.group;
-    const int b = pair / a.Hkv;
+    tile_order(a.order, tile, pair, u);
+    const int qt = div_by(u, a.group_div);
+    const int b = div_by(pair, a.hkv_div);
     const int kvh = pair - b * a.Hkv;
     const int h = kvh * a.group + (u - qt * a.group);
 
     int n_kv = a.Lk, n_q = a.Lq;
     if (a.seqlens != nullptr) {
-      const int n = min(max(a.seqlens[b], 0), a.Lk);
+      const int n = min(max(load_const(a.seqlens + b), 0), a.Lk);
       n_kv = n;
       n_q = n;
     }
@@ -745,6 +747,10 @@ hipError_t launch(const FwdParams& p, hipStream_t stream) {
   const long long nwg = (long long)a.ntq * p.B * p.H;
   if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   a.nwg = (int)nwg;
+  if (a.nwg == 0) return hipSuccess;
+  a.order = make_tile_order(a.nwg, a.group * a.ntq);
+  a.group_div = make_divisor(a.group);
+  a.hkv_div = make_divisor(p.Hkv);
   // Dense inputs run on a persistent grid, one workgroup per compute unit: the hardware hands
   // workgroups to each XCD's shader engines in a fixed turn, so with one tile per workgroup a
   // compute unit that finishes early idles until its engine's turn comes round. Variable lengths

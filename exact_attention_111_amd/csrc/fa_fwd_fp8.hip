@@ -78,7 +78,9 @@ struct Fp8Args {
   float* lse;
   int B, H, Hkv, Lq, Lk;
   int group, ntq, nwg;
-  int nprog;  // workgroups launched (tile_of_program)
+  int nprog;                   // workgroups launched (tile_of_program)
+  TileOrder order;             // tile_order over (batch, KV head) pairs, group x ntq tiles each
+  Divisor group_div, hkv_div;  // H / Hkv and Hkv as divisors
   float scale_log2;
   int causal, window;
   const int32_t* seqlens;
@@ -102,13 +104,13 @@ __global__ __launch_bounds__(kF8NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     // Workgroup order as in the bf16 prefill: (batch, KV head) pairs with group x ntq tiles
     // each, so the query heads that share a KV head run side by side on one XCD.
     int pair, u;
-    xcd_tile_order(tile_id, a.nwg, a.group * a.ntq, pair, u);
-    const int qt = u / a.group;
-    const int b = pair / a.Hkv, kvh = pair - b * a.Hkv;
+    tile_order(a.order, tile_id, pair, u);
+    const int qt = div_by(u, a.group_div);
+    const int b = div_by(pair, a.hkv_div), kvh = pair - b * a.Hkv;
     const int h = kvh * a.group + (u - qt * a.group);
     int n_kv = a.Lk, n_q = a.Lq;
     if (a.seqlens != nullptr) {
-      const int n = min(max(a.seqlens[b], 0), a.Lk);
+      const int n = min(max(load_const(a.seqlens + b), 0), a.Lk);
       n_kv = n;
       n_q = n;
     }
@@ -418,6 +420,10 @@ hipError_t launch_fwd_fp8(const Fp8FwdParams& p, hipStream_t stream) {
   const long long nwg = (long long)a.ntq * p.B * p.H;
   if (nwg > 0x7fffffffLL || (long long)p.Lk * kF8D > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   a.nwg = (int)nwg;
+  if (a.nwg == 0) return hipSuccess;
+  a.order = make_tile_order(a.nwg, a.group * a.ntq);
+  a.group_div = make_divisor(a.group);
+  a.hkv_div = make_divisor(p.Hkv);
   // Dense inputs on a persistent grid, variable lengths one workgroup per tile (as for bf16).
   const int P = p.seqlens == nullptr ? persistent_programs(reinterpret_cast<const void*>(&fwd_fp8_kernel), kF8NT) : 0;
   a.nprog = (P > 0 && a.nwg > P) ? P : a.nwg;

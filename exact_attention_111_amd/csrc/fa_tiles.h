@@ -1,5 +1,8 @@
-// fa_tiles.h — LDS layout of K/V-style tiles shared by the forward and backward kernels.
+// fa_tiles.h — LDS layouts of K/V-style tiles and the order of query tiles, shared by the
+// forward and backward kernels.
 #pragma once
+
+#include <algorithm>
 
 namespace fa {
 
@@ -32,42 +35,99 @@ __device__ __forceinline__ int kv_xor(int r) {
   return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 
-// Query tile and (batch, head) of prefill tile id `hw` (ntq query tiles per head, nwg tiles),
-// heaviest tile first. Tile id i is meant for XCD i % 8 as that XCD's slot i / 8: it is the
-// hardware workgroup id when every tile is a workgroup (hardware id i runs on XCD i % 8), and
-// tile_of_program keeps a persistent workgroup on the XCD its tile ids belong to.
-// When the (batch, head) count is a multiple of 8, head bh belongs to XCD bh % 8, so every
-// XCD gets the same mix of sequences (equal work even when lengths vary) and its L2 serves
-// the K/V of its own heads only. An XCD goes through its heads in groups of just enough
-// heads to fill its 32 CUs with query tiles, heaviest tile first across the group: one head
-// at a time when a head has 32 or more tiles (its CUs then share that head's K/V in L2;
-// walking all of an XCD's heads at once multiplied HBM re-reads 2.3x at B=1, H=32,
-// L=16384), several when heads are short (one head at a time would start the heaviest tiles
-// of later heads too late). Otherwise each XCD takes a contiguous range of logical ids,
-// heaviest tile first within a head.
-__device__ __forceinline__ void xcd_tile_order(int hw, int nwg, int ntq, int& bh, int& qt) {
-  const int xcd = hw & 7, slot = hw >> 3;
+// Division by a value fixed for a whole launch, as one 64-bit product and a shift (the
+// invariant-divisor method of Granlund and Montgomery, "Division by invariant integers using
+// multiplication", 1994): for 0 <= n < 2^31 and 1 <= d < 2^31, with l = ceil(log2 d) and
+// m = ceil(2^(31 + l) / d), which is below 2^32, m d - 2^(31 + l) < d <= 2^l and so
+// floor(n / d) = floor(m n / 2^(31 + l)). A signed division by a launch argument costs the
+// scalar unit about fifteen instructions after a reciprocal, and all the waves of a
+// workgroup decode their tile at once on the compute unit's one scalar unit.
+struct Divisor {
+  unsigned m;
+  int shift;  // 31 + l
+  int d;
+};
+
+inline Divisor make_divisor(int d) {  // host side; 1 <= d < 2^31
+  int l = 0;
+  while ((1LL << l) < d) ++l;
+  const unsigned long long m = ((1ULL << (31 + l)) + (unsigned long long)d - 1) / (unsigned long long)d;
+  return Divisor{(unsigned)m, 31 + l, d};
+}
+
+__device__ __forceinline__ int div_by(int n, const Divisor& v) {
+  return (int)(((unsigned long long)v.m * (unsigned)n) >> v.shift);
+}
+
+// Order of the query tiles of a prefill-style launch: nwg tiles, ntq per head (or per
+// (batch, KV head) pair), heaviest tile first. Tile id i is meant for XCD i % 8 as that XCD's
+// slot i / 8: it is the hardware workgroup id when every tile is a workgroup (hardware id i
+// runs on XCD i % 8), and tile_of_program keeps a persistent workgroup on the XCD its tile
+// ids belong to.
+// When the head count is a multiple of 8, head bh belongs to XCD bh % 8, so every XCD gets
+// the same mix of sequences (equal work even when lengths vary) and its L2 serves the K/V of
+// its own heads only. An XCD goes through its heads in groups of just enough heads to fill
+// its 32 CUs with query tiles, heaviest tile first across the group: one head at a time when
+// a head has 32 or more tiles (its CUs then share that head's K/V in L2; walking all of an
+// XCD's heads at once multiplied HBM re-reads 2.3x at B=1, H=32, L=16384), several when
+// heads are short (one head at a time would start the heaviest tiles of later heads too
+// late). Otherwise each XCD takes a contiguous range of tile ids, heaviest tile first within
+// a head.
+// The host computes the launch's constants once (make_tile_order); tile_order decodes a tile
+// id with products and shifts only.
+struct TileOrder {
+  int ntq;
+  int grouped;     // the head count is a multiple of 8: heads go to the XCDs in groups
+  int g_last;      // grouped: index of an XCD's last head group
+  Divisor span;    // grouped: tiles of one head group (heads per group x ntq)
+  Divisor grp;     // grouped: heads per group
+  Divisor last;    // grouped: heads in the last group (it may be smaller)
+  int per, extra;  // otherwise: tiles per XCD, and how many XCDs take one more
+  Divisor tiles;   // otherwise: ntq
+};
+
+inline TileOrder make_tile_order(int nwg, int ntq) {  // host side; nwg >= 1, ntq >= 1
+  TileOrder t{};
+  t.ntq = ntq;
   const int nheads = nwg / ntq;
-  if ((nheads & 7) == 0) {
+  t.grouped = (nheads & 7) == 0;
+  if (t.grouped) {
     const int per_xcd = nheads >> 3;
-    const int group = min(max(1, (32 + ntq - 1) / ntq), per_xcd);
-    const int g = slot / (group * ntq);
-    const int in_group = min(group, per_xcd - g * group);  // the last group may be smaller
-    const int idx = slot - g * group * ntq;
-    qt = ntq - 1 - idx / in_group;
-    bh = xcd + 8 * (g * group + idx % in_group);
+    const int group = std::min(std::max(1, (32 + ntq - 1) / ntq), per_xcd);
+    t.g_last = (per_xcd - 1) / group;
+    t.span = make_divisor(group * ntq);
+    t.grp = make_divisor(group);
+    t.last = make_divisor(per_xcd - t.g_last * group);
   } else {
-    const int per = nwg >> 3, extra = nwg & 7;
-    const int logical = xcd * per + min(xcd, extra) + slot;
-    bh = logical / ntq;
-    qt = ntq - 1 - (logical - bh * ntq);
+    t.per = nwg >> 3;
+    t.extra = nwg & 7;
+    t.tiles = make_divisor(ntq);
+  }
+  return t;
+}
+
+// Head (or pair) bh and query tile qt of tile id hw.
+__device__ __forceinline__ void tile_order(const TileOrder& t, int hw, int& bh, int& qt) {
+  const int xcd = hw & 7, slot = hw >> 3;
+  if (t.grouped) {
+    const int g = div_by(slot, t.span);
+    const int idx = slot - g * t.span.d;
+    const bool lg = g == t.g_last;
+    const Divisor in_group{lg ? t.last.m : t.grp.m, lg ? t.last.shift : t.grp.shift, lg ? t.last.d : t.grp.d};
+    const int i = div_by(idx, in_group);
+    qt = t.ntq - 1 - i;
+    bh = xcd + 8 * (g * t.grp.d + idx - i * in_group.d);
+  } else {
+    const int logical = xcd * t.per + min(xcd, t.extra) + slot;
+    bh = div_by(logical, t.tiles);
+    qt = t.ntq - 1 - (logical - bh * t.ntq);
   }
 }
 
-// Tile id (as numbered for xcd_tile_order) that workgroup p of nprog takes in its round r, or
+// Tile id (as numbered for tile_order) that workgroup p of nprog takes in its round r, or
 // -1 when it has no more. With one workgroup per tile (nprog == ntiles) workgroup p takes tile
 // p. Otherwise nprog is a multiple of 8: workgroup p stays on XCD p % 8 (the tiles whose ids
-// are p mod 8, which xcd_tile_order lists heaviest first) and takes one of them in each round
+// are p mod 8, which tile_order lists heaviest first) and takes one of them in each round
 // of nprog / 8, forward through the round in even rounds and backward in odd ones, so that
 // the workgroup with a round's heaviest tile gets the next round's lightest.
 __device__ __forceinline__ int tile_of_program(int p, int r, int nprog, int ntiles) {
