@@ -282,7 +282,7 @@ def workload_call(w, dev, window=None, page=None, fp8=False):
 # change of load can take longer: FP8 prefills launched in turn with bf16 ones, right after the
 # decode workload, went 1.93, 1.76, 1.68, ... 1.48, ... 1.33 ms over their first 70 ms while the
 # bf16 launches beside them held steady. Every timed section therefore first runs its own
-# calls untimed, each round of them bracketed by HIP events, for at least SETTLE_MS of wall
+# calls untimed, back to back, each round of them bracketed by HIP events, for at least SETTLE_MS of wall
 # time and then until the median round time of the last SETTLE_WINDOW rounds is no more than
 # SETTLE_TOL below that of the SETTLE_WINDOW before them (the times have stopped falling), or
 # SETTLE_MAX_MS has passed; then come its W warm-up launches. The figures are those of
@@ -296,18 +296,27 @@ SETTLE_LOG = {}
 
 def settle(fns, label, min_ms=SETTLE_MS, max_ms=SETTLE_MAX_MS):
     """Launch the calls in turn, untimed, until the round times have stopped falling (see
-    above); records the wall time taken under `label` in SETTLE_LOG."""
+    above); records the wall time taken under `label` in SETTLE_LOG. Rounds are launched back
+    to back, as the timed launches are, with two rounds always queued behind the one whose
+    time is read, so the GPU never idles between them: a synchronisation after every round
+    left 50-70 us gaps, under which the kernels ran faster than in the back-to-back timed
+    launches that followed (16k prefill: 1.77 ms settled, then 1.87 and 1.94 ms timed)."""
+    import collections
     import time
     import torch
     t0 = time.perf_counter()
-    rounds = []
+    rounds, queued = [], collections.deque()
     while True:
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for fn in fns:
             fn()
         b.record()
-        torch.cuda.synchronize()
+        queued.append((a, b))
+        if len(queued) < 3:
+            continue
+        a, b = queued.popleft()
+        b.synchronize()
         rounds.append(a.elapsed_time(b))
         el = (time.perf_counter() - t0) * 1e3
         if el >= max_ms:
@@ -315,7 +324,8 @@ def settle(fns, label, min_ms=SETTLE_MS, max_ms=SETTLE_MAX_MS):
         if el >= min_ms and len(rounds) >= 2 * SETTLE_WINDOW and \
                 median(rounds[-SETTLE_WINDOW:]) >= (1.0 - SETTLE_TOL) * median(rounds[-2 * SETTLE_WINDOW:-SETTLE_WINDOW]):
             break
-    SETTLE_LOG[label] = {"ms": round(el, 1), "rounds": len(rounds)}
+    torch.cuda.synchronize()
+    SETTLE_LOG[label] = {"ms": round(el, 1), "rounds": len(rounds) + len(queued)}
 
 
 def time_launches(fn, steps, warmup, label):
@@ -323,11 +333,10 @@ def time_launches(fn, steps, warmup, label):
     events on torch's current stream (the stream the kernels are launched on), after the clock
     has settled under this call's load."""
     import torch
-    settle([fn], label)
-    for _ in range(warmup):
-        fn()
-    torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    settle([fn], label)
+    for _ in range(warmup):  # no synchronisation between settle, warm-ups and timed launches
+        fn()
     for a, b in ev:
         a.record()
         fn()
@@ -345,7 +354,6 @@ def time_interleaved(fns, steps, warmup, label, rounds=4):
     for fn in fns:
         for _ in range(warmup):
             fn()
-    torch.cuda.synchronize()
     per = max(1, steps // rounds)
     ev = [[] for _ in fns]
     for _ in range(rounds):
@@ -503,11 +511,10 @@ def main():
         if ev is not None:
             ev[2].record()
 
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     settle([step], "step")
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -539,11 +546,10 @@ def main():
         fa.bwd(xp["q"], xp["k"], xp["v"], o_p, do_p, lse_p, causal=True, scale=wp.scale, workspace=ws_b,
                dq=grads[0], dk=grads[1], dv=grads[2])
 
+    bev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     settle([bwd_call], "backward")
     for _ in range(args.warmup):
         bwd_call()
-    torch.cuda.synchronize()
-    bev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     for a_, b_ in bev:
         a_.record(); bwd_call(); b_.record()
     torch.cuda.synchronize()
