@@ -29,3 +29,48 @@ def test_traffic_record_matches_sources_or_is_withheld(monkeypatch):
     for part in ("prefill", "decode"):
         rec, why = bench.traffic_record(part)
         assert rec is None and ("other sources" in why or "no counter profile" in why)
+
+
+class _ScriptedEvent:
+    """Stands in for torch.cuda.Event: each (start, end) pair reports the next scripted time."""
+
+    def __init__(self, script, **kw):
+        self.script = script
+
+    def record(self):
+        pass
+
+    def synchronize(self):
+        pass
+
+    def elapsed_time(self, end):
+        return next(self.script)
+
+
+def _settle_with(monkeypatch, times, min_ms, max_ms):
+    import itertools
+
+    import torch
+    script = iter(itertools.chain(times, itertools.repeat(times[-1])))
+    monkeypatch.setattr(torch.cuda, "Event", lambda **kw: _ScriptedEvent(script, **kw))
+    monkeypatch.setattr(torch.cuda, "synchronize", lambda *a: None)
+    calls = []
+    bench.settle([lambda: calls.append(1)], "t", min_ms=min_ms, max_ms=max_ms)
+    return bench.SETTLE_LOG["t"], len(calls)
+
+
+def test_settle_waits_until_round_times_stop_falling(monkeypatch):
+    """Round times that fall by 3% a round for 40 rounds and then hold: settling ends within two
+    comparison windows of the plateau, not before it, and every queued round was launched."""
+    W = bench.SETTLE_WINDOW
+    falling = [10.0 * 0.97 ** i for i in range(40)]
+    log, launched = _settle_with(monkeypatch, falling + [falling[-1]] * 100, min_ms=0.0, max_ms=1e9)
+    read = log["rounds"] - 2  # rounds whose time was read; two more were still queued
+    assert 40 + W <= read <= 40 + 2 * W + 1
+    assert launched == log["rounds"]
+
+
+def test_settle_stops_at_its_time_limit(monkeypatch):
+    """Times that never stop falling: the wall-time cap ends the settle."""
+    log, _ = _settle_with(monkeypatch, [1e6 * 0.9 ** i for i in range(100000)], min_ms=0.0, max_ms=30.0)
+    assert 30.0 <= log["ms"] < 1000.0
