@@ -141,6 +141,58 @@ def test_bwd_full_size_causal_L16384_d128_sampled():
             report(f"fa_bwd {w.name}: dK, dV, {len(keys)} keys of head 0: max err/allowance {rk:.3f}, {rv:.3f}")
 
 
+def test_bwd_full_size_gqa_varlen_sampled():
+    """The GQA variable-length workload (B=8, 32 query / 8 KV heads, lengths up to 8192) at full
+    size, in the order its dK/dV and dQ launches deal (batch, KV head) pairs to the XCDs.
+    Gradients start NaN: every row of a sequence must come back finite and every padding row
+    exactly zero. Then sampled dQ rows of one query head per sequence (its first and last rows
+    and rows of 128-row blocks across it) and sampled dK/dV keys of one KV head, summed over its
+    four query heads, against the oracle ("FlashAttention 与长上下文", the online-softmax
+    section: the backward recomputes P from the saved row statistics)."""
+    fa = _fa()
+    w = fa_inputs.WORKLOADS["gqa_varlen_prefill_B8_H32_Hkv8_L8192_d128"]
+    announce(entry="fa_bwd", workload=w.name, case="every row written, sampled rows and keys")
+    x = fa_inputs.workload_inputs(w, device=DEV)
+    sl = x["seqlens"]
+    o, lse = fa.fwd(x["q"], x["k"], x["v"], causal=True, scale=w.scale, seqlens=sl)
+    do = _dout(o.shape, 250)
+    nan = float("nan")
+    dq = torch.full_like(x["q"], nan)
+    dk, dv = torch.full_like(x["k"], nan), torch.full_like(x["v"], nan)
+    fa.bwd(x["q"], x["k"], x["v"], o, do, lse, causal=True, scale=w.scale, seqlens=sl, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    lens = x["seqlens_cpu"].tolist()
+    for b, n in enumerate(lens):
+        for name, g in (("dQ", dq), ("dK", dk), ("dV", dv)):
+            assert bool(torch.isfinite(g[b, :, :n]).all()), f"{name} of sequence {b}: a valid row was not written"
+            assert bool((g[b, :, n:] == 0).all()), f"{name} of sequence {b}: a padding row is not zero"
+    rng = np.random.default_rng(251)
+    group = w.H // w.Hkv
+    for b, n in enumerate(lens):
+        h = (5 * b + 3) % w.H
+        rows = np.unique(np.concatenate([[0, n - 1], np.minimum(128 * np.arange(0, n // 128 + 1, 9)
+                                                                + rng.integers(0, 128), n - 1)]))
+        q64, k64, v64, do64 = (fa_inputs.as_oracle_f64(t[b, hh, :n]) for t, hh in
+                               ((x["q"], h), (x["k"], h // group), (x["v"], h // group), (do, h)))
+        dQ, tQ = grad_rows_oracle(q64, k64, v64, do64, rows, scale=w.scale, causal=True)
+        r = _close(dq[b, h, rows], dQ, f"dQ rows of sequence {b} head {h}", tQ)
+        report(f"fa_bwd {w.name}: dQ, {len(rows)} rows of sequence {b} (length {n}), head {h}: "
+               f"max err/allowance {r:.3f}")
+    b = int(np.argmin(lens))  # the shortest sequence keeps the key oracle quick
+    n, kvh = lens[b], 3
+    keys = np.unique(np.concatenate([[0, 1, n - 1], rng.choice(n, 9, replace=False)]))
+    k64, v64 = (fa_inputs.as_oracle_f64(t[b, kvh, :n]) for t in (x["k"], x["v"]))
+    dK = dV = tK = tV = 0.0
+    for h in range(kvh * group, (kvh + 1) * group):
+        q64, do64 = (fa_inputs.as_oracle_f64(t[b, h, :n]) for t in (x["q"], do))
+        gk, gv, ak, av = grad_keys_oracle(q64, k64, v64, do64, keys, scale=w.scale, causal=True)
+        dK, dV, tK, tV = dK + gk, dV + gv, tK + ak, tV + av
+    rk = _close(dk[b, kvh, keys], dK, f"dK keys of sequence {b} KV head {kvh}", tK)
+    rv = _close(dv[b, kvh, keys], dV, f"dV keys of sequence {b} KV head {kvh}", tV)
+    report(f"fa_bwd {w.name}: dK, dV, {len(keys)} keys of sequence {b} (length {n}), KV head {kvh} "
+           f"(four query heads): max err/allowance {rk:.3f}, {rv:.3f}")
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_empty_and_single_token_sequences(d):
     """Per-sequence lengths 0, 300 and 1 in one call. The empty sequence has no visible key:
