@@ -16,7 +16,7 @@ import torch
 
 import fa_inputs
 import oracle
-from parity import compare, compare_fp8_exact, fp8_flip_slack, report
+from parity import check_written, compare, compare_fp8_exact, fp8_flip_slack, nan_filled_outputs, report
 
 pytestmark = pytest.mark.gpu
 
@@ -122,3 +122,38 @@ def test_fp8_full_size_16k_sampled():
                               what=f"fp8 16k head {h}")
         report(f"fa_fwd_fp8 {w.name}, head {h}, {len(rows)} rows: vs FP8 oracle O {st['o_max']:.3g} "
                f"LSE {st['lse_max']:.3g}; vs exact attention max err/allowance {r:.3f}")
+
+
+def test_fp8_gqa_varlen_full_size():
+    """The GQA variable-length workload with FP8 inputs (one workgroup per 256-row query tile,
+    8,192 of them): outputs start NaN, every valid row must be written and every padding row
+    come back O = 0, LSE = -inf; then the first and last row of every query tile and 8 random
+    rows of one query head per sequence against both references."""
+    w = fa_inputs.WORKLOADS["gqa_varlen_prefill_B8_H32_Hkv8_L8192_d128"]
+    announce(entry="fa_fwd_fp8", workload=w.name, case="every tile written, sampled rows")
+    x = fa_inputs.fp8_prefill_inputs(w.B, w.H, w.Hkv, w.L, w.L, w.d, seed=w.seed, device=DEV,
+                                     len_range=w.len_range)
+    o, lse = nan_filled_outputs((w.B, w.H, w.L, w.d), (w.B, w.H, w.L), torch.bfloat16, device=DEV)
+    _fa().fwd_fp8(x["q"], x["k"], x["v"], x["q_descale"], x["k_descale"], x["v_descale"], causal=True,
+                  scale=w.scale, seqlens=x["seqlens"], out=o, lse=lse)
+    torch.cuda.synchronize()
+    lens = x["seqlens_cpu"].tolist()
+    check_written(o, lse, lens)
+    rng = np.random.default_rng(660)
+    group = w.H // w.Hkv
+    for b, n in enumerate(lens):
+        h = (7 * b + 2) % w.H
+        kvh = h // group
+        rows = np.unique(np.concatenate([np.arange(0, n, 256), np.minimum(np.arange(255, n + 255, 256), n - 1),
+                                         rng.choice(n, 8, replace=False)]))
+        Q = oracle.e4m3_decode(x["q"][b, h, :n].cpu().numpy()) * float(x["q_descale"][b, h])
+        K = oracle.e4m3_decode(x["k"][b, kvh, :n].cpu().numpy()) * float(x["k_descale"][b, kvh])
+        V = oracle.e4m3_decode(x["v"][b, kvh, :n].cpu().numpy()) * float(x["v_descale"][b, kvh])
+        O, LSE = oracle.attention_fp8_head(Q, K, V, scale=w.scale, causal=True, rows=rows)
+        slack = fp8_flip_slack(Q, K, V, scale=w.scale, causal=True, rows=rows)
+        st = compare(o[b, h, rows], lse[b, h, rows], O, LSE, bf16_out=True, what=f"fp8 varlen b{b} h{h}",
+                     o_slack=slack)
+        r = compare_fp8_exact(o[b, h, rows], lse[b, h, rows], Q, K, V, scale=w.scale, causal=True, rows=rows,
+                              what=f"fp8 varlen b{b} h{h}")
+        report(f"fa_fwd_fp8 {w.name}: sequence {b} (length {n}), head {h}, {len(rows)} rows: vs FP8 oracle "
+               f"O {st['o_max']:.3g} LSE {st['lse_max']:.3g}; vs exact attention max err/allowance {r:.3f}")
