@@ -106,7 +106,8 @@ def test_paged_table_entries_past_context_not_read_and_bad_entries_clamped():
 def test_paged_decode_full_size_sampled():
     """The decode workload (64 requests, 32 query / 8 KV heads, contexts 8192..32768) with its
     cache in 16-key pages scattered through the pool, in bench.py's configuration; sampled
-    (request, head) pairs against the oracle on those requests' gathered pages."""
+    (request, head) pairs against the oracle on those requests' gathered pages, and every pair
+    against the contiguous decode."""
     w = fa_inputs.WORKLOADS["decode_B64_H32_Hkv8_ctx32768_d128"]
     P = 16
     announce(entry="fa_decode_paged", workload=w.name, P=P, case="sampled heads")
@@ -125,3 +126,14 @@ def test_paged_decode_full_size_sampled():
         O, LSE = oracle.decode_paged(fa_inputs.as_oracle_f64(x["q"][b:b + 1, h:h + 1]), kp, vp,
                                      np.arange(npg)[None], ctx[b:b + 1], page_size=P, scale=w.scale)
         compare(o[b:b + 1, h:h + 1], lse[b:b + 1, h:h + 1], O, LSE, bf16_out=True, what=f"paged 32k b{b} h{h}")
+    # Every (request, head): bitwise equal to the contiguous decode of the same cache gathered
+    # from its pages, with the paged call's capacity (that decode's every pair is checked
+    # against the oracle at full size). Table entries past a context are never read by either;
+    # they are clamped into the pool only so that the gather stays in bounds.
+    tbl = x["block_table"].long().clamp(0, x["k_pages"].shape[0] - 1)
+    cap = tbl.shape[1] * P
+    kc = x["k_pages"][tbl].permute(0, 2, 1, 3, 4).reshape(w.B, w.Hkv, cap, w.d).contiguous()
+    vc = x["v_pages"][tbl].permute(0, 2, 1, 3, 4).reshape(w.B, w.Hkv, cap, w.d).contiguous()
+    o2, l2 = _fa().decode(x["q"], kc, vc, x["ctx_lens"], scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, l2), "paged decode differs from the contiguous decode"
