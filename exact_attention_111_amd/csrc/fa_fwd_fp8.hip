@@ -6,14 +6,18 @@
 //     t = s * (scale * log2(e) * descale_q * descale_k) with s = q8 . k8 from the FP8 matrix
 //     cores (fp32 accumulation of exact products);
 //   * each row keeps an integer base-2 reference m (raised to ceil(tile max) when a tile's
-//     scores pass it), so every rescale of the running output is an exact power of two;
+//     scores pass it);
 //   * x = 2^(t - m + 8) <= 256 enters the P V product as E4M3 (v_cvt_pk_fp8_f32, round to
 //     nearest even) while the row sum l adds the unrounded x;
-//   * O = descale_v * o / l (bf16) and LSE = ln(2) (m - 8 + log2 l).
+//   * o and l are kept relative to a frame mf <= m (the row's first reference, moved up only
+//     when m passes it by more than 64): a tile's x enters with the factor 2^(m - mf), applied
+//     to P through the product's E8M0 scale operand and to l with an fma, so a rising
+//     reference costs no pass over the output accumulators. Every factor is a power of two;
+//   * O = descale_v * o / l (bf16) and LSE = ln(2) (mf - 8 + log2 l).
 // E4M3 rounding commutes with power-of-two scaling, so the result does not depend on the
 // tiling: it is the whole-row definition with the final reference.
 //
-// gfx950 mapping (v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales for both products):
+// gfx950 mapping (v_mfma_scale_f32_32x32x64_f8f6f4; unit scales except the per-row scale of P):
 //   * Workgroup: 256 query rows of one (batch, head) at a time (dense inputs: a persistent grid
 //     taking tiles in rounds, as the bf16 prefill), 8 waves of 32 rows, two per SIMD. Each
 //     wave keeps its Q rows as B operands: lane (half, col) holds dims 64 ks + 32 half ..
@@ -65,6 +69,12 @@ __device__ __forceinline__ int f8_key(int h, int T) { return 32 * (T >> 4) + 8 *
 
 __device__ __forceinline__ f32x16 mfma_f8(i32x8 a, i32x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// The same product with the B operand scaled by 2^(sb - 127) (E8M0, one per lane: the lane's
+// 32 values of B along K, here one query row's P for half of the tile's keys).
+__device__ __forceinline__ f32x16 mfma_f8_bscaled(i32x8 a, i32x8 b, f32x16 c, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, sb);
 }
 
 struct Fp8Args {
@@ -150,6 +160,7 @@ __global__ __launch_bounds__(kF8NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[nb][r] = 0.f;
     float m = kNegInf, l = 0.f;
+    float mf = kNegInf;  // the frame of o and l: the row's reference when they were last rescaled
 
     // LDS addresses. K: lane (half, col) reads row 32 kb + col, logical chunks 4 ks + 2 half
     // (+1); kv rows of the two key blocks share the swizzle, so kb is an immediate offset.
@@ -307,16 +318,27 @@ __global__ __launch_bounds__(kF8NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, cur[kb][r]);
       mx = max_of_halves(mx) * c;
       const float m_new = mx > m ? ceilf(mx) : m;
-      // 0 when there was no reference, 1 when unchanged, else an exact power of two
-      const float alpha = m == kNegInf ? 0.f : __builtin_amdgcn_ldexpf(1.f, (int)(m - m_new));
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
-        l *= alpha;
+      // o and l stay in the frame mf instead of being rescaled whenever the reference rises:
+      // this tile's x (relative to m_new, so that it fits E4M3) enters P V scaled by
+      // 2^(m_new - mf) through the product's scale of P, and l by the same factor; all of it
+      // exact powers of two. The frame is the row's first reference, and moves up (o and l
+      // rescaled) only when the reference passes it by more than 64, which keeps o and l far
+      // from overflow.
+      float frame = mf == kNegInf ? m_new : mf;
+      if (__builtin_amdgcn_ballot_w64(m_new - frame > 64.f) != 0) {
+        const bool up = m_new - frame > 64.f;
+        const float f = up ? __builtin_amdgcn_ldexpf(1.f, (int)(frame - m_new)) : 1.f;
+        l *= f;
 #pragma unroll
         for (int nb = 0; nb < kF8NB; ++nb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[nb][r] *= alpha;
+          for (int r = 0; r < 16; ++r) oacc[nb][r] *= f;
+        frame = up ? m_new : frame;
       }
+      mf = frame;
       m = m_new;
+      const int kf = m == kNegInf ? 0 : (int)(m - mf);  // 0 .. 64
+      const float sk = __builtin_amdgcn_ldexpf(1.f, kf);
       // x = 2^(t - m + 8) <= 256; a row with no reference yet has only masked scores here.
       const float off = m == kNegInf ? 0.f : 8.f - m;
       int pk[8];
@@ -328,7 +350,7 @@ __global__ __launch_bounds__(kF8NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
         for (int e = 0; e < 4; ++e) {
           const int T = 4 * i + e;
           x[e] = exp2_hw(fmaf(cur[T >> 4][T & 15], c, off));
-          l += x[e];
+          l = fmaf(x[e], sk, l);
         }
         int word = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
         word = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], word, true);
@@ -343,7 +365,7 @@ __global__ __launch_bounds__(kF8NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
         const i32x2 r2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vt + vaddr[0][nb] + 32 * kF8D));
         const i32x2 r3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vt + vaddr[1][nb] + 32 * kF8D));
         const i32x8 va = {r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
-        oacc[nb] = mfma_f8(va, pb, oacc[nb]);
+        oacc[nb] = mfma_f8_bscaled(va, pb, oacc[nb], 127 + kf);
       }
       if (mine) mask(t + 1, nxt);
     };
@@ -391,7 +413,7 @@ __global__ __launch_bounds__(kF8NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
       if (qw0 + r < a.Lq) *reinterpret_cast<u32x4*>(ob + (size_t)(qw0 + r) * kF8D + 8 * c16) = val;
     }
     if (my_q < a.Lq && half == 0)
-      a.lse[(size_t)(b * a.H + h) * a.Lq + my_q] = row_ok ? (m - 8.f + __log2f(lt)) * kLn2 : kNegInf;
+      a.lse[(size_t)(b * a.H + h) * a.Lq + my_q] = row_ok ? (mf - 8.f + __log2f(lt)) * kLn2 : kNegInf;
     // The next tile clears and refills LDS: every wave's staged-O reads must have returned.
     lds_barrier();
   }

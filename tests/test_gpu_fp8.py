@@ -157,3 +157,35 @@ def test_fp8_gqa_varlen_full_size():
                               what=f"fp8 varlen b{b} h{h}")
         report(f"fa_fwd_fp8 {w.name}: sequence {b} (length {n}), head {h}, {len(rows)} rows: vs FP8 oracle "
                f"O {st['o_max']:.3g} LSE {st['lse_max']:.3g}; vs exact attention max err/allowance {r:.3f}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_scores_rising_across_tiles(causal):
+    """Scores that rise by hundreds of base-2 units along the keys: each row's reference passes
+    its output frame by more than 64 several times, so the kernel's rare frame move (o and l
+    rescaled by an exact power of two) runs on many tiles. Q is all ones and key j's row is the
+    E4M3 value nearest 1 + 15 j / L in every dim, so row i's scores grow with its keys; V is
+    random. Against both references."""
+    B, H, Hkv, L, d = 1, 2, 1, 1000, 128
+    announce(entry="fa_fwd_fp8", case="rising scores", causal=causal, L=L)
+    g = torch.Generator().manual_seed(670)
+    qf = torch.ones((B, H, L, d))
+    kf = (1.0 + 15.0 * torch.arange(L, dtype=torch.float32) / L)[None, None, :, None].expand(B, Hkv, L, d)
+    vf = torch.randn((B, Hkv, L, d), generator=g)
+    codes = [t.contiguous().to(torch.float8_e4m3fn).view(torch.uint8).to(DEV) for t in (qf, kf, vf)]
+    ones_q = torch.ones((B, H), dtype=torch.float32, device=DEV)
+    ones_kv = torch.ones((B, Hkv), dtype=torch.float32, device=DEV)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = _fa().fwd_fp8(codes[0], codes[1], codes[2], ones_q, ones_kv, ones_kv, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    arrs = [t.cpu().numpy() for t in codes] + [ones_q.cpu().numpy(), ones_kv.cpu().numpy(), ones_kv.cpu().numpy()]
+    O, LSE = oracle.attention_fp8(*arrs, scale=scale, causal=causal)
+    K = oracle.e4m3_decode(arrs[1][0, 0])
+    Q = oracle.e4m3_decode(arrs[0][0, 0])
+    t_range = (Q[0] @ K[-1] - Q[0] @ K[0]) * scale / math.log(2.0)
+    assert t_range > 3 * 64, t_range  # the reference must pass the frame by more than 64 several times
+    for h in range(H):
+        V = oracle.e4m3_decode(arrs[2][0, 0])
+        slack = fp8_flip_slack(Q, K, V, scale=scale, causal=causal)
+        compare(o[0, h], lse[0, h], O[0, h], LSE[0, h], bf16_out=True, what=f"fp8 rising scores h{h}", o_slack=slack)
+        compare_fp8_exact(o[0, h], lse[0, h], Q, K, V, scale=scale, causal=causal, what=f"fp8 rising scores h{h}")
