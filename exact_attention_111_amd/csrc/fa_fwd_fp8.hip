@@ -292,6 +292,7 @@ __global__ __launch_bounds__(kF8NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     // Tile t + 1's K|V stage must have landed at iteration t, and the slot refilled there (of
     // tile t + 3) was last read at iteration t - 1.
     f32x16 sc[2], sn[2];
+    int pk[8] = {0, 0, 0, 0, 0, 0, 0, 0};  // P words (each fully rewritten per tile; no zeroing)
     if (ntk > 0) {
       scores(0, sc);
       mask(0, sc);
@@ -341,7 +342,6 @@ __global__ __launch_bounds__(kF8NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
       const float sk = __builtin_amdgcn_ldexpf(1.f, kf);
       // x = 2^(t - m + 8) <= 256; a row with no reference yet has only masked scores here.
       const float off = m == kNegInf ? 0.f : 8.f - m;
-      int pk[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         // bytes 4 i .. 4 i + 3 = elements (kb, r) with 16 kb + r = 4 i .. 4 i + 3
@@ -352,7 +352,7 @@ __global__ __launch_bounds__(kF8NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
           x[e] = exp2_hw(fmaf(cur[T >> 4][T & 15], c, off));
           l = fmaf(x[e], sk, l);
         }
-        int word = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+        int word = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], pk[i], false);
         word = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], word, true);
         pk[i] = word;
       }
