@@ -160,7 +160,7 @@ __global__ __launch_bounds__(kF8NT) __attribute__((amdgpu_waves_per_eu(2, 2))) v
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[nb][r] = 0.f;
     float m = kNegInf, l = 0.f;
-    float mf = kNegInf;  // the frame of o and l: the row's reference when they were last rescaled
+    float mf = kNegInf;  // the frame of o and l: the row's first reference, or the one of their last rescale
 
     // LDS addresses. K: lane (half, col) reads row 32 kb + col, logical chunks 4 ks + 2 half
     // (+1); kv rows of the two key blocks share the swizzle, so kb is an immediate offset.
