@@ -71,6 +71,7 @@ def test_settle_waits_until_round_times_stop_falling(monkeypatch):
 
 
 def test_settle_stops_at_its_time_limit(monkeypatch):
-    """Times that never stop falling: the wall-time cap ends the settle."""
-    log, _ = _settle_with(monkeypatch, [1e6 * 0.9 ** i for i in range(100000)], min_ms=0.0, max_ms=30.0)
+    """Times that never stop falling (1.6% per window of 8 rounds, far from underflow within the
+    cap): the wall-time cap ends the settle."""
+    log, _ = _settle_with(monkeypatch, [1e6 * 0.998 ** i for i in range(200000)], min_ms=0.0, max_ms=30.0)
     assert 30.0 <= log["ms"] < 1000.0
